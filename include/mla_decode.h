@@ -1,0 +1,195 @@
+/*
+ * mla_decode.h -- C ABI of the gfx950 weight-absorbed MLA decode library.
+ *
+ * The operation (weight-absorbed Multi-head Latent Attention decode over a
+ * paged latent cache):
+ *
+ *   For sequence b with kv_len L_b keys and q_len q_b query tokens, every query
+ *   row (token t, head h) holds an absorbed query q of width d_latent + d_rope
+ *   (512 + 64).  Keys are the cached latent rows c_j = [latent_j | rope_j]
+ *   gathered through the block table; values are the latent part latent_j
+ *   (d_latent wide).  With vis = L_b - q_b + t + 1 when causal, else L_b:
+ *
+ *     s_j = softmax_scale * <q, c_j>            j < vis
+ *     O   = sum_j softmax(s)_j * latent_j        (d_latent wide, bf16 out)
+ *     LSE = ln sum_j exp(s_j)                    (fp32 out)
+ *
+ *   Sources: the decode-only weight-absorbed MLA path of the KsanaLLM 0.6.0
+ *   page (prefill/decode disaggregation section); several draft tokens per
+ *   sequence verified in one decode pass at the original batch size, from the
+ *   PaddlePaddle 3.0 inference page (speculative decoding section); the
+ *   softmax_lse output and the split-K key partition of the "FlashAttention-3
+ *   in DeepSeek-R1" page (chapter 2); its per-token KV-cache scale (section
+ *   3.1) and block table (section 4.1).
+ *
+ * Calling sequence (all device work is stream-ordered, no host sync inside):
+ *
+ *   1. mla_decode_plan   host only: split-KV schedule from host-side lengths.
+ *   2. copy the plan image (plan_host, info.plan_bytes) to device memory.
+ *   3. mla_decode_fwd    main kernel: writes O/LSE for unsplit row blocks and
+ *                        partial (O, LSE) into the workspace for split ones.
+ *   4. mla_combine       merges the partials of split row blocks into O/LSE.
+ *
+ * Ownership: the caller allocates and owns every buffer; the library
+ * allocates no memory and keeps no mutable state.  Buffers must stay alive
+ * until the stream has passed the work that uses them.
+ *
+ * Errors: every call returns an mla_status; nothing throws across the ABI.
+ * Values that live in device memory (block-table entries, device lengths) are
+ * not validated: they must agree with the host lengths given to the planner
+ * and index pages inside the pool, otherwise behaviour is undefined.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* hipStream_t; NULL means the null stream of the current device. */
+typedef struct ihipStream_t* mla_stream_t;
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL_ARG = 1,           /* a required pointer is NULL                 */
+  MLA_ERR_BAD_SHAPE = 2,          /* sizes or host lengths are inconsistent     */
+  MLA_ERR_UNSUPPORTED = 3,        /* valid, but no kernel is built for it       */
+  MLA_ERR_MISALIGNED = 4,         /* a device pointer is not 16-byte aligned    */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 5,
+  MLA_ERR_PLAN_TOO_SMALL = 6,     /* plan buffer smaller than needed            */
+  MLA_ERR_BAD_PLAN = 7,           /* plan info does not match the shape         */
+  MLA_ERR_HIP = 8                 /* a HIP runtime call or launch failed        */
+} mla_status;
+
+typedef enum mla_kv_dtype {
+  MLA_KV_BF16 = 0,                /* cache rows are bf16, 2 * (d_latent + d_rope) bytes            */
+  MLA_KV_FP8_E4M3 = 1             /* OCP e4m3fn rows plus one fp32 scale per cached token          */
+} mla_kv_dtype;
+
+/* Problem shape.  Built kernels: d_latent 512, d_rope 64, page_size a power of
+ * two >= 32 (bf16) or >= 64 (fp8), 1 <= max_q_len <= MLA_MAX_Q_LEN, any
+ * num_heads >= 1. */
+typedef struct mla_shape {
+  int32_t batch;              /* B sequences                                       */
+  int32_t num_heads;          /* H query heads per token                           */
+  int32_t max_q_len;          /* padded query tokens per sequence                  */
+  int32_t d_latent;           /* value width = latent width (512)                  */
+  int32_t d_rope;             /* rope width (64); query/key width = d_latent+d_rope */
+  int32_t page_size;          /* cached tokens per page                            */
+  int32_t num_pages;          /* pages in the pool                                 */
+  int32_t max_pages_per_seq;  /* row length of the block table                     */
+  int32_t kv_dtype;           /* mla_kv_dtype                                       */
+  int32_t causal;             /* 1: token t sees keys j <= kv_len - q_len + t      */
+} mla_shape;
+
+#define MLA_MAX_Q_LEN 8
+
+/* What a plan holds, returned by the planner and passed back to fwd/combine. */
+typedef struct mla_plan_info {
+  int32_t num_workgroups;     /* grid of the main kernel                           */
+  int32_t num_items;          /* (sequence, row block, key range) work items       */
+  int32_t num_partials;       /* partial (O, LSE) slots written to the workspace   */
+  int32_t num_combine;        /* row blocks whose partials need merging            */
+  int32_t tile_tokens;        /* keys per pipeline tile                            */
+  int32_t rows_per_block;     /* query rows per work item (128)                    */
+  uint64_t plan_bytes;        /* bytes of the plan image                           */
+  uint64_t workspace_bytes;   /* workspace bytes this plan needs                   */
+} mla_plan_info;
+
+/* Library ABI version (MLA_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status status);
+
+/* Upper bounds, for allocating before the lengths are known.  num_workgroups
+ * as passed to mla_decode_plan (0 is not accepted here: pass the CU count). */
+uint64_t mla_plan_bytes_bound(const mla_shape* shape, int32_t num_workgroups);
+uint64_t mla_workspace_bytes_bound(const mla_shape* shape, int32_t num_workgroups);
+
+/* Number of compute units of a HIP device (the default workgroup count), or a
+ * negative mla_status on failure.  Needs a GPU. */
+int32_t mla_device_num_cus(int32_t device);
+
+/*
+ * Split-KV planner (host only, no HIP call).
+ *
+ * Splits sum_b ceil(q_b * H / 128) row blocks x ceil(L_b / tile) key tiles into
+ * work items and deals them to num_workgroups persistent workgroups so that
+ * each gets about the same number of tiles (a fixed per-item cost included).
+ * A row block whose key range is cut gets one partial slot per piece and a
+ * combine entry.  Key splitting with a log-sum-exp merge follows the split-K
+ * remark of the FlashAttention-3 page (chapter 2).
+ *
+ *   kv_lens_host [B]  keys per sequence, including this step's q_b tokens.
+ *   q_lens_host  [B]  query tokens per sequence (0..max_q_len); NULL means
+ *                     every sequence has max_q_len tokens.
+ *   num_workgroups    > 0; normally the device's CU count.
+ *   plan_host         caller buffer of plan_bytes bytes (>= the bound above),
+ *                     receives the plan image (int32 words, layout in the
+ *                     library source; treat it as opaque).
+ *   info              receives the plan summary.
+ *
+ * Errors: NULL_ARG; BAD_SHAPE if a length is negative, q_b > max_q_len,
+ * L_b > max_pages_per_seq * page_size, or (causal) 0 < L_b < q_b;
+ * UNSUPPORTED for shapes with no built kernel; PLAN_TOO_SMALL.
+ */
+mla_status mla_decode_plan(const mla_shape* shape, const int32_t* kv_lens_host,
+                           const int32_t* q_lens_host, int32_t num_workgroups,
+                           void* plan_host, uint64_t plan_bytes, mla_plan_info* info);
+
+/*
+ * Main decode kernel launch.
+ *
+ *   plan_dev     device copy of the plan image described by *info.
+ *   q            [B, max_q_len, H, d_latent + d_rope] bf16, row-major.  Rows
+ *                t >= q_lens[b] are never read.
+ *   kv_cache     [num_pages, page_size, d_latent + d_rope] bf16, or e4m3 bytes
+ *                for MLA_KV_FP8_E4M3.  Slots past kv_len and pages not in the
+ *                sequence's first ceil(kv_len / page_size) block-table entries
+ *                never influence the result.
+ *   kv_scale     [num_pages, page_size] fp32 per-token scales (fp8 only, else
+ *                ignored; may be NULL for bf16).
+ *   block_table  [B, max_pages_per_seq] int32 physical page ids.
+ *   kv_lens, q_lens  [B] int32 device copies of the planner's lengths
+ *                (q_lens may be NULL: every sequence has max_q_len tokens).
+ *   softmax_scale    multiplies <q, c_j>.
+ *   o            [B, max_q_len, H, d_latent] bf16 output; rows t >= q_b untouched.
+ *   lse          [B, max_q_len, H] fp32 natural-log LSE, or NULL.
+ *   workspace    >= info->workspace_bytes, 256-byte aligned; holds partials:
+ *                fp32 O [num_partials][128][d_latent], then fp32 LSE
+ *                [num_partials][128].
+ *
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, BAD_PLAN,
+ * WORKSPACE_TOO_SMALL, HIP (launch failure).
+ */
+mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info,
+                          const void* plan_dev, const void* q, const void* kv_cache,
+                          const float* kv_scale, const int32_t* block_table,
+                          const int32_t* kv_lens, const int32_t* q_lens,
+                          float softmax_scale, void* o, float* lse,
+                          void* workspace, uint64_t workspace_bytes, mla_stream_t stream);
+
+/*
+ * Merge of split row blocks: for each combine entry of the plan,
+ *   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) * O_s  -> bf16,
+ * reading the workspace partials laid out as described for mla_decode_fwd.
+ * A row whose partials are all empty (LSE_s = -inf) gets O = 0, LSE = -inf.
+ * No-op when info->num_combine == 0.  Must run after mla_decode_fwd on the
+ * same stream (or after the caller filled the partials itself).
+ */
+mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info,
+                       const void* plan_dev, const void* workspace,
+                       uint64_t workspace_bytes, const int32_t* q_lens,
+                       void* o, float* lse, mla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

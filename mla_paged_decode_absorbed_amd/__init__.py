@@ -1,0 +1,241 @@
+"""Weight-absorbed MLA decode over a paged latent KV cache on MI355X (gfx950).
+
+Thin ctypes binding over ``libmla_decode.so`` (C ABI in ``include/mla_decode.h``).
+It only marshals arguments: every step of the decode runs in the library's HIP
+kernels, and torch supplies device memory and the current stream.  There is no
+CPU fallback: calls fail loudly when the library is missing.
+
+Typical use::
+
+    import mla_paged_decode_absorbed_amd as mla
+    shape = mla.Shape.make(batch=B, num_heads=128, max_q_len=1, page_size=64,
+                           num_pages=kv.shape[0], max_pages_per_seq=bt.shape[1])
+    plan = mla.plan(shape, kv_lens_host)                 # host planner + upload
+    out, lse = mla.decode(shape, plan, q, kv, bt, kv_lens_dev, q_lens_dev, scale)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "decode_fwd", "combine",
+    "decode", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+ROWS_PER_BLOCK = 128
+D_LATENT = 512
+D_ROPE = 64
+
+EXPORTED_SYMBOLS = (
+    "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
+    "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
+    "mla_decode_fwd", "mla_combine",
+)
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, *, batch, num_heads, max_q_len, page_size, num_pages, max_pages_per_seq,
+             kv_dtype=KV_BF16, causal=True, d_latent=D_LATENT, d_rope=D_ROPE) -> "Shape":
+        return cls(batch, num_heads, max_q_len, d_latent, d_rope, page_size, num_pages,
+                   max_pages_per_seq, kv_dtype, int(bool(causal)))
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("num_workgroups", ctypes.c_int32), ("num_items", ctypes.c_int32),
+        ("num_partials", ctypes.c_int32), ("num_combine", ctypes.c_int32),
+        ("tile_tokens", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+        ("plan_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and type the C ABI.  Raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mla_paged_decode_absorbed_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, U64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+    sp, ip = ctypes.POINTER(Shape), ctypes.POINTER(PlanInfo)
+    lib.mla_abi_version.restype = I32
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [I32]
+    lib.mla_plan_bytes_bound.restype = U64
+    lib.mla_plan_bytes_bound.argtypes = [sp, I32]
+    lib.mla_workspace_bytes_bound.restype = U64
+    lib.mla_workspace_bytes_bound.argtypes = [sp, I32]
+    lib.mla_device_num_cus.restype = I32
+    lib.mla_device_num_cus.argtypes = [I32]
+    lib.mla_decode_plan.restype = I32
+    lib.mla_decode_plan.argtypes = [sp, P, P, I32, P, U64, ip]
+    lib.mla_decode_fwd.restype = I32
+    lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
+    lib.mla_combine.restype = I32
+    lib.mla_combine.argtypes = [sp, ip, P, P, U64, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mla_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MLAError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+@dataclass
+class Plan:
+    info: PlanInfo
+    host: np.ndarray          # int32 plan image
+    device: object            # torch int32 tensor on the GPU (or None before upload)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.info.workspace_bytes)
+
+    # Readers of the plan image (layout documented in csrc/plan_layout.h).
+    def wg_start(self) -> np.ndarray:
+        off, G = int(self.host[8]), int(self.host[2])
+        return self.host[off:off + G + 1]
+
+    def items(self) -> np.ndarray:
+        """[num_items, 5]: b, row0, k0, k1, slot (-1 = direct output)."""
+        off, n = int(self.host[9]), int(self.host[3])
+        return self.host[off:off + 8 * n].reshape(n, 8)[:, :5]
+
+    def combine_entries(self) -> np.ndarray:
+        """[num_combine, 4]: b, row0, first_slot, n_splits."""
+        off, n = int(self.host[10]), int(self.host[4])
+        return self.host[off:off + 4 * n].reshape(n, 4)
+
+
+def plan(shape: Shape, kv_lens_host, q_lens_host=None, num_workgroups: Optional[int] = None,
+         device=None, upload: bool = True) -> Plan:
+    """Run the host planner and (optionally) copy the plan image to the GPU."""
+    lib = load_library()
+    kv = np.ascontiguousarray(np.asarray(kv_lens_host, dtype=np.int32))
+    ql = None if q_lens_host is None else np.ascontiguousarray(np.asarray(q_lens_host, np.int32))
+    if num_workgroups is None:
+        dev = 0
+        if device is not None:
+            import torch
+            dev = torch.device(device).index or 0
+        num_workgroups = lib.mla_device_num_cus(dev)
+        if num_workgroups <= 0:
+            raise MLAError(-num_workgroups, "mla_device_num_cus")
+    nbytes = lib.mla_plan_bytes_bound(ctypes.byref(shape), int(num_workgroups))
+    if nbytes == 0:
+        # let the planner report why the shape is rejected
+        nbytes = 64
+    host = np.zeros((nbytes + 3) // 4, dtype=np.int32)
+    info = PlanInfo()
+    st = lib.mla_decode_plan(ctypes.byref(shape), kv.ctypes.data if kv.size else None,
+                             None if ql is None else ql.ctypes.data, int(num_workgroups),
+                             host.ctypes.data, host.nbytes, ctypes.byref(info))
+    _check(st, "mla_decode_plan")
+    host = host[: info.plan_bytes // 4].copy()
+    dev_t = None
+    if upload:
+        import torch
+        dev_t = torch.from_numpy(host).to(device or "cuda")
+    return Plan(info=info, host=host, device=dev_t)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode_fwd(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm_scale: float,
+               out, lse, workspace, kv_scale=None, stream=None):
+    """Launch the main kernel (``mla_decode_fwd``) on torch device tensors."""
+    lib = load_library()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(pl.info), _ptr(pl.device), _ptr(q),
+                            _ptr(kv_cache), _ptr(kv_scale), _ptr(block_table), _ptr(kv_lens),
+                            _ptr(q_lens), float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                            ws_bytes, _stream(stream))
+    _check(st, "mla_decode_fwd")
+
+
+def combine(shape: Shape, pl: Plan, workspace, q_lens, out, lse, stream=None):
+    """Launch the partial merge (``mla_combine``)."""
+    lib = load_library()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.mla_combine(ctypes.byref(shape), ctypes.byref(pl.info), _ptr(pl.device),
+                         _ptr(workspace), ws_bytes, _ptr(q_lens), _ptr(out), _ptr(lse),
+                         _stream(stream))
+    _check(st, "mla_combine")
+
+
+def alloc_workspace(pl: Plan, device="cuda"):
+    import torch
+    n = max(1, (pl.workspace_bytes + 255) // 256 * 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm_scale: float, *,
+           kv_scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Full decode step: main kernel, then the combine of split row blocks.
+
+    q [B, q_max, H, 576] bf16; kv_cache [pages, P, 576] bf16 (or uint8 e4m3 with
+    kv_scale [pages, P] fp32); block_table [B, max_pages] int32; kv_lens / q_lens
+    [B] int32 on the device.  Returns (out [B, q_max, H, 512] bf16, lse fp32)."""
+    import torch
+    B, qmax, H = shape.batch, shape.max_q_len, shape.num_heads
+    dev = q.device
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bfloat16 tensor")
+    if tuple(q.shape) != (B, qmax, H, D_LATENT + D_ROPE):
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the shape struct")
+    for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("kv_lens", kv_lens)):
+        if not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be contiguous and on {dev}")
+    if out is None:
+        out = torch.empty((B, qmax, H, D_LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, qmax, H), dtype=torch.float32, device=dev)
+    if workspace is None and pl.info.num_partials > 0:
+        workspace = alloc_workspace(pl, dev)
+    decode_fwd(shape, pl, q, kv_cache, block_table, kv_lens, q_lens, sm_scale, out, lse,
+               workspace, kv_scale=kv_scale, stream=stream)
+    combine(shape, pl, workspace, q_lens, out, lse, stream=stream)
+    return out, lse

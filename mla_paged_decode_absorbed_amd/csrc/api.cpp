@@ -1,0 +1,163 @@
+// C-ABI entry points: argument checks, then one launch each.  No allocation,
+// no host synchronisation, no mutable global state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+#include "mla_decode.h"
+#include "plan_layout.h"
+#include "validate.h"
+
+using namespace mla;
+
+namespace {
+
+int ilog2(int32_t x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+mla_status check_info(const mla_shape* s, const mla_plan_info* info) {
+  if (!info) return MLA_ERR_NULL_ARG;
+  if (info->num_workgroups < 1 || info->num_items < 0 || info->num_partials < 0 ||
+      info->num_combine < 0 || info->rows_per_block != kRowsPerBlock ||
+      info->tile_tokens != tile_tokens_for(s->kv_dtype))
+    return MLA_ERR_BAD_PLAN;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case MLA_ERR_BAD_SHAPE: return "inconsistent shape or lengths";
+    case MLA_ERR_UNSUPPORTED: return "shape or dtype has no built kernel";
+    case MLA_ERR_MISALIGNED: return "device pointer is not 16-byte aligned";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the plan needs";
+    case MLA_ERR_PLAN_TOO_SMALL: return "plan buffer smaller than the plan needs";
+    case MLA_ERR_BAD_PLAN: return "plan info does not match the shape";
+    case MLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+uint64_t mla_plan_bytes_bound(const mla_shape* shape, int32_t num_workgroups) {
+  if (validate_shape(shape) != MLA_OK || num_workgroups < 1) return 0;
+  return plan_words_bound(*shape, num_workgroups) * sizeof(int32_t);
+}
+
+uint64_t mla_workspace_bytes_bound(const mla_shape* shape, int32_t num_workgroups) {
+  if (validate_shape(shape) != MLA_OK || num_workgroups < 1) return 0;
+  return partial_bytes(2 * int64_t(num_workgroups));
+}
+
+int32_t mla_device_num_cus(int32_t device) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return -int32_t(MLA_ERR_HIP);
+  return n;
+}
+
+mla_status mla_decode_plan(const mla_shape* shape, const int32_t* kv_lens_host,
+                           const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
+                           uint64_t plan_bytes, mla_plan_info* info) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  if ((shape->batch > 0 && !kv_lens_host) || !plan_host || !info) return MLA_ERR_NULL_ARG;
+  if (num_workgroups < 1) return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(plan_host) & 3u) != 0) return MLA_ERR_MISALIGNED;
+  st = validate_lengths(shape, kv_lens_host, q_lens_host);
+  if (st != MLA_OK) return st;
+  return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
+                    static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info);
+}
+
+mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, const void* plan_dev,
+                          const void* q, const void* kv_cache, const float* kv_scale,
+                          const int32_t* block_table, const int32_t* kv_lens,
+                          const int32_t* q_lens, float softmax_scale, void* o, float* lse,
+                          void* workspace, uint64_t workspace_bytes, mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  st = check_info(shape, info);
+  if (st != MLA_OK) return st;
+  if (shape->batch == 0 || info->num_items == 0) return MLA_OK;
+  if (!plan_dev || !q || !kv_cache || !block_table || !kv_lens || !o) return MLA_ERR_NULL_ARG;
+  if (shape->kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale) return MLA_ERR_NULL_ARG;
+  if (info->num_partials > 0 && !workspace) return MLA_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(o) || !aligned16(plan_dev) ||
+      (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) ||
+      (kv_scale && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return MLA_ERR_MISALIGNED;
+  if (workspace_bytes < info->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+
+  DecodeArgs a{};
+  a.plan = static_cast<const int32_t*>(plan_dev);
+  a.q = static_cast<const uint8_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.q_lens = q_lens;
+  a.o = static_cast<uint8_t*>(o);
+  a.lse = lse;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    uint64_t(info->num_partials) * kRowsPerBlock *
+                                                        kDLatent * sizeof(float))
+                         : nullptr;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.num_heads = shape->num_heads;
+  a.max_q_len = shape->max_q_len;
+  a.page_shift = ilog2(shape->page_size);
+  a.max_pages = shape->max_pages_per_seq;
+  a.causal = shape->causal;
+  a.num_wg = info->num_workgroups;
+  return launch_decode(a, shape->kv_dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info, const void* plan_dev,
+                       const void* workspace, uint64_t workspace_bytes, const int32_t* q_lens,
+                       void* o, float* lse, mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  st = check_info(shape, info);
+  if (st != MLA_OK) return st;
+  if (info->num_combine == 0 || shape->batch == 0) return MLA_OK;
+  if (!plan_dev || !workspace || !o) return MLA_ERR_NULL_ARG;
+  if (!aligned16(o) || !aligned16(plan_dev) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return MLA_ERR_MISALIGNED;
+  if (workspace_bytes < info->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  CombineArgs a{};
+  a.plan = static_cast<const int32_t*>(plan_dev);
+  a.part_o = static_cast<const float*>(workspace);
+  a.part_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                              uint64_t(info->num_partials) * kRowsPerBlock *
+                                                  kDLatent * sizeof(float));
+  a.q_lens = q_lens;
+  a.o = static_cast<uint8_t*>(o);
+  a.lse = lse;
+  a.num_heads = shape->num_heads;
+  a.max_q_len = shape->max_q_len;
+  a.num_combine = info->num_combine;
+  return launch_combine(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
+                                                                                 : MLA_ERR_HIP;
+}
+
+}  // extern "C"

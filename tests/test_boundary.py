@@ -1,0 +1,211 @@
+"""C-ABI boundary checks that need no GPU: the library loads and exports its
+symbols, the planner's schedule is a valid partition, and argument validation
+returns the documented status codes before any device work."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import mla_paged_decode_absorbed_amd as mla
+
+HEADER = "include/mla_decode.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    import os, re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    decl = open(os.path.join(root, HEADER)).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(mla_[a-z_0-9]+)\(", decl, re.M))
+    assert names == set(mla.EXPORTED_SYMBOLS)
+    dyn = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", dyn, re.M), n
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for st in range(9):
+        assert len(mla.status_string(st)) >= 2
+    assert mla.status_string(99) == "unknown status"
+
+
+def _shape(B=4, H=128, qmax=1, P=64, pages=1000, maxp=200, kvd=mla.KV_BF16, causal=True, **kw):
+    return mla.Shape.make(batch=B, num_heads=H, max_q_len=qmax, page_size=P, num_pages=pages,
+                          max_pages_per_seq=maxp, kv_dtype=kvd, causal=causal, **kw)
+
+
+def _check_partition(shape, pl, kv_lens, q_lens):
+    """Every (sequence, row block, key tile) is covered by exactly one item; the
+    pieces of a row block are contiguous and ordered; slots/combine agree."""
+    T = pl.info.tile_tokens
+    items = pl.items()
+    ws = pl.wg_start()
+    assert ws[0] == 0 and ws[-1] == len(items) and np.all(np.diff(ws) >= 0)
+    H = shape.num_heads
+    want = {}
+    for b in range(shape.batch):
+        q = shape.max_q_len if q_lens is None else int(q_lens[b])
+        for r0 in range(0, q * H, 128):
+            want[(b, r0)] = int(kv_lens[b])
+    got = {}
+    for it in items:
+        b, r0, k0, k1, slot = map(int, it)
+        got.setdefault((b, r0), []).append((k0, k1, slot))
+    assert set(got) == set(want)
+    comb = {(int(c[0]), int(c[1])): (int(c[2]), int(c[3])) for c in pl.combine_entries()}
+    used_slots = []
+    for key, pieces in got.items():
+        pieces.sort()
+        L = want[key]
+        assert pieces[0][0] == 0 and pieces[-1][1] == L
+        for (a0, a1, _), (b0, b1, _) in zip(pieces, pieces[1:]):
+            assert a1 == b0 and a0 < a1 and a0 % T == 0
+        if len(pieces) == 1:
+            assert pieces[0][2] == -1 and key not in comb
+        else:
+            first, n = comb[key]
+            assert n == len(pieces)
+            assert [p[2] for p in pieces] == list(range(first, first + n))
+            used_slots += [p[2] for p in pieces]
+    assert sorted(used_slots) == list(range(pl.info.num_partials))
+    assert pl.info.num_combine == len(comb)
+    return items
+
+
+@pytest.mark.parametrize("seed,B,qmax,lo,hi,kvd", [
+    (0, 64, 1, 1024, 4096, mla.KV_BF16),
+    (1, 128, 2, 512, 8192, mla.KV_BF16),
+    (2, 16, 1, 16384, 32768, mla.KV_FP8_E4M3),
+    (3, 7, 2, 2, 300, mla.KV_BF16),
+    (4, 1, 1, 1, 1, mla.KV_BF16),
+    (5, 300, 1, 64, 200, mla.KV_BF16),
+])
+def test_plan_partitions_and_balances(seed, B, qmax, lo, hi, kvd):
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    ql = rng.integers(1, qmax, size=B, endpoint=True).astype(np.int32) if qmax > 1 else None
+    kv = np.maximum(kv, 2 if qmax > 1 else 1).astype(np.int32)
+    maxp = int((kv.max() + 63) // 64)
+    shape = _shape(B=B, qmax=qmax, pages=int(((kv + 63) // 64).sum()), maxp=maxp, kvd=kvd)
+    pl = mla.plan(shape, kv, ql, num_workgroups=256, upload=False)
+    items = _check_partition(shape, pl, kv, ql)
+    # balance: per-workgroup tile cost within one item cost (+ a cut's slack) of the mean
+    T = pl.info.tile_tokens
+    ws = pl.wg_start()
+    cost = [sum((int(k1) - int(k0) + T - 1) // T + 4 for _, _, k0, k1, _ in items[ws[g]:ws[g + 1]])
+            for g in range(pl.info.num_workgroups)]
+    mean = sum(cost) / len(cost)
+    assert max(cost) <= np.ceil(mean) + 4 + 2
+    assert pl.info.num_workgroups <= 256
+    assert pl.info.workspace_bytes <= mla.load_library().mla_workspace_bytes_bound(
+        ctypes.byref(shape), 256)
+
+
+def test_plan_deterministic_and_mixed_q_lens():
+    kv = np.array([5, 4000, 70, 1, 9000], np.int32)
+    ql = np.array([2, 1, 2, 0, 1], np.int32)
+    shape = _shape(B=5, qmax=2, maxp=200)
+    a = mla.plan(shape, kv, ql, num_workgroups=32, upload=False)
+    b = mla.plan(shape, kv, ql, num_workgroups=32, upload=False)
+    assert np.array_equal(a.host, b.host)
+    items = _check_partition(shape, a, kv, ql)
+    assert not any(int(it[0]) == 3 for it in items)   # q_len 0 -> no work
+
+
+def test_non_causal_zero_length_gets_an_item():
+    shape = _shape(B=2, causal=False)
+    pl = mla.plan(shape, np.array([0, 100], np.int32), num_workgroups=8, upload=False)
+    items = pl.items()
+    assert any(int(it[0]) == 0 and int(it[2]) == 0 and int(it[3]) == 0 for it in items)
+
+
+@pytest.mark.parametrize("kw,kv,ql,status", [
+    (dict(d_latent=256), [10], None, 3),
+    (dict(P=16), [10], None, 3),
+    (dict(P=48), [10], None, 3),
+    (dict(P=32, kvd=mla.KV_FP8_E4M3), [10], None, 3),
+    (dict(kvd=7), [10], None, 3),
+    (dict(qmax=9), [10], None, 3),
+    (dict(H=0), [10], None, 2),
+    (dict(maxp=1), [65], None, 2),            # kv_len beyond the block-table capacity
+    (dict(qmax=2), [1], [2], 2),              # causal: kv_len < q_len
+    (dict(qmax=2), [5], [3], 2),              # q_len > max_q_len
+    (dict(), [-1], None, 2),
+])
+def test_plan_rejects(kw, kv, ql, status):
+    shape = _shape(B=1, **kw)
+    with pytest.raises(mla.MLAError) as e:
+        mla.plan(shape, np.array(kv, np.int32), None if ql is None else np.array(ql, np.int32),
+                 num_workgroups=8, upload=False)
+    assert e.value.status == status
+
+
+def test_plan_buffer_too_small(lib):
+    shape = _shape(B=3)
+    kv = np.array([100, 200, 300], np.int32)
+    buf = np.zeros(8, np.int32)
+    info = mla.PlanInfo()
+    st = lib.mla_decode_plan(ctypes.byref(shape), kv.ctypes.data, None, 8, buf.ctypes.data,
+                             buf.nbytes, ctypes.byref(info))
+    assert st == 6
+    st = lib.mla_decode_plan(None, kv.ctypes.data, None, 8, buf.ctypes.data, buf.nbytes,
+                             ctypes.byref(info))
+    assert st == 1
+
+
+class _FakeTensor:
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_fwd_and_combine_validate_before_any_launch(lib):
+    shape = _shape(B=2)
+    pl = mla.plan(shape, np.array([100, 3000], np.int32), num_workgroups=64, upload=False)
+    info = pl.info
+    A = 0x10000   # aligned fake device addresses; never dereferenced on these paths
+    args = dict(plan=A, q=A, kv=A, scale=None, bt=A, kvl=A, ql=None, o=A, lse=A, ws=A)
+
+    def fwd(**over):
+        a = {**args, **over}
+        return lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(info), a["plan"], a["q"],
+                                  a["kv"], a["scale"], a["bt"], a["kvl"], a["ql"], 0.07, a["o"],
+                                  a["lse"], a["ws"], a.get("wsb", 0), None)
+
+    assert fwd(q=None) == 1
+    assert fwd(o=None) == 1
+    assert fwd(q=A + 8) == 4
+    assert fwd(ws=A + 16, wsb=1 << 40) == 4 if info.num_partials else True
+    if info.num_partials:
+        assert fwd(wsb=16) == 5
+    bad = mla.PlanInfo.from_buffer_copy(info)
+    bad.tile_tokens = 64
+    assert lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(bad), A, A, A, None, A, A, None,
+                              0.07, A, A, A, 1 << 40, None) == 7
+    fp8 = _shape(B=2, kvd=mla.KV_FP8_E4M3)
+    pl8 = mla.plan(fp8, np.array([100, 3000], np.int32), num_workgroups=64, upload=False)
+    assert lib.mla_decode_fwd(ctypes.byref(fp8), ctypes.byref(pl8.info), A, A, A, None, A, A,
+                              None, 0.07, A, A, A, 1 << 40, None) == 1   # missing scales
+    if info.num_combine:
+        assert lib.mla_combine(ctypes.byref(shape), ctypes.byref(info), A, None, 1 << 40, None, A,
+                               A, None) == 1
+        assert lib.mla_combine(ctypes.byref(shape), ctypes.byref(info), A, A, 16, None, A, A,
+                               None) == 5
+
+
+def test_empty_batch_is_a_noop(lib):
+    shape = _shape(B=0)
+    pl = mla.plan(shape, np.zeros(0, np.int32), num_workgroups=8, upload=False)
+    assert pl.info.num_items == 0
+    assert lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(pl.info), None, None, None, None,
+                              None, None, None, 1.0, None, None, None, 0, None) == 0
