@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of weight-absorbed MLA paged decode on one MI355X.
+
+One step = one decode call over one batch: the main kernel (mla_decode_fwd)
+and the merge of split row blocks (mla_combine), with the split plan built on
+the host once per batch (a serving step reuses it for every layer; its host
+time is reported separately).  Inputs are seeded synthetic tensors with the
+workload's shapes, already resident in HBM.  Consecutive steps rotate over
+several copies of the inputs whose total size is well above the 256 MB
+Infinity Cache, so every step streams its cache from HBM.
+
+Prints ONE JSON line:
+  value       KV GB/s: cached latent bytes of the visible keys / device time per step
+  us_per_call device time per step (fwd + combine), from HIP events
+  roofline    dominant kernel (mla_decode_kernel): algorithmic bytes (or FLOPs)
+              per launch / its average launch time, against MI355X peak
+  cpu_baseline the float64 oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/call, KV HBM GB/s and % of roofline at DeepSeek-V3 shapes"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MALL_BYTES = 256 << 20
+KERNEL_SOURCES = ("decode_kernel.hip", "kernels.h", "plan_layout.h")
+DECODE_KERNEL = "mla_decode_kernel"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_counts(case):
+    """Algorithmic bytes and FLOPs of one decode call.
+
+    Bytes: every visible cached row once (bf16: 1152 B; e4m3: 576 B + a 4 B
+    scale), every valid query row (1152 B), output row (1024 B) and LSE (4 B),
+    the block-table entries in use and the two length arrays.
+    FLOPs: 2 * (576 + 512) per (query row, visible key)."""
+    H, D, Dv, P = case.num_heads, case.d_qk, case.d_latent, case.page_size
+    kv_row = D * 2 if case.kv_dtype == "bf16" else D + 4
+    kv_tokens = int(case.kv_lens.astype("int64").sum())
+    rows = int(case.q_lens.astype("int64").sum()) * H
+    pages = sum((int(L) + P - 1) // P for L in case.kv_lens)
+    kv_bytes = kv_tokens * kv_row
+    other = rows * (D * 2 + Dv * 2 + 4) + pages * 4 + case.batch * 8
+    visible = 0
+    for L, qb in zip(case.kv_lens, case.q_lens):
+        for t in range(int(qb)):
+            visible += max(0, int(L) - int(qb) + t + 1) if case.causal else int(L)
+    flops = 2 * visible * H * (D + Dv)
+    return dict(kv_bytes=kv_bytes, alg_bytes=kv_bytes + other, flops=flops,
+                kv_tokens=kv_tokens, rows=rows)
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{DECODE_KERNEL}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(case, seconds: float, kv_bytes_total: int):
+    """Time the float64 oracle on the sequences of the same workload, taken in
+    order (and cycling) until ``seconds`` have passed."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        import threadpoolctl
+    except ImportError:   # pragma: no cover
+        threadpoolctl = None
+    done = 0
+    tokens = 0
+    order = [b for b in range(case.batch) if int(case.q_lens[b]) > 0]
+    t0 = time.perf_counter()
+    while order and time.perf_counter() - t0 < seconds:
+        b = order[done % len(order)]
+        oracle.mla_decode_ref_seq(case, b)
+        done += 1
+        tokens += int(case.kv_lens[b])
+    el = time.perf_counter() - t0
+    threads = 1
+    if threadpoolctl is not None:
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = int(info[0].get("num_threads", 1))
+    row = case.d_qk * 2 if case.kv_dtype == "bf16" else case.d_qk + 4
+    gbs = tokens * row / el / 1e9
+    frac = tokens * row / kv_bytes_total
+    return {
+        "value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"float64 numpy oracle, {done} sequence evaluations taken in order "
+                   f"(cycling) from the {case.batch} of the workload = {frac:.2f}x its KV "
+                   f"tokens, in {el:.1f} s; "
+                   f"os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"),
+        "us_per_call_equiv": round(el / max(frac, 1e-12) * 1e6, 1),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v3_decode_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this decode path runs on a single MI355X "
+              "(sharding by sequence is a design note, not built). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_absorbed_amd as mla
+    from workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    mla.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"workload {args.workload}: generating inputs")
+    case = workload(args.workload)
+    cnt = workload_counts(case)
+    kvd = mla.KV_BF16 if case.kv_dtype == "bf16" else mla.KV_FP8_E4M3
+    shape = mla.Shape.make(batch=case.batch, num_heads=case.num_heads, max_q_len=case.max_q_len,
+                           page_size=case.page_size, num_pages=case.num_pages,
+                           max_pages_per_seq=case.max_pages, kv_dtype=kvd, causal=case.causal)
+    t0 = time.perf_counter()
+    for _ in range(20):
+        pl = mla.plan(shape, case.kv_lens, case.q_lens, device=dev, upload=False)
+    plan_us = (time.perf_counter() - t0) / 20 * 1e6
+    pl = mla.plan(shape, case.kv_lens, case.q_lens, device=dev)
+
+    # input sets: enough copies that consecutive steps miss the Infinity Cache
+    kv_np = case.kv.view(np.int16) if case.kv_dtype == "bf16" else case.kv
+    set_bytes = case.kv.nbytes + case.q.nbytes + case.batch * case.max_q_len * case.num_heads * 1024
+    nsets = max(2, math.ceil(3 * MALL_BYTES / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(dev)
+        kv = torch.from_numpy(kv_np).to(dev)
+        if case.kv_dtype == "bf16":
+            kv = kv.view(torch.bfloat16)
+        sc = None if case.kv_scale is None else torch.from_numpy(case.kv_scale).to(dev)
+        bt = torch.from_numpy(case.block_table).to(dev)
+        kvl = torch.from_numpy(case.kv_lens).to(dev)
+        ql = torch.from_numpy(case.q_lens).to(dev)
+        out = torch.empty((case.batch, case.max_q_len, case.num_heads, 512), dtype=torch.bfloat16,
+                          device=dev)
+        lse = torch.empty((case.batch, case.max_q_len, case.num_heads), dtype=torch.float32,
+                          device=dev)
+        sets.append((q, kv, sc, bt, kvl, ql, out, lse))
+    ws = mla.alloc_workspace(pl, dev) if pl.info.num_partials > 0 else None
+    stream = torch.cuda.current_stream()
+    log(f"plan: {pl.info.num_workgroups} workgroups, {pl.info.num_items} items, "
+        f"{pl.info.num_partials} partials, {pl.info.num_combine} combine; {nsets} input sets")
+
+    def step(k):
+        q, kv, sc, bt, kvl, ql, out, lse = sets[k % nsets]
+        mla.decode_fwd(shape, pl, q, kv, bt, kvl, ql, case.sm_scale, out, lse, ws, kv_scale=sc,
+                       stream=stream)
+
+    def step_combine(k):
+        q, kv, sc, bt, kvl, ql, out, lse = sets[k % nsets]
+        mla.combine(shape, pl, ws, ql, out, lse, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+        step_combine(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+        step_combine(k)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    step_ms = [ev[k][0].elapsed_time(ev[k][2]) for k in range(K)]
+    fwd_avg = sum(fwd_ms) / K
+    step_avg = sum(step_ms) / K
+    log(f"timed {K} steps: wall {wall * 1e3:.2f} ms, fwd avg {fwd_avg * 1e3:.2f} us, "
+        f"step avg {step_avg * 1e3:.2f} us")
+
+    # warm reference: one input set, the Infinity Cache may hold the cache
+    warm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for k in range(K):
+        warm[k][0].record(stream)
+        step(0)
+        step_combine(0)
+        warm[k][1].record(stream)
+    torch.cuda.synchronize()
+    warm_avg = sum(warm[k][0].elapsed_time(warm[k][1]) for k in range(K)) / K
+
+    t_step = step_avg * 1e-3
+    t_fwd = fwd_avg * 1e-3
+    kv_gbs = cnt["kv_bytes"] / t_step / 1e9
+    tflops = cnt["flops"] / t_step / 1e12
+    t_hbm = cnt["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = cnt["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        achieved, peak, unit, bound = cnt["alg_bytes"] / t_fwd / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = cnt["flops"] / t_fwd / 1e12, MFMA_BF16_PEAK_TFLOPS, \
+            "TFLOP/s", "mfma"
+    traffic = read_traffic(args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_avg, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "bf16+e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": case.batch, "num_heads": case.num_heads,
+            "d_qk": case.d_qk, "d_v": case.d_latent, "q_len_max": case.max_q_len,
+            "page_size": case.page_size, "kv_dtype": case.kv_dtype,
+            "kv_tokens": cnt["kv_tokens"], "kv_len_mean": round(float(case.kv_lens.mean()), 1),
+        },
+        "us_per_call": round(step_avg * 1e3, 2),
+        "us_fwd_kernel": round(fwd_avg * 1e3, 2),
+        "us_per_call_warm": round(warm_avg * 1e3, 2),
+        "tflops": round(tflops, 2),
+        "pct_roofline_call": round(100 * max(t_hbm, t_mfma) / t_step, 1),
+        "roofline": {
+            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": DECODE_KERNEL,
+            "alg_bytes_per_launch": cnt["alg_bytes"], "flops_per_launch": cnt["flops"],
+        },
+        "plan": {"host_us": round(plan_us, 1), "workgroups": pl.info.num_workgroups,
+                 "items": pl.info.num_items, "partials": pl.info.num_partials,
+                 "combine_blocks": pl.info.num_combine},
+        "wall_s_timed": round(wall, 4),
+        "input_sets": nsets,
+        "kernel_source_sha256": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: float64 oracle for about {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, cnt["kv_bytes"])
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
