@@ -143,6 +143,9 @@ def main() -> int:
     ap.add_argument("--workload", default="v3_decode_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --steps times "
+                         "(scales HBM byte counters against a kernel of known traffic)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -160,9 +163,19 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    mla.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n,
+                          "bytes_written_per_copy": n, "copies": max(1, args.steps)}))
+        return 0
+    mla.load_library()
 
     log(f"workload {args.workload}: generating inputs")
     case = workload(args.workload)

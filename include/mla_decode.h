@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 /* hipStream_t; NULL means the null stream of the current device. */
 typedef struct ihipStream_t* mla_stream_t;
@@ -72,7 +72,7 @@ typedef enum mla_kv_dtype {
 } mla_kv_dtype;
 
 /* Problem shape.  Built kernels: d_latent 512, d_rope 64, page_size a power of
- * two >= 32 (bf16) or >= 64 (fp8), 1 <= max_q_len <= MLA_MAX_Q_LEN, any
+ * two >= 16 (bf16) or >= 64 (fp8), 1 <= max_q_len <= MLA_MAX_Q_LEN, any
  * num_heads >= 1. */
 typedef struct mla_shape {
   int32_t batch;              /* B sequences                                       */
@@ -95,8 +95,9 @@ typedef struct mla_plan_info {
   int32_t num_items;          /* (sequence, row block, key range) work items       */
   int32_t num_partials;       /* partial (O, LSE) slots written to the workspace   */
   int32_t num_combine;        /* row blocks whose partials need merging            */
-  int32_t tile_tokens;        /* keys per pipeline tile                            */
-  int32_t rows_per_block;     /* query rows per work item (128)                    */
+  int32_t tile_tokens;        /* keys per pipeline tile (16)                       */
+  int32_t rows_per_block;     /* query rows per planner unit / partial slot (128)  */
+  int32_t phases;             /* workgroups sharing a unit's keys: 1, 2 or 4       */
   uint64_t plan_bytes;        /* bytes of the plan image                           */
   uint64_t workspace_bytes;   /* workspace bytes this plan needs                   */
 } mla_plan_info;
@@ -119,12 +120,16 @@ int32_t mla_device_num_cus(int32_t device);
 /*
  * Split-KV planner (host only, no HIP call).
  *
- * Splits sum_b ceil(q_b * H / 128) row blocks x ceil(L_b / tile) key tiles into
+ * Splits sum_b ceil(q_b * H / 128) row blocks x ceil(L_b / 64) key rounds into
  * work items and deals them to num_workgroups persistent workgroups so that
- * each gets about the same number of tiles (a fixed per-item cost included).
- * A row block whose key range is cut gets one partial slot per piece and a
- * combine entry.  Key splitting with a log-sum-exp merge follows the split-K
- * remark of the FlashAttention-3 page (chapter 2).
+ * each gets about the same number of rounds (a fixed per-item cost included).
+ * When there are few row blocks, groups of 2 or 4 workgroups on one XCD share
+ * a block (each takes 64 or 32 of its rows over the same keys, which then come
+ * from HBM once); info->phases reports the group size.  A row block whose key
+ * range is cut gets one partial slot per piece and a combine entry.  Key
+ * splitting with a log-sum-exp merge follows the split-K remark of the
+ * FlashAttention-3 page (chapter 2).  MLA_PHASES (1, 2, 4) forces the group
+ * size and MLA_NUM_WORKGROUPS the workgroup count (tuning and tests).
  *
  *   kv_lens_host [B]  keys per sequence, including this step's q_b tokens.
  *   q_lens_host  [B]  query tokens per sequence (0..max_q_len); NULL means

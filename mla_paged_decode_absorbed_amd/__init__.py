@@ -67,6 +67,7 @@ class PlanInfo(ctypes.Structure):
         ("num_workgroups", ctypes.c_int32), ("num_items", ctypes.c_int32),
         ("num_partials", ctypes.c_int32), ("num_combine", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+        ("phases", ctypes.c_int32),
         ("plan_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -135,9 +136,14 @@ class Plan:
         return self.host[off:off + G + 1]
 
     def items(self) -> np.ndarray:
-        """[num_items, 5]: b, row0, k0, k1, slot (-1 = direct output)."""
+        """[num_items, 6]: b, row0, k0, k1, slot (-1 = direct output), row offset
+        of the item inside its 128-row unit (and partial slot)."""
         off, n = int(self.host[9]), int(self.host[3])
-        return self.host[off:off + 8 * n].reshape(n, 8)[:, :5]
+        return self.host[off:off + 8 * n].reshape(n, 8)[:, :6]
+
+    @property
+    def phases(self) -> int:
+        return int(self.info.phases)
 
     def combine_entries(self) -> np.ndarray:
         """[num_combine, 4]: b, row0, first_slot, n_splits."""

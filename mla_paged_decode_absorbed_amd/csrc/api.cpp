@@ -25,7 +25,8 @@ mla_status check_info(const mla_shape* s, const mla_plan_info* info) {
   if (!info) return MLA_ERR_NULL_ARG;
   if (info->num_workgroups < 1 || info->num_items < 0 || info->num_partials < 0 ||
       info->num_combine < 0 || info->rows_per_block != kRowsPerBlock ||
-      info->tile_tokens != tile_tokens_for(s->kv_dtype))
+      info->tile_tokens != tile_tokens_for(s->kv_dtype) ||
+      (info->phases != 1 && info->phases != 2 && info->phases != 4))
     return MLA_ERR_BAD_PLAN;
   return MLA_OK;
 }
@@ -125,6 +126,7 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   a.max_pages = shape->max_pages_per_seq;
   a.causal = shape->causal;
   a.num_wg = info->num_workgroups;
+  a.phases = info->phases;
   return launch_decode(a, shape->kv_dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;

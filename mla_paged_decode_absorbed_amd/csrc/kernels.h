@@ -24,6 +24,7 @@ struct DecodeArgs {
   int32_t max_pages;
   int32_t causal;
   int32_t num_wg;
+  int32_t phases;             // waves sharing one row group (1, 2 or 4)
 };
 
 struct CombineArgs {

@@ -18,7 +18,7 @@ inline mla_status validate_shape(const mla_shape* s) {
   if (s->kv_dtype != MLA_KV_BF16 && s->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
   if (s->d_latent != kDLatent || s->d_rope != kDRope) return MLA_ERR_UNSUPPORTED;
   if (s->max_q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
-  if (!is_pow2(s->page_size) || s->page_size < tile_tokens_for(s->kv_dtype))
+  if (!is_pow2(s->page_size) || s->page_size < min_page_size_for(s->kv_dtype))
     return MLA_ERR_UNSUPPORTED;
   if (s->causal != 0 && s->causal != 1) return MLA_ERR_BAD_SHAPE;
   // 32-bit row indexing inside the kernels

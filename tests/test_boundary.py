@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for st in range(9):
         assert len(mla.status_string(st)) >= 2
     assert mla.status_string(99) == "unknown status"
@@ -43,38 +43,54 @@ def _shape(B=4, H=128, qmax=1, P=64, pages=1000, maxp=200, kvd=mla.KV_BF16, caus
 
 
 def _check_partition(shape, pl, kv_lens, q_lens):
-    """Every (sequence, row block, key tile) is covered by exactly one item; the
-    pieces of a row block are contiguous and ordered; slots/combine agree."""
-    T = pl.info.tile_tokens
+    """Every (sequence, query row, key round) is covered by exactly one item; the
+    pieces of a 128-row unit are contiguous and ordered, split at round
+    boundaries; the workgroups of one piece share its key range and cover
+    disjoint row slices; slots/combine agree."""
+    R_TOK = 64
     items = pl.items()
     ws = pl.wg_start()
+    PH = pl.phases
+    assert PH in (1, 2, 4)
     assert ws[0] == 0 and ws[-1] == len(items) and np.all(np.diff(ws) >= 0)
     H = shape.num_heads
     want = {}
     for b in range(shape.batch):
         q = shape.max_q_len if q_lens is None else int(q_lens[b])
         for r0 in range(0, q * H, 128):
-            want[(b, r0)] = int(kv_lens[b])
+            want[(b, r0)] = (int(kv_lens[b]), min(128, q * H - r0))
     got = {}
-    for it in items:
-        b, r0, k0, k1, slot = map(int, it)
-        got.setdefault((b, r0), []).append((k0, k1, slot))
+    for g in range(pl.info.num_workgroups):
+        for it in items[ws[g]:ws[g + 1]]:
+            b, row0, k0, k1, slot, off = map(int, it)
+            assert off % (128 // PH) == 0 and 0 <= off < 128
+            # the workgroups of one piece are consecutive and start on a multiple of PH
+            assert g % PH == off // (128 // PH)
+            got.setdefault((b, row0 - off), []).append((k0, k1, slot, off, g // PH))
     assert set(got) == set(want)
     comb = {(int(c[0]), int(c[1])): (int(c[2]), int(c[3])) for c in pl.combine_entries()}
     used_slots = []
-    for key, pieces in got.items():
-        pieces.sort()
-        L = want[key]
-        assert pieces[0][0] == 0 and pieces[-1][1] == L
-        for (a0, a1, _), (b0, b1, _) in zip(pieces, pieces[1:]):
-            assert a1 == b0 and a0 < a1 and a0 % T == 0
-        if len(pieces) == 1:
-            assert pieces[0][2] == -1 and key not in comb
+    for key, parts in got.items():
+        L, rows = want[key]
+        n_sub = -(-rows // (128 // PH))
+        pieces = {}
+        for k0, k1, slot, off, proc in parts:
+            pieces.setdefault((k0, k1, slot), []).append((off, proc))
+        for (k0, k1, slot), subs in pieces.items():
+            offs = sorted(o for o, _ in subs)
+            assert offs == [i * (128 // PH) for i in range(n_sub)]
+            assert len({p for _, p in subs}) == 1     # one processor per piece
+        ranges = sorted(pieces)
+        assert ranges[0][0] == 0 and ranges[-1][1] == L
+        for (a0, a1, _), (b0, b1, _) in zip(ranges, ranges[1:]):
+            assert a1 == b0 and a0 < a1 and b0 % R_TOK == 0
+        if len(ranges) == 1:
+            assert ranges[0][2] == -1 and key not in comb
         else:
             first, n = comb[key]
-            assert n == len(pieces)
-            assert [p[2] for p in pieces] == list(range(first, first + n))
-            used_slots += [p[2] for p in pieces]
+            assert n == len(ranges)
+            assert [p[2] for p in ranges] == list(range(first, first + n))
+            used_slots += [p[2] for p in ranges]
     assert sorted(used_slots) == list(range(pl.info.num_partials))
     assert pl.info.num_combine == len(comb)
     return items
@@ -97,13 +113,12 @@ def test_plan_partitions_and_balances(seed, B, qmax, lo, hi, kvd):
     shape = _shape(B=B, qmax=qmax, pages=int(((kv + 63) // 64).sum()), maxp=maxp, kvd=kvd)
     pl = mla.plan(shape, kv, ql, num_workgroups=256, upload=False)
     items = _check_partition(shape, pl, kv, ql)
-    # balance: per-workgroup tile cost within one item cost (+ a cut's slack) of the mean
-    T = pl.info.tile_tokens
+    # balance: per-workgroup round cost within one item cost (+ a cut's slack) of the mean
     ws = pl.wg_start()
-    cost = [sum((int(k1) - int(k0) + T - 1) // T + 4 for _, _, k0, k1, _ in items[ws[g]:ws[g + 1]])
+    cost = [sum((int(it[3]) - int(it[2]) + 63) // 64 + 2 for it in items[ws[g]:ws[g + 1]])
             for g in range(pl.info.num_workgroups)]
     mean = sum(cost) / len(cost)
-    assert max(cost) <= np.ceil(mean) + 4 + 2
+    assert max(cost) <= np.ceil(mean) + 2 + 2
     assert pl.info.num_workgroups <= 256
     assert pl.info.workspace_bytes <= mla.load_library().mla_workspace_bytes_bound(
         ctypes.byref(shape), 256)
@@ -129,7 +144,7 @@ def test_non_causal_zero_length_gets_an_item():
 
 @pytest.mark.parametrize("kw,kv,ql,status", [
     (dict(d_latent=256), [10], None, 3),
-    (dict(P=16), [10], None, 3),
+    (dict(P=8), [10], None, 3),
     (dict(P=48), [10], None, 3),
     (dict(P=32, kvd=mla.KV_FP8_E4M3), [10], None, 3),
     (dict(kvd=7), [10], None, 3),
@@ -190,6 +205,10 @@ def test_fwd_and_combine_validate_before_any_launch(lib):
         assert fwd(wsb=16) == 5
     bad = mla.PlanInfo.from_buffer_copy(info)
     bad.tile_tokens = 64
+    assert lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(bad), A, A, A, None, A, A, None,
+                              0.07, A, A, A, 1 << 40, None) == 7
+    bad = mla.PlanInfo.from_buffer_copy(info)
+    bad.phases = 3
     assert lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(bad), A, A, A, None, A, A, None,
                               0.07, A, A, A, 1 << 40, None) == 7
     fp8 = _shape(B=2, kvd=mla.KV_FP8_E4M3)

@@ -5,6 +5,7 @@ fp8-e4m3 cache 6e-2 and 2e-2; LSE |diff| <= 1e-3 (our bar; see DESIGN.md);
 indexing exact (bitwise-identical output under page relayout for a fixed plan).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -48,10 +49,29 @@ def shape_of(case: MLACase, block_table=None):
                           causal=case.causal)
 
 
-def run_gpu(case: MLACase, num_workgroups=None, block_table=None, pl=None, repeats=1):
+def make_plan(shape, case, num_workgroups=None, phases=None):
+    """Host plan; ``phases`` forces the workgroup-group size (MLA_PHASES)."""
+    old = os.environ.get("MLA_PHASES")
+    try:
+        if phases is not None:
+            os.environ["MLA_PHASES"] = str(phases)
+        pl = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=num_workgroups)
+    finally:
+        if phases is not None:
+            if old is None:
+                del os.environ["MLA_PHASES"]
+            else:
+                os.environ["MLA_PHASES"] = old
+    if phases is not None:
+        assert pl.phases == phases
+    return pl
+
+
+def run_gpu(case: MLACase, num_workgroups=None, block_table=None, pl=None, repeats=1,
+            phases=None):
     shape = shape_of(case, block_table)
     if pl is None:
-        pl = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=num_workgroups)
+        pl = make_plan(shape, case, num_workgroups, phases)
     q, kv, sc, bt, kvl, ql = to_dev(case, block_table)
     outs = []
     for _ in range(repeats):
@@ -104,33 +124,40 @@ def check(case: MLACase, out, lse, seqs=None, tol=None):
 
 # ---------------------------------------------------------------- small, exhaustive
 
-@pytest.mark.parametrize("kv_lens", [[1], [31, 32, 33], [63, 64, 65, 127, 128, 129], [4097]])
-def test_bf16_q1_edge_lengths(kv_lens):
+PHASES = [1, 2, 4]
+
+
+@pytest.mark.parametrize("phases", PHASES)
+@pytest.mark.parametrize("kv_lens", [[1], [15, 16, 17], [63, 64, 65, 127, 128, 129], [4097]])
+def test_bf16_q1_edge_lengths(kv_lens, phases):
     case = make_case(kv_lens=kv_lens, seed=11, sm_scale=1 / math.sqrt(192))
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
+@pytest.mark.parametrize("phases", PHASES)
 @pytest.mark.parametrize("kv_lens", [[2, 3], [33, 64, 65], [300, 1000]])
-def test_bf16_q2_causal(kv_lens):
+def test_bf16_q2_causal(kv_lens, phases):
     case = make_case(kv_lens=kv_lens, q_lens=[2] * len(kv_lens), seed=12,
                      sm_scale=1 / math.sqrt(192))
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
-def test_bf16_mixed_q_lens_and_empty_sequence():
+@pytest.mark.parametrize("phases", PHASES)
+def test_bf16_mixed_q_lens_and_empty_sequence(phases):
     case = make_case(kv_lens=[70, 2, 900, 5, 129], q_lens=[1, 2, 2, 0, 1], max_q_len=2, seed=13,
                      sm_scale=1 / math.sqrt(192))
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
+@pytest.mark.parametrize("phases", [1, 4])
 @pytest.mark.parametrize("H,q", [(16, 1), (16, 2), (64, 2), (32, 4), (128, 4)])
-def test_head_counts_and_longer_drafts(H, q):
+def test_head_counts_and_longer_drafts(H, q, phases):
     case = make_case(kv_lens=[97, 640, 4], q_lens=[q, q, q], num_heads=H, seed=14,
                      sm_scale=1 / math.sqrt(192))
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
@@ -141,48 +168,56 @@ def test_non_causal_q2():
     check(case, out, lse)
 
 
-@pytest.mark.parametrize("P", [32, 128, 256])
+@pytest.mark.parametrize("P", [16, 32, 128, 256])
 def test_bf16_page_sizes(P):
     case = make_case(kv_lens=[1, 255, 700], page_size=P, seed=16, sm_scale=1 / math.sqrt(192))
     (out, lse), _ = run_gpu(case)
     check(case, out, lse)
 
 
-@pytest.mark.parametrize("nwg", [1, 2, 7, 64, 256, 1000])
-def test_forced_split_counts(nwg):
+@pytest.mark.parametrize("phases", PHASES)
+@pytest.mark.parametrize("nwg", [1, 4, 8, 64, 256, 1000])
+def test_forced_split_counts(nwg, phases):
+    if nwg % phases:
+        pytest.skip("workgroup count not a multiple of the group size")
     case = make_case(kv_lens=[3000, 700, 65, 1800], q_lens=[1, 2, 1, 2], seed=17,
                      sm_scale=1 / math.sqrt(192))
-    (out, lse), pl = run_gpu(case, num_workgroups=nwg)
+    (out, lse), pl = run_gpu(case, num_workgroups=nwg, phases=phases)
     check(case, out, lse)
-    if nwg >= 64:
+    if nwg >= 64 * phases:
         assert pl.info.num_combine > 0
 
 
-def test_peaky_softmax_rescale_path():
+@pytest.mark.parametrize("phases", PHASES)
+def test_peaky_softmax(phases):
+    # scores spread over hundreds of units: later tiles overshoot the first
+    # tile's reference max and restart their item
     case = make_case(kv_lens=[2000, 513], q_lens=[1, 2], seed=18, q_std=8.0,
                      sm_scale=1 / math.sqrt(192))
-    # a late, very large key forces the running max up by far more than 2^8
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
-def test_late_dominant_key():
+@pytest.mark.parametrize("phases", PHASES)
+def test_late_dominant_key(phases):
     case = make_case(kv_lens=[1500], q_lens=[1], seed=19, sm_scale=1 / math.sqrt(192))
     q = oracle.decode_bf16(case.q[0, 0])
-    # overwrite cached token 1400 with a scaled copy of head 0's query: huge score late
+    # overwrite cached token 1400 with a scaled copy of head 0's query: its
+    # score is far above every earlier one (forces a restart with a new max)
     L = 1400
     page, slot = case.block_table[0, L // 64], L % 64
     import torch as _t
     v = _t.from_numpy((q[0] * 0.25).astype(np.float32)).to(_t.bfloat16).view(_t.int16).numpy()
     case.kv[page, slot] = v.view(np.uint16)
-    (out, lse), _ = run_gpu(case, num_workgroups=1)
+    (out, lse), _ = run_gpu(case, num_workgroups=phases, phases=phases)
     check(case, out, lse)
 
 
-def test_fp8_small():
+@pytest.mark.parametrize("phases", PHASES)
+def test_fp8_small(phases):
     case = make_case(kv_lens=[1, 64, 65, 1000, 3000], q_lens=[1, 1, 2, 2, 1], kv_dtype="fp8_e4m3",
                      seed=20, sm_scale=1 / math.sqrt(192))
-    (out, lse), _ = run_gpu(case)
+    (out, lse), _ = run_gpu(case, phases=phases)
     check(case, out, lse)
 
 
@@ -210,11 +245,12 @@ def _relayout(case, seed):
     return MLACase(**{**case.__dict__, "kv": kv, "kv_scale": sc, "block_table": bt})
 
 
+@pytest.mark.parametrize("phases", [1, 4])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
-def test_page_relayout_is_bitwise_identical(kv_dtype):
+def test_page_relayout_is_bitwise_identical(kv_dtype, phases):
     case = make_case(kv_lens=[700, 64, 1234], q_lens=[2, 1, 1], kv_dtype=kv_dtype, seed=22,
                      sm_scale=1 / math.sqrt(192))
-    (o1, l1), pl = run_gpu(case, num_workgroups=16)
+    (o1, l1), pl = run_gpu(case, num_workgroups=16, phases=phases)
     c2 = _relayout(case, 5)
     (o2, l2), _ = run_gpu(c2, pl=pl)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
@@ -230,10 +266,11 @@ def test_unused_block_table_entries_never_read():
     check(case, out, lse)
 
 
-def test_repeat_runs_bitwise_equal():
+@pytest.mark.parametrize("phases", PHASES)
+def test_repeat_runs_bitwise_equal(phases):
     case = make_case(kv_lens=[2500, 900, 33], q_lens=[2, 1, 2], seed=24,
                      sm_scale=1 / math.sqrt(192))
-    runs, _ = run_gpu(case, num_workgroups=64, repeats=20)
+    runs, _ = run_gpu(case, num_workgroups=64, repeats=20, phases=phases)
     o0, l0 = runs[0]
     for o, l in runs[1:]:
         assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
