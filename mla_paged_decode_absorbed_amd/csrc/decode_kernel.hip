@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gfx950_asm.h"
 #include "kernels.h"
 #include "plan_layout.h"
 
@@ -56,8 +57,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_PTR(T) T __attribute__((address_space(3)))*
 
 constexpr int kThreads = 256;
 constexpr int kTileTok = 16;                  // keys per tile
@@ -99,33 +98,6 @@ __device__ __forceinline__ int slot_bf16(int r8, int c8, int rh) {
 }
 __device__ __forceinline__ int slot_fp8(int r, int cc) { return 16 * cc + (r ^ (8 * (cc & 1))); }
 
-// HBM -> LDS copy of 16 (or 4) bytes per lane: LDS destination = lds_base +
-// 16 (4) * lane, source = sbase + voff.  M0 is saved and restored.
-__device__ __forceinline__ void lds_dma_x4(uint32_t lds_base, int voff, const void* sbase) {
-  int tmp;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(tmp)
-      : "s"(lds_base), "v"(voff), "s"(sbase)
-      : "memory");
-}
-__device__ __forceinline__ void lds_dma_x1(uint32_t lds_base, int voff, const void* sbase) {
-  int tmp;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %2, %3 offset:0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(tmp)
-      : "s"(lds_base), "v"(voff), "s"(sbase)
-      : "memory");
-}
-
 // A wave-uniform pointer, kept in SGPRs (the copies take a scalar base).
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
@@ -133,15 +105,6 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
   return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
-}
-
-// Wait until at most N of this wave's vector-memory operations are in flight.
-// The "memory" clobber keeps later LDS reads after the wait.
-#define MLA_VM_WAIT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
-// Workgroup barrier that also completes this wave's LDS operations first, so
-// LDS stores (restart flag, merge slots) are visible to every wave after it.
-__device__ __forceinline__ void barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait for round j of this wave given `ahead` later rounds already issued
@@ -218,8 +181,7 @@ __device__ __forceinline__ void issue_round(const DmaCtx<KVD>& c, int j) {
   const uint32_t lds = c.ring + stage * C::TILE;
   // an opaque copy of the lane id keeps these offsets from being hoisted out
   // of the key loop (they would pin VGPRs for its whole duration)
-  int lane;
-  asm volatile("" : "=v"(lane) : "0"(c.lane));
+  const int lane = opaque(c.lane);
   if constexpr (KVD == 0) {
     // copy 2*cg + rh: rows 8rh.., chunks 8cg.. (row bytes 128cg .. 128cg+127)
     const int c8a = 2 * (lane >> 4), lo = (lane >> 3) & 1;
@@ -263,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(
   constexpr int RG = 4 / PH;          // row groups of 32 per item
   constexpr int NR = kRounds<KVD>;
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const uint32_t smem_base = (uint32_t)(uintptr_t)(LDS_PTR(char))smem;
+  const uint32_t smem_base = lds_address(smem);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

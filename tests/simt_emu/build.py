@@ -1,0 +1,61 @@
+"""Build tests/simt_emu/_build/run_case: the library's kernel sources compiled
+for the host CPU against the lane-thread emulator, with AddressSanitizer.
+
+The kernel sources are copied unchanged next to the emulator's version of
+gfx950_asm.h (the only file replaced), so the emulated code is the code the
+gfx950 library is built from.  Host-only: nothing here targets a GPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+CSRC = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "_build")
+BIN = os.path.join(OUT, "run_case")
+
+KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "api.cpp", "plan.cpp",
+                "kernels.h", "plan_layout.h", "validate.h"]
+
+
+def compiler() -> str:
+    for c in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("clang++ not found")
+
+
+def build(sanitize: bool = True) -> str:
+    src = os.path.join(OUT, "src")
+    os.makedirs(src, exist_ok=True)
+    for f in KERNEL_FILES:
+        shutil.copyfile(os.path.join(CSRC, f), os.path.join(src, f))
+    shutil.copyfile(os.path.join(HERE, "gfx950_asm.h"), os.path.join(src, "gfx950_asm.h"))
+    flags = ["-std=c++20", "-O1", "-g", "-pthread", "-fno-omit-frame-pointer",
+             f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument"]
+    if sanitize:
+        flags.append("-fsanitize=address")
+    units = [os.path.join(src, f) for f in ("decode_kernel.hip", "combine_kernel.hip",
+                                             "api.cpp", "plan.cpp")]
+    units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
+    objs = []
+    for u in units:
+        obj = os.path.join(OUT, os.path.basename(u) + ".o")
+        cmd = [compiler(), *flags, "-x", "c++", "-c", u, "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"emulator build failed on {u}:\n{res.stderr[-4000:]}")
+        objs.append(obj)
+    cmd = [compiler(), *flags, *objs, "-o", BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"emulator link failed:\n{res.stderr[-4000:]}")
+    return BIN
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,386 @@
+// Lane-thread runtime behind the host stand-in for <hip/hip_runtime.h>.
+//
+// Register layouts of the wave-level operations follow the CDNA3/CDNA4 ISA
+// documentation of the instructions the kernels use:
+//   v_mfma_f32_16x16x32_bf16: A row i = lane%16, k = 8*(lane/16)+e; B column
+//     j = lane%16, same k; D column j = lane%16, rows 4*(lane/16)+r.
+//   v_mfma_f32_32x32x16_bf16: A row i = lane%32, k = 8*(lane/32)+e; B column
+//     j = lane%32, same k; D column j = lane%32, rows 8*(r/4)+4*(lane/32)+r%4.
+//   ds_read_b64_tr_b16: in each 16-lane group, lane i names 4 bf16 of row i/4
+//     (elements 4*(i%4)..) of a 4 x 16 block and receives its column i.
+//   ds_read_b64_tr_b8: lane i names 8 bytes of row i/2 (bytes 8*(i%2)..) of an
+//     8 x 16 byte block and receives its column i.
+//   v_permlane16_swap(a, b): a' = rows {a0, b0, a2, b2}, b' = {a1, b1, a3, b3}
+//     of the four 16-lane rows; v_permlane32_swap: a' = {a.lo, b.lo}, b' =
+//     {a.hi, b.hi} of the two 32-lane halves.
+#include <hip/hip_runtime.h>
+#include <sanitizer/common_interface_defs.h>
+#include <sys/mman.h>
+
+#include <atomic>
+
+#include <cstdio>
+#include <cstdlib>
+#include <deque>
+#include <memory>
+#include <vector>
+
+thread_local EmuIdx threadIdx;
+thread_local EmuIdx blockIdx;
+
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+  *value = 256;
+  return hipSuccess;
+}
+hipError_t hipGetLastError() { return hipSuccess; }
+
+// Minimal x86-64 context switch: saves the callee-saved registers on the
+// current stack, stores the stack pointer to *save and resumes `to`.
+extern "C" void emu_ctx_switch(void** save, void* to);
+asm(R"(
+  .text
+  .globl emu_ctx_switch
+  .type emu_ctx_switch,@function
+emu_ctx_switch:
+  pushq %rbp
+  pushq %rbx
+  pushq %r12
+  pushq %r13
+  pushq %r14
+  pushq %r15
+  movq %rsp, (%rdi)
+  movq %rsi, %rsp
+  popq %r15
+  popq %r14
+  popq %r13
+  popq %r12
+  popq %rbx
+  popq %rbp
+  ret
+  .size emu_ctx_switch, .-emu_ctx_switch
+)");
+
+namespace emu {
+namespace {
+
+constexpr int kLdsLimit = 160 * 1024;      // LDS bytes of one CU
+constexpr size_t kStackBytes = 512 * 1024;  // per lane fiber
+
+[[noreturn]] void fail(const char* what) {
+  std::fprintf(stderr, "simt-emu: %s (block %u, thread %u)\n", what, blockIdx.x, threadIdx.x);
+  std::fflush(stderr);
+  std::abort();
+}
+
+struct Barrier {
+  int n = 0, count = 0;
+  unsigned gen = 0;
+};
+
+struct Wave {
+  Barrier bar;
+  alignas(64) unsigned char slot[64][128];
+};
+
+struct Pending {
+  unsigned char* dst;
+  unsigned char data[16];
+  int n;
+};
+
+struct Fiber {
+  void* sp = nullptr;
+  unsigned char* stack = nullptr;   // mapping incl. one guard page
+  int tid = 0, lane = 0;
+  Wave* wave = nullptr;
+  Barrier* wait_bar = nullptr;
+  unsigned wait_gen = 0;
+  bool done = false;
+  std::deque<Pending> dma;
+};
+
+struct Sched {
+  void* sp = nullptr;
+  const void* bottom = nullptr;
+  size_t size = 0;
+  Fiber* cur = nullptr;
+  Barrier block_bar;
+  std::vector<std::unique_ptr<Wave>> waves;
+  void (*body)(void*) = nullptr;
+  void* arg = nullptr;
+};
+Sched S;
+
+std::atomic<const unsigned char*> lds_base{nullptr};
+
+void apply(const Pending& p) { std::memcpy(p.dst, p.data, p.n); }
+
+void yield_to_scheduler(bool finishing) {
+  Fiber* f = S.cur;
+  void* fake = nullptr;
+  __sanitizer_start_switch_fiber(finishing ? nullptr : &fake, S.bottom, S.size);
+  emu_ctx_switch(&f->sp, S.sp);
+  __sanitizer_finish_switch_fiber(fake, &S.bottom, &S.size);
+}
+
+void wait_on(Barrier& b) {
+  const unsigned g = b.gen;
+  if (++b.count == b.n) {
+    b.count = 0;
+    ++b.gen;
+    return;
+  }
+  S.cur->wait_bar = &b;
+  S.cur->wait_gen = g;
+  yield_to_scheduler(false);
+}
+
+extern "C" void emu_fiber_entry() {
+  __sanitizer_finish_switch_fiber(nullptr, &S.bottom, &S.size);
+  Fiber* f = S.cur;
+  S.body(S.arg);
+  for (const Pending& p : f->dma) apply(p);   // the end of the program waits
+  f->dma.clear();
+  f->done = true;
+  yield_to_scheduler(true);
+  fail("finished fiber resumed");
+}
+
+template <typename T, typename F>
+auto wave_op(const T& in, F&& f) {
+  static_assert(sizeof(T) <= sizeof(Wave::slot[0]), "slot");
+  Fiber& me = *S.cur;
+  Wave& w = *me.wave;
+  std::memcpy(w.slot[me.lane], &in, sizeof(T));
+  wait_on(w.bar);
+  auto get = [&](int l) {
+    T x;
+    std::memcpy(&x, w.slot[l], sizeof(T));
+    return x;
+  };
+  auto r = f(me.lane, get);
+  wait_on(w.bar);
+  return r;
+}
+
+
+}  // namespace
+
+void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
+  const int nt = int(block.x * block.y * block.z);
+  if (nt % 64 != 0) fail("block size is not a multiple of 64");
+  const long page = 4096;
+  std::vector<Fiber> fib(nt);
+  for (Fiber& f : fib) {
+    void* m = mmap(nullptr, kStackBytes + page, PROT_READ | PROT_WRITE,
+                   MAP_PRIVATE | MAP_ANONYMOUS | MAP_NORESERVE, -1, 0);
+    if (m == MAP_FAILED) fail("cannot map a fiber stack");
+    mprotect(m, page, PROT_NONE);   // guard page below the stack
+    f.stack = static_cast<unsigned char*>(m);
+  }
+  S.body = body;
+  S.arg = arg;
+  for (unsigned bz = 0; bz < grid.z; ++bz)
+    for (unsigned by = 0; by < grid.y; ++by)
+      for (unsigned bx = 0; bx < grid.x; ++bx) {
+        S.block_bar = Barrier{nt, 0, 0};
+        S.waves.clear();
+        for (int w = 0; w < nt / 64; ++w) {
+          S.waves.push_back(std::make_unique<Wave>());
+          S.waves.back()->bar.n = 64;
+        }
+        for (int t = 0; t < nt; ++t) {
+          Fiber& f = fib[t];
+          f.tid = t;
+          f.lane = t & 63;
+          f.wave = S.waves[t >> 6].get();
+          f.wait_bar = nullptr;
+          f.done = false;
+          f.dma.clear();
+          // initial frame: six zeroed callee-saved registers, then the entry
+          uint64_t* top = reinterpret_cast<uint64_t*>(f.stack + page + kStackBytes);
+          top -= 2;
+          top[0] = reinterpret_cast<uint64_t>(&emu_fiber_entry);
+          top[1] = 0;
+          top -= 6;
+          for (int i = 0; i < 6; ++i) top[i] = 0;
+          f.sp = top;
+        }
+        int alive = nt;
+        while (alive > 0) {
+          bool progressed = false;
+          for (int t = 0; t < nt; ++t) {
+            Fiber& f = fib[t];
+            if (f.done) continue;
+            if (f.wait_bar && f.wait_bar->gen == f.wait_gen) continue;
+            f.wait_bar = nullptr;
+            threadIdx = EmuIdx{unsigned(t), 0u, 0u};
+            blockIdx = EmuIdx{bx, by, bz};
+            S.cur = &f;
+            void* fake = nullptr;
+            __sanitizer_start_switch_fiber(&fake, f.stack + page, kStackBytes);
+            emu_ctx_switch(&S.sp, f.sp);
+            __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
+            progressed = true;
+            if (f.done) --alive;
+          }
+          if (!progressed) fail("deadlock: every live lane waits at a barrier no lane can complete");
+        }
+      }
+  for (Fiber& f : fib) munmap(f.stack, kStackBytes + page);
+}
+
+uint32_t lds_address(const void* p) {
+  const unsigned char* c = static_cast<const unsigned char*>(p);
+  const unsigned char* expected = nullptr;
+  lds_base.compare_exchange_strong(expected, c);
+  const unsigned char* b = lds_base.load();
+  if (c < b || c - b >= kLdsLimit) fail("LDS address outside the shared array");
+  return uint32_t(c - b);
+}
+
+void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
+  const unsigned char* b = lds_base.load();
+  if (!b) fail("LDS copy before any LDS address was taken");
+  const uint64_t off = uint64_t(lds) + uint64_t(bytes) * S.cur->lane;
+  if (off + bytes > uint64_t(kLdsLimit)) fail("LDS copy destination beyond the LDS size");
+  Pending p;
+  p.dst = const_cast<unsigned char*>(b) + off;
+  p.n = bytes;
+  std::memcpy(p.data, static_cast<const unsigned char*>(sbase) + voff, bytes);   // checked read
+  S.cur->dma.push_back(p);
+}
+
+// s_waitcnt is per wave: every lane's copies land before any lane goes on.
+void vm_wait(int n) {
+  auto& q = S.cur->dma;
+  while (int(q.size()) > n) {
+    apply(q.front());
+    q.pop_front();
+  }
+  wait_on(S.cur->wave->bar);
+}
+
+void block_barrier() { wait_on(S.block_bar); }
+
+uint32_t readfirstlane(uint32_t v) {
+  return wave_op(v, [](int, auto get) { return get(0); });
+}
+
+int shfl_xor(int v, int mask) {
+  return wave_op(v, [mask](int l, auto get) { return get((l ^ mask) & 63); });
+}
+float shfl_xor(float v, int mask) {
+  return wave_op(v, [mask](int l, auto get) { return get((l ^ mask) & 63); });
+}
+
+int any(int pred) {
+  return wave_op(pred != 0, [](int, auto get) {
+    for (int l = 0; l < 64; ++l)
+      if (get(l)) return 1;
+    return 0;
+  });
+}
+
+emu_u32x2 permlane16_swap(uint32_t a, uint32_t b) {
+  struct AB { uint32_t a, b; };
+  return wave_op(AB{a, b}, [](int l, auto get) {
+    const int row = l >> 4;
+    emu_u32x2 r;
+    r[0] = (row & 1) ? get(l - 16).b : get(l).a;
+    r[1] = (row & 1) ? get(l).b : get(l + 16).a;
+    return r;
+  });
+}
+
+emu_u32x2 permlane32_swap(uint32_t a, uint32_t b) {
+  struct AB { uint32_t a, b; };
+  return wave_op(AB{a, b}, [](int l, auto get) {
+    emu_u32x2 r;
+    r[0] = l < 32 ? get(l).a : get(l - 32).b;
+    r[1] = l < 32 ? get(l + 32).a : get(l).b;
+    return r;
+  });
+}
+
+emu_f32x4 mfma16x16x32(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c) {
+  struct In { emu_bf16x8 a, b; };
+  const emu_f32x4 out = wave_op(In{a, b}, [](int l, auto get) {
+    emu_f32x4 d;
+    const int j = l & 15;
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * (l >> 4) + r;
+      float s = 0.f;
+      for (int k = 0; k < 32; ++k)
+        s += float(get(i + 16 * (k >> 3)).a[k & 7]) * float(get(j + 16 * (k >> 3)).b[k & 7]);
+      d[r] = s;
+    }
+    return d;
+  });
+  return out + c;
+}
+
+emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c) {
+  struct In { emu_bf16x8 a, b; };
+  const emu_f32x16 out = wave_op(In{a, b}, [](int l, auto get) {
+    emu_f32x16 d;
+    const int j = l & 31;
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      float s = 0.f;
+      for (int k = 0; k < 16; ++k)
+        s += float(get(i + 32 * (k >> 3)).a[k & 7]) * float(get(j + 32 * (k >> 3)).b[k & 7]);
+      d[r] = s;
+    }
+    return d;
+  });
+  return out + c;
+}
+
+emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
+  return wave_op(p, [](int l, auto get) {
+    const int g = l >> 4, i = l & 15;
+    emu_bf16x4 r;
+    for (int row = 0; row < 4; ++row) {
+      emu_bf16x4 v;
+      std::memcpy(&v, get(16 * g + 4 * row + (i >> 2)), sizeof v);   // checked 8-byte read
+      r[row] = v[i & 3];
+    }
+    return r;
+  });
+}
+
+emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p) {
+  return wave_op(p, [](int l, auto get) {
+    const int g = l >> 4, i = l & 15;
+    unsigned char out[8];
+    for (int row = 0; row < 8; ++row) {
+      unsigned char v[8];
+      std::memcpy(v, get(16 * g + 2 * row + (i >> 3)), 8);
+      out[row] = v[i & 7];
+    }
+    emu_i32x2 r;
+    std::memcpy(&r, out, 8);
+    return r;
+  });
+}
+
+// OCP e4m3 (FN variant: no infinities, S.1111.111 is NaN), bias 7.
+static float e4m3_to_f32(unsigned v) {
+  const unsigned s = (v >> 7) & 1, e = (v >> 3) & 15, m = v & 7;
+  float x;
+  if (e == 15 && m == 7) x = NAN;
+  else if (e == 0) x = std::ldexp(float(m), -9);
+  else x = std::ldexp(float(8 + m), int(e) - 10);
+  return s ? -x : x;
+}
+
+emu_f32x2 cvt_pk_f32_fp8(int v, bool hi) {
+  const unsigned u = unsigned(v) >> (hi ? 16 : 0);
+  emu_f32x2 r;
+  r[0] = e4m3_to_f32(u & 0xff);
+  r[1] = e4m3_to_f32((u >> 8) & 0xff);
+  return r;
+}
+
+}  // namespace emu

@@ -1,0 +1,30 @@
+// Emulator version of the kernel's inline-assembly helpers (same names and
+// signatures as the library's gfx950_asm.h): LDS-DMA copies are queued per
+// lane and land at the vmcnt waits; the barrier is a workgroup rendezvous.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LDS_PTR(T) T*
+
+namespace emu {
+uint32_t lds_address(const void* p);
+void lds_dma(uint32_t lds_base, int voff, const void* sbase, int bytes);
+void vm_wait(int n);
+void block_barrier();
+}  // namespace emu
+
+namespace mla {
+inline uint32_t lds_address(const void* p) { return emu::lds_address(p); }
+inline void lds_dma_x4(uint32_t lds_base, int voff, const void* sbase) {
+  emu::lds_dma(lds_base, voff, sbase, 16);
+}
+inline void lds_dma_x1(uint32_t lds_base, int voff, const void* sbase) {
+  emu::lds_dma(lds_base, voff, sbase, 4);
+}
+#define MLA_VM_WAIT(N) emu::vm_wait(N)
+inline void barrier() { emu::block_barrier(); }
+inline int opaque(int x) { return x; }
+template <typename T>
+inline void require_vgpr(const T&) {}
+}  // namespace mla

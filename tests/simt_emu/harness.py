@@ -1,0 +1,72 @@
+"""Run a decode case through the emulated kernels (tests/simt_emu/_build/run_case)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BIN = os.path.join(HERE, "_build", "run_case")
+MAGIC = 0x4D4C4145
+
+
+def ensure_built() -> str:
+    from tests.simt_emu import build as _b  # noqa: WPS433
+    if not os.path.exists(BIN) or _stale():
+        _b.build()
+    return BIN
+
+
+def _stale() -> bool:
+    from tests.simt_emu import build as _b
+    t = os.path.getmtime(BIN)
+    srcs = [os.path.join(_b.CSRC, f) for f in _b.KERNEL_FILES]
+    srcs += [os.path.join(HERE, f) for f in ("gfx950_asm.h", "emu_runtime.cpp", "run_case.cpp",
+                                              os.path.join("hip", "hip_runtime.h"))]
+    return any(os.path.getmtime(s) > t for s in srcs)
+
+
+def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
+        env_extra: dict | None = None):
+    """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta)."""
+    B, H, qmax = case.batch, case.num_heads, case.max_q_len
+    kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
+    hdr = np.array([MAGIC, B, H, qmax, case.page_size, case.num_pages, case.max_pages, kv_dtype,
+                    int(case.causal), num_workgroups, 1, 0], dtype=np.int32)
+    with tempfile.TemporaryDirectory() as d:
+        fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
+        with open(fin, "wb") as f:
+            f.write(hdr.tobytes())
+            f.write(np.float32(case.sm_scale).tobytes())
+            f.write(np.ascontiguousarray(case.q).tobytes())
+            f.write(np.ascontiguousarray(case.kv).tobytes())
+            if kv_dtype == 1:
+                f.write(np.ascontiguousarray(case.kv_scale, dtype=np.float32).tobytes())
+            f.write(np.ascontiguousarray(case.block_table, dtype=np.int32).tobytes())
+            f.write(np.ascontiguousarray(case.kv_lens, dtype=np.int32).tobytes())
+            f.write(np.ascontiguousarray(case.q_lens, dtype=np.int32).tobytes())
+        env = dict(os.environ)
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+        if phases is not None:
+            env["MLA_PHASES"] = str(phases)
+        if env_extra:
+            env.update(env_extra)
+        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+                             timeout=timeout, env=env)
+        if os.environ.get("EMU_SHOW"):
+            print(res.stdout[-20000:], res.stderr[-4000:])
+        if res.returncode != 0:
+            raise RuntimeError(f"emulated run failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
+        raw = np.fromfile(fout, dtype=np.uint8)
+    meta = raw[:16].view(np.int32).copy()
+    n_o = B * qmax * H * 512 * 2
+    out = raw[16:16 + n_o].view(np.uint16).reshape(B, qmax, H, 512)
+    lse = raw[16 + n_o:].view(np.float32).reshape(B, qmax, H)
+    return out, lse, {"num_items": int(meta[0]), "num_partials": int(meta[1]),
+                      "num_combine": int(meta[2]), "phases": int(meta[3])}
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,127 @@
+// Runs one decode case through the library's C ABI with the kernels executed
+// by the lane-thread emulator.  Every buffer is allocated at its exact size,
+// so AddressSanitizer reports any access of the kernels outside the inputs,
+// outputs, plan or workspace.
+//
+// usage: run_case <in.bin> <out.bin>
+//   in.bin : int32 header[12] = {magic, B, H, qmax, page_size, num_pages,
+//            max_pages, kv_dtype, causal, num_workgroups, has_q_lens, 0},
+//            float scale, then q (B*qmax*H*576 bf16), kv cache (pages*P*576
+//            elements), kv scales (pages*P fp32, e4m3 only), block table
+//            (B*max_pages int32), kv_lens (B int32), q_lens (B int32, if any)
+//   out.bin: int32 {num_items, num_partials, num_combine, phases}, then O
+//            (B*qmax*H*512 bf16) and LSE (B*qmax*H fp32)
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "mla_decode.h"
+
+namespace {
+
+[[noreturn]] void die(const char* m) {
+  std::fprintf(stderr, "run_case: %s\n", m);
+  std::exit(2);
+}
+
+void* exact_alloc(size_t n, size_t align = 16) {
+  if (n == 0) return nullptr;
+  const size_t rounded = (n + align - 1) / align * align;
+  if (rounded != n) die("buffer size is not a multiple of its alignment");
+  void* p = std::aligned_alloc(align, n);
+  if (!p) die("out of memory");
+  return p;
+}
+
+void read_into(FILE* f, void* dst, size_t n) {
+  if (n && std::fread(dst, 1, n, f) != n) die("short input file");
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc != 3) die("usage: run_case <in.bin> <out.bin>");
+  FILE* f = std::fopen(argv[1], "rb");
+  if (!f) die("cannot open input");
+  int32_t hd[12];
+  float scale;
+  read_into(f, hd, sizeof hd);
+  read_into(f, &scale, sizeof scale);
+  if (hd[0] != 0x4d4c4145) die("bad magic");
+  mla_shape s{};
+  s.batch = hd[1];
+  s.num_heads = hd[2];
+  s.d_latent = 512;
+  s.d_rope = 64;
+  s.max_q_len = hd[3];
+  s.page_size = hd[4];
+  s.num_pages = hd[5];
+  s.max_pages_per_seq = hd[6];
+  s.kv_dtype = hd[7];
+  s.causal = hd[8];
+  const int nwg = hd[9];
+  const bool has_ql = hd[10] != 0;
+  const size_t rows = size_t(s.batch) * s.max_q_len * s.num_heads;
+  const size_t kv_elems = size_t(s.num_pages) * s.page_size * 576;
+  const size_t kv_bytes = kv_elems * (s.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 2);
+
+  void* q = exact_alloc(rows * 576 * 2);
+  void* kv = exact_alloc(kv_bytes);
+  float* ksc = s.kv_dtype == MLA_KV_FP8_E4M3
+                   ? static_cast<float*>(exact_alloc(size_t(s.num_pages) * s.page_size * 4, 4))
+                   : nullptr;
+  int32_t* bt = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * s.max_pages_per_seq * 4, 4));
+  int32_t* kvl = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4));
+  int32_t* ql = has_ql ? static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4)) : nullptr;
+  read_into(f, q, rows * 576 * 2);
+  read_into(f, kv, kv_bytes);
+  if (ksc) read_into(f, ksc, size_t(s.num_pages) * s.page_size * 4);
+  read_into(f, bt, size_t(s.batch) * s.max_pages_per_seq * 4);
+  read_into(f, kvl, size_t(s.batch) * 4);
+  if (ql) read_into(f, ql, size_t(s.batch) * 4);
+  std::fclose(f);
+
+  const uint64_t bound = mla_plan_bytes_bound(&s, nwg);
+  if (bound == 0) die("shape rejected by mla_plan_bytes_bound");
+  std::vector<int32_t> host_plan(bound / 4 + 1);
+  mla_plan_info info{};
+  mla_status st = mla_decode_plan(&s, kvl, ql, nwg, host_plan.data(), host_plan.size() * 4, &info);
+  if (st != MLA_OK) die("mla_decode_plan failed");
+  // the "device" plan image: exactly plan_bytes long
+  void* plan = exact_alloc(info.plan_bytes);
+  std::memcpy(plan, host_plan.data(), info.plan_bytes);
+  void* ws = info.workspace_bytes ? exact_alloc(info.workspace_bytes, 256) : nullptr;
+
+  void* o = exact_alloc(rows * 512 * 2);
+  float* lse = static_cast<float*>(exact_alloc(rows * 4, 4));
+  // sentinels: rows the kernels must not write keep them
+  std::memset(o, 0xC1, rows * 512 * 2);
+  for (size_t i = 0; i < rows; ++i) lse[i] = 12345.0f;
+
+  st = mla_decode_fwd(&s, &info, plan, q, kv, ksc, bt, kvl, ql, scale, o, lse, ws,
+                      info.workspace_bytes, nullptr);
+  if (st != MLA_OK) die("mla_decode_fwd failed");
+  st = mla_combine(&s, &info, plan, ws, info.workspace_bytes, ql, o, lse, nullptr);
+  if (st != MLA_OK) die("mla_combine failed");
+
+  FILE* g = std::fopen(argv[2], "wb");
+  if (!g) die("cannot open output");
+  const int32_t meta[4] = {info.num_items, info.num_partials, info.num_combine, info.phases};
+  std::fwrite(meta, 1, sizeof meta, g);
+  std::fwrite(o, 1, rows * 512 * 2, g);
+  std::fwrite(lse, 1, rows * 4, g);
+  std::fclose(g);
+  std::free(q);
+  std::free(kv);
+  std::free(ksc);
+  std::free(bt);
+  std::free(kvl);
+  std::free(ql);
+  std::free(plan);
+  std::free(ws);
+  std::free(o);
+  std::free(lse);
+  return 0;
+}
