@@ -36,7 +36,7 @@ METRIC = "MLA decode µs/call, KV HBM GB/s and % of roofline at DeepSeek-V3 shap
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ("decode_kernel.hip", "kernels.h", "plan_layout.h")
+KERNEL_SOURCES = ("decode_kernel.hip", "gfx950_asm.h", "kernels.h", "plan_layout.h")
 DECODE_KERNEL = "mla_decode_kernel"
 
 

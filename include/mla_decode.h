@@ -123,13 +123,14 @@ int32_t mla_device_num_cus(int32_t device);
  * Splits sum_b ceil(q_b * H / 128) row blocks x ceil(L_b / 64) key rounds into
  * work items and deals them to num_workgroups persistent workgroups so that
  * each gets about the same number of rounds (a fixed per-item cost included).
- * When there are few row blocks, groups of 2 or 4 workgroups on one XCD share
- * a block (each takes 64 or 32 of its rows over the same keys, which then come
- * from HBM once); info->phases reports the group size.  A row block whose key
- * range is cut gets one partial slot per piece and a combine entry.  Key
- * splitting with a log-sum-exp merge follows the split-K remark of the
- * FlashAttention-3 page (chapter 2).  MLA_PHASES (1, 2, 4) forces the group
- * size and MLA_NUM_WORKGROUPS the workgroup count (tuning and tests).
+ * A row block whose key range is cut gets one partial slot per piece and a
+ * combine entry.  Key splitting with a log-sum-exp merge follows the split-K
+ * remark of the FlashAttention-3 page (chapter 2).  By default every row block
+ * is taken by one workgroup (info->phases = 1).  MLA_PHASES=2 or 4 (when it
+ * divides num_workgroups) instead lets groups of 2 or 4 workgroups on one XCD
+ * share a block (each takes 64 or 32 of its rows over the same keys, which then
+ * come from HBM once); MLA_NUM_WORKGROUPS forces the workgroup count.  Both are
+ * for tuning and tests.
  *
  *   kv_lens_host [B]  keys per sequence, including this step's q_b tokens.
  *   q_lens_host  [B]  query tokens per sequence (0..max_q_len); NULL means

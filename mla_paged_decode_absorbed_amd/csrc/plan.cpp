@@ -58,15 +58,15 @@ std::vector<Unit> make_units(const mla_shape& s, const int32_t* kv_lens, const i
   return units;
 }
 
-// Phases per processor: the most that still leaves every processor work.
-int choose_phases(int64_t n_units, int32_t G) {
+// Phases per processor.  Measured on MI355X, sharing a unit's keys between
+// 2 or 4 workgroups (one 16-key tile per wave and round, one round in flight)
+// is slower than splitting the key range of whole 128-row units and merging
+// the partials, for every shape tried (DeepSeek-V3 decode 126 vs 181 us/call,
+// long-context e4m3 255 vs 1383 us/call), so 1 is the default; MLA_PHASES=2
+// or 4 selects the shared-key schedule.
+int choose_phases(int64_t /*n_units*/, int32_t G) {
   const int forced = env_int("MLA_PHASES", 0);
-  if (forced == 1 || forced == 2 || forced == 4) return forced;
-  for (int ph : {4, 2}) {
-    if (G % ph != 0) continue;
-    if (G % 8 == 0 && (G / 8) % ph != 0) continue;   // keep a processor inside one XCD
-    if (n_units * ph <= int64_t(G) * 5 / 4) return ph;
-  }
+  if ((forced == 2 || forced == 4) && G % forced == 0) return forced;
   return 1;
 }
 
