@@ -68,6 +68,10 @@ emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c);
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p);
 emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p);
 emu_f32x2 cvt_pk_f32_fp8(int v, bool hi);
+inline unsigned long long memtime() {
+  static unsigned long long t = 0;
+  return ++t;
+}
 }  // namespace emu
 
 #define hipLaunchKernelGGL(K, G, B, SH, ST, ...) emu::launch(K, dim3(G), dim3(B), __VA_ARGS__)
@@ -87,6 +91,16 @@ emu_f32x2 cvt_pk_f32_fp8(int v, bool hi);
 #define __log2f(x) log2f(x)
 #define __logf(x) logf(x)
 #define __expf(x) expf(x)
+#define __builtin_amdgcn_s_memtime() emu::memtime()
+#define HIP_SYMBOL(x) (&(x))
+inline hipError_t hipMemcpyFromSymbol(void* dst, const void* sym, size_t n) {
+  std::memcpy(dst, sym, n);
+  return hipSuccess;
+}
+inline hipError_t hipMemcpyToSymbol(const void* sym, const void* src, size_t n) {
+  std::memcpy(const_cast<void*>(sym), src, n);
+  return hipSuccess;
+}
 
 inline unsigned __float_as_uint(float x) { return __builtin_bit_cast(unsigned, x); }
 inline float __uint_as_float(unsigned x) { return __builtin_bit_cast(float, x); }

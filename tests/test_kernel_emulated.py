@@ -76,3 +76,28 @@ def test_emulated_kernels_match_oracle(kv_lens, q_lens, nwg, phases, kv_dtype):
     out, lse, meta = harness.run(case, nwg, phases)
     assert meta["phases"] == phases
     _check(case, out, lse)
+
+
+@pytest.mark.parametrize("H,q,P,causal", [(16, 4, 16, True), (64, 3, 256, True),
+                                          (128, 2, 32, False)])
+def test_emulated_heads_drafts_pages(H, q, P, causal):
+    # q * H > 128 rows: several row blocks per sequence; small and large pages
+    case = make_case(kv_lens=[77, 300], q_lens=[q, 1], num_heads=H, page_size=P, causal=causal,
+                     seed=31, sm_scale=1 / math.sqrt(192))
+    out, lse, meta = harness.run(case, 6, 1)
+    _check(case, out, lse)
+
+
+def test_emulated_restart_on_late_dominant_key():
+    # a cached row far above the first tile's reference max forces the
+    # restart path (a second pass with the raised reference)
+    case = make_case(kv_lens=[700], q_lens=[1], seed=19, sm_scale=1 / math.sqrt(192))
+    q = oracle.decode_bf16(case.q[0, 0])
+    L = 650
+    page, slot = case.block_table[0, L // 64], L % 64
+    import torch
+    v = torch.from_numpy(q[0].astype(np.float32)).to(torch.bfloat16)   # over 50 log2 units above
+    case.kv[page, slot] = v.view(torch.int16).numpy().view(np.uint16)
+    for phases, nwg in ((1, 1), (4, 4)):
+        out, lse, _ = harness.run(case, nwg, phases)
+        _check(case, out, lse)
