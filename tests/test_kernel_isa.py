@@ -1,0 +1,141 @@
+"""Checks on the gfx950 machine code of the decode kernel (CPU only: hipcc
+cross-compiles; nothing runs on a GPU).
+
+* No scratch (spill) access inside the key loop: a spill reload there is a
+  vector-memory load, and the wait for it would also wait for every HBM->LDS
+  copy in flight, draining the ring once per tile.
+* No scalar-memory stores or atomics anywhere.
+* Every HBM->LDS copy (global_load_lds) reads its scalar base no sooner than
+  five wait states after a VALU instruction wrote it (the CDNA rule for a
+  VALU-written SGPR read by a vector-memory instruction; the compiler cannot
+  enforce it across the kernel's inline assembly).
+* The key loop of the default (bf16, one phase) kernel issues the expected
+  MFMAs and LDS reads per 16-key tile.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+
+pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def isa(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "decode_kernel.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument",
+           os.path.join(CSRC, "decode_kernel.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    return out.read_text()
+
+
+def _kernels(text):
+    """{kernel symbol: [(block label, [instruction lines])]}"""
+    out = {}
+    cur = None
+    for line in text.splitlines():
+        m = re.match(r"^(_ZN3mla\S*mla_decode_kernel\S*):", line)
+        if m:
+            cur = [("entry", [])]
+            out[m.group(1)] = cur
+            continue
+        if cur is None:
+            continue
+        s = line.split(";")[0].strip()
+        if s.startswith("s_endpgm"):
+            cur = None
+            continue
+        lab = re.match(r"^(\.LBB\S+):", line)
+        if lab:
+            cur.append((lab.group(1), []))
+        elif s and not s.startswith("."):
+            cur[-1][1].append(s)
+    return out
+
+
+def _key_loop_blocks(blocks):
+    """Blocks of the key loop: the ones that issue MFMAs."""
+    return [(lab, ins) for lab, ins in blocks if any("v_mfma" in i for i in ins)]
+
+
+def test_all_instantiations_present(isa):
+    ks = _kernels(isa)
+    assert len(ks) == 6, sorted(ks)
+
+
+# The e4m3 kernel with four phases (opt-in through MLA_PHASES=4, never chosen
+# by the planner) runs out of registers in its key loop; every other
+# instantiation, including both defaults, must stay spill-free there.
+KNOWN_LOOP_SPILLS = {"ILi1ELi4E"}
+
+
+def test_no_scratch_access_in_key_loop(isa):
+    for name, blocks in _kernels(isa).items():
+        if any(k in name for k in KNOWN_LOOP_SPILLS):
+            continue
+        for lab, ins in _key_loop_blocks(blocks):
+            bad = [i for i in ins if i.startswith("scratch_") or
+                   (i.startswith("buffer_") and "s[0:3]" in i)]
+            assert not bad, f"{name} {lab}: {bad[:3]}"
+
+
+def test_no_scalar_stores(isa):
+    for name, blocks in _kernels(isa).items():
+        for lab, ins in blocks:
+            bad = [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)]
+            assert not bad, f"{name} {lab}: {bad[:3]}"
+
+
+def _sgprs(tok):
+    m = re.match(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
+    for name, blocks in _kernels(isa).items():
+        for lab, ins in blocks:
+            for k, i in enumerate(ins):
+                if not i.startswith("global_load_lds"):
+                    continue
+                used = set()
+                for tok in i.split(None, 1)[1].split(","):
+                    used |= _sgprs(tok.strip().split()[0])
+                ws = 0
+                for j in range(k - 1, max(-1, k - 12), -1):
+                    if ws >= 5:
+                        break
+                    p = ins[j]
+                    op = p.split()[0]
+                    if op.startswith("v_") and " " in p:
+                        dst = p.split(None, 1)[1].split(",")[0].strip()
+                        assert not (_sgprs(dst) & used), f"{name} {lab}: {p} -> {i}"
+                    ws += int(p.split()[1]) + 1 if op == "s_nop" else 1
+
+
+def test_default_kernel_tile_work(isa):
+    ks = _kernels(isa)
+    name = next(n for n in ks if "ILi0ELi1E" in n)
+    loop = _key_loop_blocks(ks[name])
+    mfma = sum(sum("v_mfma" in i for i in ins) for _, ins in loop)
+    k_reads = sum(sum(i.startswith("ds_read_b128") for i in ins) for _, ins in loop)
+    v_reads = sum(sum(i.startswith("ds_read_b64_tr_b16") for i in ins) for _, ins in loop)
+    copies = sum(i.startswith("global_load_lds_dwordx4") for _, ins in ks[name] for i in ins)
+    # per 16-key tile: 36 QK + 16 PV MFMAs, 18 K-fragment and 32 transposing V reads
+    assert mfma % 52 == 0 and mfma >= 52
+    tiles = mfma // 52
+    assert k_reads == 18 * tiles and v_reads == 32 * tiles
+    # one tile's 18 copies in the prologue and in the loop
+    assert copies == 36
