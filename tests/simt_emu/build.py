@@ -29,14 +29,19 @@ def compiler() -> str:
     raise RuntimeError("clang++ not found")
 
 
-def build(sanitize: bool = True) -> str:
-    src = os.path.join(OUT, "src")
+def build(sanitize: bool = True, decode_source: str | None = None, tag: str = "") -> str:
+    """Build the emulator binary.  ``decode_source`` replaces the library's
+    decode_kernel.hip (a candidate kernel); ``tag`` names that binary."""
+    out = os.path.join(OUT, tag) if tag else OUT
+    src = os.path.join(out, "src")
     os.makedirs(src, exist_ok=True)
     for f in KERNEL_FILES:
         shutil.copyfile(os.path.join(CSRC, f), os.path.join(src, f))
+    if decode_source:
+        shutil.copyfile(decode_source, os.path.join(src, "decode_kernel.hip"))
     shutil.copyfile(os.path.join(HERE, "gfx950_asm.h"), os.path.join(src, "gfx950_asm.h"))
     flags = ["-std=c++20", "-O1", "-g", "-pthread", "-fno-omit-frame-pointer",
-             f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument"]
+             f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument", "-Wno-psabi"]
     if sanitize:
         flags.append("-fsanitize=address")
     units = [os.path.join(src, f) for f in ("decode_kernel.hip", "combine_kernel.hip",
@@ -44,17 +49,18 @@ def build(sanitize: bool = True) -> str:
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     objs = []
     for u in units:
-        obj = os.path.join(OUT, os.path.basename(u) + ".o")
+        obj = os.path.join(out, os.path.basename(u) + ".o")
         cmd = [compiler(), *flags, "-x", "c++", "-c", u, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"emulator build failed on {u}:\n{res.stderr[-4000:]}")
         objs.append(obj)
-    cmd = [compiler(), *flags, *objs, "-o", BIN]
+    binary = os.path.join(out, "run_case")
+    cmd = [compiler(), *flags, *objs, "-o", binary]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"emulator link failed:\n{res.stderr[-4000:]}")
-    return BIN
+    return binary
 
 
 if __name__ == "__main__":

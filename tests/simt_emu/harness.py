@@ -29,7 +29,7 @@ def _stale() -> bool:
 
 
 def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
-        env_extra: dict | None = None):
+        env_extra: dict | None = None, binary: str | None = None):
     """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta)."""
     B, H, qmax = case.batch, case.num_heads, case.max_q_len
     kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
@@ -53,7 +53,7 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
             env["MLA_PHASES"] = str(phases)
         if env_extra:
             env.update(env_extra)
-        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+        res = subprocess.run([binary or ensure_built(), fin, fout], capture_output=True, text=True,
                              timeout=timeout, env=env)
         if os.environ.get("EMU_SHOW"):
             print(res.stdout[-20000:], res.stderr[-4000:])

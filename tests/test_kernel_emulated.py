@@ -10,6 +10,7 @@ does not model instruction timing, hazards or the compiler's register
 allocation: the GPU parity tests remain the bar for those.
 """
 import math
+import os
 import shutil
 
 import numpy as np
@@ -101,3 +102,28 @@ def test_emulated_restart_on_late_dominant_key():
     for phases, nwg in ((1, 1), (4, 4)):
         out, lse, _ = harness.run(case, nwg, phases)
         _check(case, out, lse)
+
+
+# ---------------------------------------------------------------- candidate kernel
+CANDIDATE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "simt_emu", "candidates",
+                         "decode_kernel_pairs.hip")
+
+
+@pytest.fixture(scope="module")
+def candidate_binary():
+    from tests.simt_emu import build as _b
+    return _b.build(decode_source=CANDIDATE, tag="pairs")
+
+
+@pytest.mark.parametrize("kv_lens,q_lens,nwg,kv_dtype,H,P", [
+    ([3000, 700, 65, 1800], [1, 2, 1, 2], 1, "bf16", 128, 64),     # several items per workgroup
+    ([1, 15, 16, 17, 129, 31, 33], [1, 1, 2, 1, 2, 1, 2], 12, "bf16", 128, 64),
+    ([900, 70], [1, 2], 16, "fp8_e4m3", 128, 64),
+    ([77, 300], [4, 1], 6, "bf16", 16, 16),
+])
+def test_candidate_pairs_kernel_matches_oracle(candidate_binary, kv_lens, q_lens, nwg, kv_dtype,
+                                               H, P):
+    case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, kv_dtype=kv_dtype, num_heads=H,
+                     page_size=P, sm_scale=1 / math.sqrt(192))
+    out, lse, meta = harness.run(case, nwg, 1, binary=candidate_binary)
+    _check(case, out, lse)
