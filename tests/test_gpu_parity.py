@@ -161,6 +161,16 @@ def test_head_counts_and_longer_drafts(H, q, phases):
     check(case, out, lse)
 
 
+@pytest.mark.parametrize("phases", [1, 4])
+@pytest.mark.parametrize("H", [16, 128])
+def test_max_draft_length(H, phases):
+    # MLA_MAX_Q_LEN = 8 query tokens per sequence: up to 8 row blocks of 128
+    case = make_case(kv_lens=[40, 600, 8], q_lens=[8, 8, 8], num_heads=H, seed=15,
+                     sm_scale=1 / math.sqrt(192))
+    (out, lse), _ = run_gpu(case, num_workgroups=16, phases=phases)
+    check(case, out, lse)
+
+
 def test_non_causal_q2():
     case = make_case(kv_lens=[50, 333], q_lens=[2, 2], causal=False, seed=15,
                      sm_scale=1 / math.sqrt(192))

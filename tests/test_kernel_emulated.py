@@ -79,7 +79,7 @@ def test_emulated_kernels_match_oracle(kv_lens, q_lens, nwg, phases, kv_dtype):
     _check(case, out, lse)
 
 
-@pytest.mark.parametrize("H,q,P,causal", [(16, 4, 16, True), (64, 3, 256, True),
+@pytest.mark.parametrize("H,q,P,causal", [(16, 4, 16, True), (16, 8, 16, True), (64, 3, 256, True),
                                           (128, 2, 32, False)])
 def test_emulated_heads_drafts_pages(H, q, P, causal):
     # q * H > 128 rows: several row blocks per sequence; small and large pages
