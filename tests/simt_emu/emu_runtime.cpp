@@ -21,6 +21,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <deque>
 #include <memory>
 #include <vector>
@@ -115,6 +116,17 @@ std::atomic<const unsigned char*> lds_base{nullptr};
 
 void apply(const Pending& p) { std::memcpy(p.dst, p.data, p.n); }
 
+// EMU_SCHED=drift runs each wave alone until it blocks at a workgroup barrier
+// (waves drift apart as far as the kernel's synchronisation allows); the
+// default interleaves the waves one wave operation at a time.
+bool drift_schedule() {
+  static const bool v = [] {
+    const char* e = std::getenv("EMU_SCHED");
+    return e && std::strcmp(e, "drift") == 0;
+  }();
+  return v;
+}
+
 void yield_to_scheduler(bool finishing) {
   Fiber* f = S.cur;
   void* fake = nullptr;
@@ -207,22 +219,40 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           f.sp = top;
         }
         int alive = nt;
+        auto resume = [&](int t) -> bool {   // false if the lane cannot run now
+          Fiber& f = fib[t];
+          if (f.done) return false;
+          if (f.wait_bar && f.wait_bar->gen == f.wait_gen) return false;
+          f.wait_bar = nullptr;
+          threadIdx = EmuIdx{unsigned(t), 0u, 0u};
+          blockIdx = EmuIdx{bx, by, bz};
+          S.cur = &f;
+          void* fake = nullptr;
+          __sanitizer_start_switch_fiber(&fake, f.stack + page, kStackBytes);
+          emu_ctx_switch(&S.sp, f.sp);
+          __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
+          if (f.done) --alive;
+          return true;
+        };
+        const int nw = nt / 64;
+        unsigned rot = 0;
         while (alive > 0) {
           bool progressed = false;
-          for (int t = 0; t < nt; ++t) {
-            Fiber& f = fib[t];
-            if (f.done) continue;
-            if (f.wait_bar && f.wait_bar->gen == f.wait_gen) continue;
-            f.wait_bar = nullptr;
-            threadIdx = EmuIdx{unsigned(t), 0u, 0u};
-            blockIdx = EmuIdx{bx, by, bz};
-            S.cur = &f;
-            void* fake = nullptr;
-            __sanitizer_start_switch_fiber(&fake, f.stack + page, kStackBytes);
-            emu_ctx_switch(&S.sp, f.sp);
-            __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
-            progressed = true;
-            if (f.done) --alive;
+          if (drift_schedule()) {
+            // one wave at a time, run until it can go no further (it waits
+            // at a workgroup barrier or has finished); start with a rotating
+            // wave so that every wave gets ahead of the others in turn
+            for (int k = 0; k < nw; ++k) {
+              const int w = int((rot + k) % nw);
+              for (bool moved = true; moved;) {
+                moved = false;
+                for (int t = 64 * w; t < 64 * w + 64; ++t) moved |= resume(t);
+                progressed |= moved;
+              }
+            }
+            ++rot;
+          } else {
+            for (int t = 0; t < nt; ++t) progressed |= resume(t);
           }
           if (!progressed) fail("deadlock: every live lane waits at a barrier no lane can complete");
         }
@@ -239,6 +269,18 @@ uint32_t lds_address(const void* p) {
   return uint32_t(c - b);
 }
 
+// EMU_DMA_LAND=issue lands every copy at once (a copy into a stage that
+// another wave still reads then corrupts that read: write-after-read races);
+// the default lands copies at the issuing wave's vmcnt wait (a read before
+// the wait sees stale data: read-after-write races).
+bool land_at_issue() {
+  static const bool v = [] {
+    const char* e = std::getenv("EMU_DMA_LAND");
+    return e && std::strcmp(e, "issue") == 0;
+  }();
+  return v;
+}
+
 void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
   const unsigned char* b = lds_base.load();
   if (!b) fail("LDS copy before any LDS address was taken");
@@ -248,7 +290,8 @@ void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
   p.dst = const_cast<unsigned char*>(b) + off;
   p.n = bytes;
   std::memcpy(p.data, static_cast<const unsigned char*>(sbase) + voff, bytes);   // checked read
-  S.cur->dma.push_back(p);
+  if (land_at_issue()) apply(p);
+  else S.cur->dma.push_back(p);
 }
 
 // s_waitcnt is per wave: every lane's copies land before any lane goes on.

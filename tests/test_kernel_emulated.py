@@ -70,13 +70,43 @@ CASES = [
 ]
 
 
+# Emulation modes.  EMU_DMA_LAND: "wait" lands LDS copies at the issuing
+# wave's vmcnt wait (a read of a stage before its wait sees stale data),
+# "issue" lands them at once (a copy into a stage another wave still reads
+# corrupts that read).  EMU_SCHED: "lockstep" interleaves the waves one wave
+# operation at a time, "drift" runs each wave alone up to its next workgroup
+# barrier, so waves get as far apart as the kernel's synchronisation allows.
+MODES = {
+    "wait-lockstep": {"EMU_DMA_LAND": "wait", "EMU_SCHED": "lockstep"},
+    "wait-drift": {"EMU_DMA_LAND": "wait", "EMU_SCHED": "drift"},
+    "issue-drift": {"EMU_DMA_LAND": "issue", "EMU_SCHED": "drift"},
+}
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
 @pytest.mark.parametrize("kv_lens,q_lens,nwg,phases,kv_dtype", CASES)
-def test_emulated_kernels_match_oracle(kv_lens, q_lens, nwg, phases, kv_dtype):
+def test_emulated_kernels_match_oracle(kv_lens, q_lens, nwg, phases, kv_dtype, mode):
     case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=29, kv_dtype=kv_dtype,
                      sm_scale=1 / math.sqrt(192), max_q_len=2)
-    out, lse, meta = harness.run(case, nwg, phases)
+    out, lse, meta = harness.run(case, nwg, phases, env_extra=MODES[mode])
     assert meta["phases"] == phases
     _check(case, out, lse)
+
+
+def test_emulation_catches_a_missing_barrier(tmp_path):
+    # the library kernel with its per-round workgroup barrier taken out: a
+    # wave refills ring stages other waves still read.  Runs on the CPU only.
+    from tests.simt_emu import build as _b
+    src = open(os.path.join(_b.CSRC, "decode_kernel.hip")).read()
+    marker = "barrier();   // tiles of round j come from all waves"
+    assert marker in src
+    planted = tmp_path / "decode_kernel.hip"
+    planted.write_text(src.replace(marker, "/* barrier removed */"))
+    binary = _b.build(decode_source=str(planted), tag="planted_race")
+    case = make_case(kv_lens=[700, 300], q_lens=[2, 1], seed=5, sm_scale=1 / math.sqrt(192))
+    out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra=MODES["issue-drift"])
+    with pytest.raises(AssertionError):
+        _check(case, out, lse)
 
 
 @pytest.mark.parametrize("H,q,P,causal", [(16, 4, 16, True), (16, 8, 16, True), (64, 3, 256, True),
@@ -100,8 +130,9 @@ def test_emulated_restart_on_late_dominant_key():
     v = torch.from_numpy(q[0].astype(np.float32)).to(torch.bfloat16)   # over 50 log2 units above
     case.kv[page, slot] = v.view(torch.int16).numpy().view(np.uint16)
     for phases, nwg in ((1, 1), (4, 4)):
-        out, lse, _ = harness.run(case, nwg, phases)
-        _check(case, out, lse)
+        for mode in ("wait-lockstep", "issue-drift"):
+            out, lse, _ = harness.run(case, nwg, phases, env_extra=MODES[mode])
+            _check(case, out, lse)
 
 
 # ---------------------------------------------------------------- candidate kernel
@@ -125,5 +156,6 @@ def test_candidate_pairs_kernel_matches_oracle(candidate_binary, kv_lens, q_lens
                                                H, P):
     case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, kv_dtype=kv_dtype, num_heads=H,
                      page_size=P, sm_scale=1 / math.sqrt(192))
-    out, lse, meta = harness.run(case, nwg, 1, binary=candidate_binary)
-    _check(case, out, lse)
+    for mode in ("wait-lockstep", "issue-drift"):
+        out, lse, meta = harness.run(case, nwg, 1, binary=candidate_binary, env_extra=MODES[mode])
+        _check(case, out, lse)
