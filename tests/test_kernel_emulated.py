@@ -119,7 +119,7 @@ def test_emulated_heads_drafts_pages(H, q, P, causal):
     _check(case, out, lse)
 
 
-def test_emulated_restart_on_late_dominant_key():
+def _late_dominant_key_case():
     # a cached row far above the first tile's reference max forces the
     # restart path (a second pass with the raised reference)
     case = make_case(kv_lens=[700], q_lens=[1], seed=19, sm_scale=1 / math.sqrt(192))
@@ -129,6 +129,11 @@ def test_emulated_restart_on_late_dominant_key():
     import torch
     v = torch.from_numpy(q[0].astype(np.float32)).to(torch.bfloat16)   # over 50 log2 units above
     case.kv[page, slot] = v.view(torch.int16).numpy().view(np.uint16)
+    return case
+
+
+def test_emulated_restart_on_late_dominant_key():
+    case = _late_dominant_key_case()
     for phases, nwg in ((1, 1), (4, 4)):
         for mode in ("wait-lockstep", "issue-drift"):
             out, lse, _ = harness.run(case, nwg, phases, env_extra=MODES[mode])
@@ -151,6 +156,7 @@ def candidate_binary():
     ([1, 15, 16, 17, 129, 31, 33], [1, 1, 2, 1, 2, 1, 2], 12, "bf16", 128, 64),
     ([900, 70], [1, 2], 16, "fp8_e4m3", 128, 64),
     ([77, 300], [4, 1], 6, "bf16", 16, 16),
+    ([77, 300], [8, 1], 6, "bf16", 16, 16),                         # longest draft
 ])
 def test_candidate_pairs_kernel_matches_oracle(candidate_binary, kv_lens, q_lens, nwg, kv_dtype,
                                                H, P):
@@ -159,3 +165,15 @@ def test_candidate_pairs_kernel_matches_oracle(candidate_binary, kv_lens, q_lens
     for mode in ("wait-lockstep", "issue-drift"):
         out, lse, meta = harness.run(case, nwg, 1, binary=candidate_binary, env_extra=MODES[mode])
         _check(case, out, lse)
+
+
+def test_candidate_restart_and_phased_plans(candidate_binary):
+    # the restart pass of the 32-key kernel, and the library kernel it keeps
+    # for plans with several phases
+    case = _late_dominant_key_case()
+    for phases, nwg in ((1, 1), (4, 4)):
+        for mode in ("wait-lockstep", "issue-drift"):
+            out, lse, meta = harness.run(case, nwg, phases, binary=candidate_binary,
+                                         env_extra=MODES[mode])
+            assert meta["phases"] == phases
+            _check(case, out, lse)

@@ -11,6 +11,10 @@ cross-compiles; nothing runs on a GPU).
   enforce it across the kernel's inline assembly).
 * The key loop of the default (bf16, one phase) kernel issues the expected
   MFMAs and LDS reads per 16-key tile.
+
+The same checks run on the candidate kernel kept with the CPU emulator
+(tests/simt_emu/candidates), whose default instantiation steps 32 keys at a
+time.
 """
 import os
 import re
@@ -26,17 +30,23 @@ HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shut
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def isa(tmp_path_factory):
+SOURCES = {
+    "library": os.path.join(CSRC, "decode_kernel.hip"),
+    "candidate": os.path.join(ROOT, "tests", "simt_emu", "candidates", "decode_kernel_pairs.hip"),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SOURCES))
+def isa(request, tmp_path_factory):
     out = tmp_path_factory.mktemp("isa") / "decode_kernel.s"
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument",
-           os.path.join(CSRC, "decode_kernel.hip"), "-o", str(out)]
+           SOURCES[request.param], "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
-    return out.read_text()
+    return request.param, out.read_text()
 
 
 def _kernels(text):
@@ -69,7 +79,7 @@ def _key_loop_blocks(blocks):
 
 
 def test_all_instantiations_present(isa):
-    ks = _kernels(isa)
+    ks = _kernels(isa[1])
     assert len(ks) == 6, sorted(ks)
 
 
@@ -80,7 +90,7 @@ KNOWN_LOOP_SPILLS = {"ILi1ELi4E"}
 
 
 def test_no_scratch_access_in_key_loop(isa):
-    for name, blocks in _kernels(isa).items():
+    for name, blocks in _kernels(isa[1]).items():
         if any(k in name for k in KNOWN_LOOP_SPILLS):
             continue
         for lab, ins in _key_loop_blocks(blocks):
@@ -90,7 +100,7 @@ def test_no_scratch_access_in_key_loop(isa):
 
 
 def test_no_scalar_stores(isa):
-    for name, blocks in _kernels(isa).items():
+    for name, blocks in _kernels(isa[1]).items():
         for lab, ins in blocks:
             bad = [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)]
             assert not bad, f"{name} {lab}: {bad[:3]}"
@@ -105,7 +115,7 @@ def _sgprs(tok):
 
 
 def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
-    for name, blocks in _kernels(isa).items():
+    for name, blocks in _kernels(isa[1]).items():
         for lab, ins in blocks:
             for k, i in enumerate(ins):
                 if not i.startswith("global_load_lds"):
@@ -126,16 +136,25 @@ def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
 
 
 def test_default_kernel_tile_work(isa):
-    ks = _kernels(isa)
-    name = next(n for n in ks if "ILi0ELi1E" in n)
+    which, text = isa
+    ks = _kernels(text)
+    if which == "library":
+        name = next(n for n in ks if "ILi0ELi1E" in n)
+        # per 16-key tile: 36 QK + 16 PV MFMAs, 18 K-fragment and 32
+        # transposing V reads
+        step_mfma, step_k, step_v = 52, 18, 32
+    else:
+        name = next(n for n in ks if "mla_decode_kernel_pairsILi0E" in n)
+        # per 32 keys: 36 QK (32x32x16) + 32 PV MFMAs, 36 K-fragment and 64
+        # transposing V reads
+        step_mfma, step_k, step_v = 68, 36, 64
     loop = _key_loop_blocks(ks[name])
     mfma = sum(sum("v_mfma" in i for i in ins) for _, ins in loop)
     k_reads = sum(sum(i.startswith("ds_read_b128") for i in ins) for _, ins in loop)
     v_reads = sum(sum(i.startswith("ds_read_b64_tr_b16") for i in ins) for _, ins in loop)
     copies = sum(i.startswith("global_load_lds_dwordx4") for _, ins in ks[name] for i in ins)
-    # per 16-key tile: 36 QK + 16 PV MFMAs, 18 K-fragment and 32 transposing V reads
-    assert mfma % 52 == 0 and mfma >= 52
-    tiles = mfma // 52
-    assert k_reads == 18 * tiles and v_reads == 32 * tiles
+    assert mfma % step_mfma == 0 and mfma >= step_mfma
+    steps = mfma // step_mfma
+    assert k_reads == step_k * steps and v_reads == step_v * steps
     # one tile's 18 copies in the prologue and in the loop
     assert copies == 36
