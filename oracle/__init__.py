@@ -28,10 +28,13 @@ What it computes, and where the pages state it:
 * fp8-e4m3 cache with one scale per cached token, symmetric, zero-point 0
   (FlashAttention-3 page, section 3.1, per-token KV calibration; PaddlePaddle
   3.0 page on low-bit KV cache).
+* Writing a step's new tokens into their page slots, quantizing them with
+  that per-token scale for an e4m3 cache (``append_ref``).
 
-Every function below is pinned by ``tests/test_oracle_pins.py`` against
-something other than itself (closed forms, the non-absorbed identity, brute
-force, library casts, invariants); see each docstring.
+Every function below is pinned by ``tests/test_oracle_pins.py`` (the
+append by ``tests/test_oracle_append_pins.py``) against something other than
+itself (closed forms, the non-absorbed identity, brute force, library casts,
+invariants); see each docstring.
 """
 from .codecs import decode_bf16, decode_e4m3, decode_kv_rows  # noqa: F401
 from .mla_ref import (  # noqa: F401
@@ -43,4 +46,10 @@ from .mla_ref import (  # noqa: F401
     non_absorbed_ref,
     scalar_mla_ref,
     visible_keys,
+)
+from .append_ref import (  # noqa: F401
+    append_positions,
+    encode_e4m3,
+    kv_append_ref,
+    quantize_rows_e4m3,
 )
