@@ -17,6 +17,9 @@ Prints ONE JSON line:
   cpu_baseline the float64 oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The append_* workloads instead time the cache append (mla_kv_append) alone:
+one decode step's new tokens, or a prompt's worth per sequence.
 """
 from __future__ import annotations
 
@@ -135,6 +138,140 @@ def cpu_baseline(case, seconds: float, kv_bytes_total: int):
     }
 
 
+APPEND_KERNEL = "mla_kv_append_kernel"
+APPEND_WORKLOADS = {
+    # name: (sequences, new tokens per sequence, cached tokens per sequence, kv dtype)
+    "append_step_v3_bf16": (64, 1, 2560, "bf16"),
+    "append_prompt_bf16": (64, 2560, 2560, "bf16"),
+    "append_prompt_fp8": (64, 2560, 2560, "fp8_e4m3"),
+}
+
+
+def append_counts(B, n, kv_dtype, page_size=64):
+    """Algorithmic bytes of one append: each new row read once (1152 B) and
+    written once (bf16 1152 B; e4m3 576 B + a 4 B scale), one block-table
+    entry per page touched, the two length arrays."""
+    rows = B * n
+    written = 1152 if kv_dtype == "bf16" else 576 + 4
+    pages = B * ((n + page_size - 1) // page_size)
+    return dict(rows=rows, alg_bytes=rows * (1152 + written) + pages * 4 + B * 8)
+
+
+def append_cpu_baseline(rows_np, kv_dtype, seconds: float):
+    """The oracle's append on a bounded sample: chunks of 256 rows of the
+    workload, taken in order, each appended as one sequence's new tokens into
+    a 4-page cache, until ``seconds`` pass."""
+    import numpy as np
+
+    from oracle import append_ref
+
+    P, chunk = 64, 256
+    n = rows_np.shape[0]
+    kv = np.zeros((chunk // P, P, 576), np.uint16 if kv_dtype == "bf16" else np.uint8)
+    sc = None if kv_dtype == "bf16" else np.zeros((chunk // P, P), np.float32)
+    bt = np.arange(chunk // P, dtype=np.int32)[None, :]
+    lens = np.array([chunk], np.int32)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        k0 = (done * chunk) % max(1, n - chunk + 1)
+        block = rows_np[None, k0:k0 + chunk]
+        kv, sc, _ = append_ref.kv_append_ref(kv, sc, bt, lens, lens, block, P, kv_dtype)
+        done += 1
+    el = time.perf_counter() - t0
+    rows_done = done * chunk
+    written = 1152 if kv_dtype == "bf16" else 580
+    return {
+        "value": round(rows_done * (1152 + written) / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"numpy oracle append, {rows_done} rows of the workload in chunks of "
+                   f"{chunk}, each into a 4-page cache, in {el:.1f} s"),
+    }
+
+
+def main_append(args) -> int:
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_absorbed_amd as mla
+
+    B, n, L, kv_dtype = APPEND_WORKLOADS[args.workload]
+    P = 64
+    dev = torch.device("cuda:0")
+    mla.load_library()
+    cnt = append_counts(B, n, kv_dtype, P)
+    log(f"workload {args.workload}: {B} sequences x {n} new tokens ({cnt['rows']} rows)")
+    rng = np.random.default_rng(2)
+    pages_per_seq = (L + P - 1) // P
+    pool = B * pages_per_seq
+    bt_np = rng.permutation(pool).astype(np.int32).reshape(B, pages_per_seq)
+    kv_lens_np = np.full(B, L, np.int32)
+    new_np = np.full(B, n, np.int32)
+    rows32 = (rng.standard_normal((B * n, 576), dtype=np.float32) * 0.5)
+    rows_bits = torch.from_numpy(rows32).to(torch.bfloat16).view(torch.int16).numpy()
+    kvd = mla.KV_BF16 if kv_dtype == "bf16" else mla.KV_FP8_E4M3
+    shape = mla.Shape.make(batch=B, num_heads=128, max_q_len=1, page_size=P, num_pages=pool,
+                           max_pages_per_seq=pages_per_seq, kv_dtype=kvd)
+    row_bytes = 1152 if kv_dtype == "bf16" else 576
+    set_bytes = B * n * 1152 + pool * P * row_bytes
+    nsets = max(2, math.ceil(3 * MALL_BYTES / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        src = torch.from_numpy(rows_bits).view(torch.bfloat16).to(dev).view(B, n, 576)
+        if kv_dtype == "bf16":
+            kv = torch.empty((pool, P, 576), dtype=torch.int16, device=dev)
+            sc = None
+        else:
+            kv = torch.empty((pool, P, 576), dtype=torch.uint8, device=dev)
+            sc = torch.empty((pool, P), dtype=torch.float32, device=dev)
+        sets.append((src, kv, sc))
+    bt = torch.from_numpy(bt_np).to(dev)
+    kvl = torch.from_numpy(kv_lens_np).to(dev)
+    nl = torch.from_numpy(new_np).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step(k):
+        src, kv, sc = sets[k % nsets]
+        mla.kv_append(shape, src, bt, kvl, kv, new_lens=nl, kv_scale=sc, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    w0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    avg_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(K)) / K
+    t = avg_ms * 1e-3
+    achieved = cnt["alg_bytes"] / t / 1e9
+    log(f"timed {K} appends: avg {avg_ms * 1e3:.2f} us, {achieved:.1f} GB/s")
+    res = {
+        "metric": "MLA cache append µs/call and HBM GB/s",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(avg_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if kv_dtype == "bf16" else "bf16->e4m3", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "new_tokens_per_seq": n,
+                   "kv_len": L, "page_size": P, "kv_dtype": kv_dtype},
+        "us_per_call": round(avg_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": APPEND_KERNEL, "alg_bytes_per_launch": cnt["alg_bytes"]},
+        "wall_s_timed": round(wall, 4), "input_sets": nsets, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle append for about {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = append_cpu_baseline(rows_bits.view(np.uint16), kv_dtype,
+                                                  args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +302,8 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in APPEND_WORKLOADS:
+        return main_append(args)
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)

@@ -30,6 +30,9 @@
  *                        partial (O, LSE) into the workspace for split ones.
  *   4. mla_combine       merges the partials of split row blocks into O/LSE.
  *
+ * mla_kv_append writes the step's new tokens into the cache; on the stream it
+ * goes before mla_decode_fwd of the same step.
+ *
  * Ownership: the caller allocates and owns every buffer; the library
  * allocates no memory and keeps no mutable state.  Buffers must stay alive
  * until the stream has passed the work that uses them.
@@ -193,6 +196,51 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info,
                        const void* plan_dev, const void* workspace,
                        uint64_t workspace_bytes, const int32_t* q_lens,
                        void* o, float* lse, mla_stream_t stream);
+
+/*
+ * Cache append: writes this step's new tokens into the paged cache, the
+ * write that precedes the decode of every step.
+ *
+ * Token t (t < n_b) of sequence b goes to position p = kv_lens[b] - n_b + t
+ * (kv_lens counts the new tokens, as for the decode), i.e. slot p % page_size
+ * of page block_table[b][p / page_size] (the page/block-table layout of the
+ * FlashAttention-3 in DeepSeek-R1 page, section 4.1).
+ *
+ *   shape          the decode's shape: batch, page_size, num_pages,
+ *                  max_pages_per_seq and kv_dtype are used (num_heads,
+ *                  max_q_len and causal are validated but not used).
+ *   max_new_tokens padded new tokens per sequence (>= 1; may exceed
+ *                  MLA_MAX_Q_LEN, e.g. for a prompt's tokens).
+ *   new_rows       [B, max_new_tokens, d_latent + d_rope] bf16, row-major: the
+ *                  latent + rope row of each new token.  Rows t >= n_b are not
+ *                  read.
+ *   new_lens       [B] int32 device n_b, or NULL (every n_b = max_new_tokens).
+ *   block_table, kv_lens  as for mla_decode_fwd (device).
+ *   kv_cache       [num_pages, page_size, d_latent + d_rope] bf16 or e4m3 bytes;
+ *                  only the slots of new tokens are written.
+ *   kv_scale       [num_pages, page_size] fp32 (e4m3 only, else ignored).
+ *                  For e4m3 each row is stored as code = RNE(x / s), the
+ *                  magnitude clamped to 448, with s = max|x| / 448 in fp32
+ *                  (1 for an all-zero row) written to kv_scale: one symmetric
+ *                  scale per token, the per-token absmax calibration of the
+ *                  FlashAttention-3 page (section 3.1) over the e4m3 range.
+ *                  Values must be finite.
+ *   skipped        optional int32 device counter (may be NULL): incremented
+ *                  once for each new token whose position falls outside
+ *                  [0, max_pages_per_seq * page_size) or whose page id falls
+ *                  outside [0, num_pages), and for every row of a sequence
+ *                  with n_b > max_new_tokens; such rows are not written.  The
+ *                  caller zeroes it.
+ *
+ * Rows of different tokens must not share a slot (a block table never maps
+ * two positions to one slot); nothing else in the cache changes.
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED (new_rows, kv_cache
+ * not 16-byte aligned), HIP (launch failure).  B = 0 is a no-op.
+ */
+mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const void* new_rows,
+                         const int32_t* new_lens, const int32_t* block_table,
+                         const int32_t* kv_lens, void* kv_cache, float* kv_scale,
+                         int32_t* skipped, mla_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "decode_fwd", "combine",
-    "decode", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
+    "decode", "kv_append", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
@@ -37,7 +37,7 @@ D_ROPE = 64
 EXPORTED_SYMBOLS = (
     "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
-    "mla_decode_fwd", "mla_combine",
+    "mla_decode_fwd", "mla_combine", "mla_kv_append",
 )
 
 
@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
     lib.mla_combine.restype = I32
     lib.mla_combine.argtypes = [sp, ip, P, P, U64, P, P, P, P]
+    lib.mla_kv_append.restype = I32
+    lib.mla_kv_append.argtypes = [sp, I32, P, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -245,3 +247,43 @@ def decode(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm
                workspace, kv_scale=kv_scale, stream=stream)
     combine(shape, pl, workspace, q_lens, out, lse, stream=stream)
     return out, lse
+
+
+def kv_append(shape: Shape, new_rows, block_table, kv_lens, kv_cache, *, new_lens=None,
+              kv_scale=None, skipped=None, stream=None):
+    """Write each sequence's new tokens into the paged cache (``mla_kv_append``).
+
+    new_rows [B, max_new, 576] bf16 (max_new may exceed the decode's q_len
+    limit); new_lens [B] int32 device tensor or None (all max_new);
+    block_table / kv_lens as for ``decode`` (kv_lens counts the new tokens);
+    kv_cache [pages, P, 576] bf16, or uint8 e4m3 with kv_scale [pages, P] fp32;
+    skipped: optional int32 device tensor of one element that counts rows whose
+    slot falls outside the pool (the caller zeroes it)."""
+    import torch
+    lib = load_library()
+    if new_rows.dtype != torch.bfloat16 or not new_rows.is_contiguous() or new_rows.dim() != 3:
+        raise ValueError("new_rows must be a contiguous [B, max_new, 576] bfloat16 tensor")
+    if new_rows.shape[0] != shape.batch or new_rows.shape[2] != D_LATENT + D_ROPE:
+        raise ValueError(f"new_rows shape {tuple(new_rows.shape)} does not match the shape struct")
+    dev = new_rows.device
+    for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("kv_lens", kv_lens),
+                    ("new_lens", new_lens), ("kv_scale", kv_scale), ("skipped", skipped)):
+        if t is not None and (not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be contiguous and on {dev}")
+    B, P, NP = shape.batch, shape.page_size, shape.num_pages
+    fp8 = shape.kv_dtype == KV_FP8_E4M3
+    sizes = [("kv_cache", kv_cache, NP * P * (D_LATENT + D_ROPE), 1 if fp8 else 2),
+             ("block_table", block_table, B * shape.max_pages_per_seq, 4),
+             ("kv_lens", kv_lens, B, 4), ("new_lens", new_lens, B, 4), ("skipped", skipped, 1, 4)]
+    if fp8:
+        sizes.append(("kv_scale", kv_scale, NP * P, 4))
+    for name, t, n, esize in sizes:
+        if t is None:
+            continue
+        if t.numel() != n or t.element_size() != esize:
+            raise ValueError(f"{name} must hold {n} elements of {esize} bytes, "
+                             f"not {t.numel()} of {t.element_size()}")
+    st = lib.mla_kv_append(ctypes.byref(shape), int(new_rows.shape[1]), _ptr(new_rows),
+                           _ptr(new_lens), _ptr(block_table), _ptr(kv_lens), _ptr(kv_cache),
+                           _ptr(kv_scale), _ptr(skipped), _stream(stream))
+    _check(st, "mla_kv_append")

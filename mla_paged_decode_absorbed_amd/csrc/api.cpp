@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "append.h"
 #include "kernels.h"
 #include "mla_decode.h"
 #include "plan_layout.h"
@@ -160,6 +161,40 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info, const 
   a.num_combine = info->num_combine;
   return launch_combine(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
                                                                                  : MLA_ERR_HIP;
+}
+
+mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const void* new_rows,
+                         const int32_t* new_lens, const int32_t* block_table,
+                         const int32_t* kv_lens, void* kv_cache, float* kv_scale,
+                         int32_t* skipped, mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  if (max_new_tokens < 1) return MLA_ERR_BAD_SHAPE;
+  if (int64_t(shape->batch) * max_new_tokens >= (int64_t(1) << 31)) return MLA_ERR_UNSUPPORTED;
+  if (shape->batch == 0) return MLA_OK;
+  if (!new_rows || !block_table || !kv_lens || !kv_cache) return MLA_ERR_NULL_ARG;
+  if (shape->kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale) return MLA_ERR_NULL_ARG;
+  if (!aligned16(new_rows) || !aligned16(kv_cache) ||
+      (kv_scale && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) ||
+      (skipped && (reinterpret_cast<uintptr_t>(skipped) & 3u)))
+    return MLA_ERR_MISALIGNED;
+
+  AppendArgs a{};
+  a.src = static_cast<const uint8_t*>(new_rows);
+  a.new_lens = new_lens;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.kv = static_cast<uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.skipped = skipped;
+  a.batch = shape->batch;
+  a.max_new = max_new_tokens;
+  a.page_shift = ilog2(shape->page_size);
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  return launch_append(a, shape->kv_dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 
 thread_local EmuIdx threadIdx;
 thread_local EmuIdx blockIdx;
+thread_local EmuIdx gridDim;
 
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
   *value = 256;
@@ -226,6 +227,7 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           f.wait_bar = nullptr;
           threadIdx = EmuIdx{unsigned(t), 0u, 0u};
           blockIdx = EmuIdx{bx, by, bz};
+          gridDim = EmuIdx{grid.x, grid.y, grid.z};
           S.cur = &f;
           void* fake = nullptr;
           __sanitizer_start_switch_fiber(&fake, f.stack + page, kStackBytes);

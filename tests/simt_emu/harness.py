@@ -1,4 +1,5 @@
-"""Run a decode case through the emulated kernels (tests/simt_emu/_build/run_case)."""
+"""Run a decode or cache-append case through the emulated kernels
+(tests/simt_emu/_build/run_case)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 BIN = os.path.join(HERE, "_build", "run_case")
 MAGIC = 0x4D4C4145
+APPEND_MAGIC = 0x4D4C4141
 
 
 def ensure_built() -> str:
@@ -66,6 +68,42 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
     lse = raw[16 + n_o:].view(np.float32).reshape(B, qmax, H)
     return out, lse, {"num_items": int(meta[0]), "num_partials": int(meta[1]),
                       "num_combine": int(meta[2]), "phases": int(meta[3])}
+
+
+def run_append(kv, kv_scale, block_table, kv_lens, new_lens, new_rows_bits, page_size: int,
+               kv_dtype: str, with_counter: bool = True, timeout: float = 600.0):
+    """mla_kv_append on the emulator.  Returns (kv', kv_scale' or None, skipped
+    or None); the inputs are not modified."""
+    B, max_new = new_rows_bits.shape[0], new_rows_bits.shape[1]
+    kvd = {"bf16": 0, "fp8_e4m3": 1}[kv_dtype]
+    hdr = np.array([APPEND_MAGIC, B, max_new, page_size, kv.shape[0], block_table.shape[1], kvd,
+                    int(new_lens is not None), int(with_counter), 0, 0, 0], dtype=np.int32)
+    with tempfile.TemporaryDirectory() as d:
+        fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
+        with open(fin, "wb") as f:
+            f.write(hdr.tobytes())
+            f.write(np.ascontiguousarray(new_rows_bits, dtype=np.uint16).tobytes())
+            f.write(np.ascontiguousarray(kv).tobytes())
+            if kvd == 1:
+                f.write(np.ascontiguousarray(kv_scale, dtype=np.float32).tobytes())
+            f.write(np.ascontiguousarray(block_table, dtype=np.int32).tobytes())
+            f.write(np.ascontiguousarray(kv_lens, dtype=np.int32).tobytes())
+            if new_lens is not None:
+                f.write(np.ascontiguousarray(new_lens, dtype=np.int32).tobytes())
+        env = dict(os.environ)
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+                             timeout=timeout, env=env)
+        if res.returncode != 0:
+            raise RuntimeError(f"emulated append failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
+        raw = np.fromfile(fout, dtype=np.uint8)
+    skipped = int(raw[:4].view(np.int32)[0])
+    n_kv = kv.nbytes
+    kv_out = raw[4:4 + n_kv].view(kv.dtype).reshape(kv.shape).copy()
+    sc_out = None
+    if kvd == 1:
+        sc_out = raw[4 + n_kv:].view(np.float32).reshape(kv_scale.shape).copy()
+    return kv_out, sc_out, (skipped if with_counter else None)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -29,6 +29,7 @@ struct EmuIdx {
 };
 extern thread_local EmuIdx threadIdx;
 extern thread_local EmuIdx blockIdx;
+extern thread_local EmuIdx gridDim;
 
 typedef int hipError_t;
 enum : int { hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorLaunchFailure = 2 };
@@ -104,5 +105,6 @@ inline hipError_t hipMemcpyToSymbol(const void* sym, const void* src, size_t n) 
 
 inline unsigned __float_as_uint(float x) { return __builtin_bit_cast(unsigned, x); }
 inline float __uint_as_float(unsigned x) { return __builtin_bit_cast(float, x); }
+inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_RELAXED); }
 inline int min(int a, int b) { return a < b ? a : b; }
 inline int max(int a, int b) { return a > b ? a : b; }

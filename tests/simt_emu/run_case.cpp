@@ -11,6 +11,14 @@
 //            (B*max_pages int32), kv_lens (B int32), q_lens (B int32, if any)
 //   out.bin: int32 {num_items, num_partials, num_combine, phases}, then O
 //            (B*qmax*H*512 bf16) and LSE (B*qmax*H fp32)
+//
+// A cache-append case (mla_kv_append) has its own magic:
+//   in.bin : int32 header[12] = {magic, B, max_new, page_size, num_pages,
+//            max_pages, kv_dtype, has_new_lens, has_skipped, 0, 0, 0}, then
+//            the new rows (B*max_new*576 bf16), kv cache, kv scales (e4m3
+//            only), block table, kv_lens, new_lens (if any)
+//   out.bin: int32 skipped count (-1 without a counter), then the kv cache
+//            and, for e4m3, the kv scales
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -39,6 +47,58 @@ void read_into(FILE* f, void* dst, size_t n) {
   if (n && std::fread(dst, 1, n, f) != n) die("short input file");
 }
 
+int run_append(FILE* f, const int32_t* hd, const char* out_path) {
+  mla_shape s{};
+  s.batch = hd[1];
+  s.num_heads = 1;
+  s.max_q_len = 1;
+  s.d_latent = 512;
+  s.d_rope = 64;
+  s.page_size = hd[3];
+  s.num_pages = hd[4];
+  s.max_pages_per_seq = hd[5];
+  s.kv_dtype = hd[6];
+  s.causal = 1;
+  const int max_new = hd[2];
+  const bool has_nl = hd[7] != 0, has_sk = hd[8] != 0;
+  const bool fp8 = s.kv_dtype == MLA_KV_FP8_E4M3;
+  const size_t src_bytes = size_t(s.batch) * max_new * 576 * 2;
+  const size_t kv_bytes = size_t(s.num_pages) * s.page_size * 576 * (fp8 ? 1 : 2);
+  const size_t sc_bytes = fp8 ? size_t(s.num_pages) * s.page_size * 4 : 0;
+  void* src = exact_alloc(src_bytes);
+  void* kv = exact_alloc(kv_bytes);
+  float* ksc = fp8 ? static_cast<float*>(exact_alloc(sc_bytes, 4)) : nullptr;
+  int32_t* bt = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * s.max_pages_per_seq * 4, 4));
+  int32_t* kvl = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4));
+  int32_t* nl = has_nl ? static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4)) : nullptr;
+  int32_t* sk = has_sk ? static_cast<int32_t*>(exact_alloc(4, 4)) : nullptr;
+  read_into(f, src, src_bytes);
+  read_into(f, kv, kv_bytes);
+  if (ksc) read_into(f, ksc, sc_bytes);
+  read_into(f, bt, size_t(s.batch) * s.max_pages_per_seq * 4);
+  read_into(f, kvl, size_t(s.batch) * 4);
+  if (nl) read_into(f, nl, size_t(s.batch) * 4);
+  std::fclose(f);
+  if (sk) *sk = 0;
+  const mla_status st = mla_kv_append(&s, max_new, src, nl, bt, kvl, kv, ksc, sk, nullptr);
+  if (st != MLA_OK) die("mla_kv_append failed");
+  FILE* g = std::fopen(out_path, "wb");
+  if (!g) die("cannot open output");
+  const int32_t skipped = sk ? *sk : -1;
+  std::fwrite(&skipped, 1, sizeof skipped, g);
+  std::fwrite(kv, 1, kv_bytes, g);
+  if (ksc) std::fwrite(ksc, 1, sc_bytes, g);
+  std::fclose(g);
+  std::free(src);
+  std::free(kv);
+  std::free(ksc);
+  std::free(bt);
+  std::free(kvl);
+  std::free(nl);
+  std::free(sk);
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -48,6 +108,7 @@ int main(int argc, char** argv) {
   int32_t hd[12];
   float scale;
   read_into(f, hd, sizeof hd);
+  if (hd[0] == 0x4d4c4141) return run_append(f, hd, argv[2]);
   read_into(f, &scale, sizeof scale);
   if (hd[0] != 0x4d4c4145) die("bad magic");
   mla_shape s{};

@@ -228,3 +228,45 @@ def test_empty_batch_is_a_noop(lib):
     assert pl.info.num_items == 0
     assert lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(pl.info), None, None, None, None,
                               None, None, None, 1.0, None, None, None, 0, None) == 0
+
+
+def test_kv_append_validates_before_any_launch(lib):
+    A = 0x10000   # aligned fake device addresses; never dereferenced on these paths
+
+    def app(shape, max_new=2, rows=A, nl=None, bt=A, kvl=A, kv=A, sc=None, sk=None):
+        return lib.mla_kv_append(ctypes.byref(shape), max_new, rows, nl, bt, kvl, kv, sc, sk, None)
+
+    shape = _shape(B=2)
+    assert app(shape, rows=None) == 1
+    assert app(shape, bt=None) == 1
+    assert app(shape, kvl=None) == 1
+    assert app(shape, kv=None) == 1
+    assert app(shape, rows=A + 8) == 4
+    assert app(shape, kv=A + 4) == 4
+    assert app(shape, sk=A + 2) == 4
+    assert app(shape, max_new=0) == 2
+    assert app(shape, max_new=1 << 30) == 3      # B * max_new rows past 32-bit indexing
+    fp8 = _shape(B=2, kvd=mla.KV_FP8_E4M3)
+    assert app(fp8) == 1                          # missing scales
+    assert app(fp8, sc=A + 2) == 4
+    bad = _shape(B=2)
+    bad.d_latent = 256
+    assert app(bad) == 3
+    # an empty batch is a no-op that reads no pointer
+    assert app(_shape(B=0), rows=None, bt=None, kvl=None, kv=None) == 0
+    # the binding rejects buffers whose sizes do not match the shape
+    import torch
+    rows = torch.zeros((2, 2, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mla.kv_append(shape, rows[:1], torch.zeros(2, 16, dtype=torch.int32),
+                      torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int16))
+    small = _shape(B=2, pages=2, maxp=2)
+    kv = torch.zeros((2, 64, 576), dtype=torch.int16)
+    bt = torch.zeros((2, 2), dtype=torch.int32)
+    with pytest.raises(ValueError, match="kv_lens"):
+        mla.kv_append(small, rows, bt, torch.zeros(3, dtype=torch.int32), kv)
+    with pytest.raises(ValueError, match="kv_cache"):
+        mla.kv_append(small, rows, bt, torch.zeros(2, dtype=torch.int32), kv[:1])
+    with pytest.raises(ValueError, match="skipped"):
+        mla.kv_append(small, rows, bt, torch.zeros(2, dtype=torch.int32), kv,
+                      skipped=torch.zeros(1, dtype=torch.int64))

@@ -158,3 +158,47 @@ def test_default_kernel_tile_work(isa):
     assert k_reads == step_k * steps and v_reads == step_v * steps
     # one tile's 18 copies in the prologue and in the loop
     assert copies == 36
+
+
+# ---------------------------------------------------------------- cache append
+
+@pytest.fixture(scope="module")
+def append_isa(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "append_kernel.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument",
+           os.path.join(CSRC, "append_kernel.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    return out.read_text()
+
+
+def _append_kernels(text):
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.match(r"^(_ZN3mla\S*mla_kv_append_kernel\S*):", line)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+            continue
+        if cur is None:
+            continue
+        s = line.split(";")[0].strip()
+        if s.startswith("s_endpgm"):
+            cur = None
+        elif s and not s.startswith(".") and not s.endswith(":"):
+            cur.append(s)
+    return out
+
+
+def test_append_kernel_machine_code(append_isa):
+    ks = _append_kernels(append_isa)
+    assert len(ks) == 2, sorted(ks)
+    for name, ins in ks.items():
+        assert not [i for i in ins if i.startswith("scratch_")], name
+        assert not [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)], name
+    fp8 = next(ins for n, ins in ks.items() if "ILi1E" in n)
+    # x / s and max|x| / 448 are correctly rounded fp32 divisions (the code
+    # decision must match the oracle's fp32 quotient): 16 values + 1 scale
+    assert sum(i.startswith("v_div_fixup_f32") for i in fp8) >= 17
