@@ -12,9 +12,20 @@
 // KV-cache inference the PaddlePaddle 3.0 inference page lists.  An all-zero
 // row gets scale 1 (its codes are all zero either way).
 //
-// One wave per row: lane l moves 16-byte chunk l (8 bf16 values) and lanes
-// 0..7 also chunk 64 + l, so every load and store is a contiguous 1 KB (+128
-// B) span.  A bounded grid strides over the rows.
+// A wave takes kRowsPerWave consecutive rows at a time: it issues every
+// load of them before any store, so each wave keeps about 4.6 KB of reads in
+// flight.  Lane l moves 16-byte chunk l (8 bf16 values) of a row and lanes
+// 0..7 also chunk 64 + l, so every load and store is a contiguous 1 KB
+// (+128 B) span.  A bounded grid strides over the rows.
+//
+// e4m3: the codes must be those of the correctly rounded fp32 quotients x / s.
+// One correctly rounded reciprocal y = 1/s per row, q0 = |x| * y, then one
+// correction step q = q0 + (|x| - q0 * s) * y in fused multiply-adds gives
+// that quotient whenever the remainder |x| - q0 * s stays in the normal range
+// (Markstein's theorem on division through a reciprocal); where it does not,
+// the quotient is below 2^-49 and its code is 0 either way.  A check over
+// every pair of bf16 values (|x| <= max|x|) with s >= 2^-64 finds the same
+// codes as true division; rows with smaller scales take a true division.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,32 +40,25 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;                     // waves (rows in flight) per workgroup
+constexpr int kWaves = 4;                     // waves per workgroup
+constexpr int kRowsPerWave = 4;               // rows a wave loads before it stores any
 constexpr int kRowBytes = kDQK * 2;           // 1152 bytes of a bf16 row
 constexpr int kChunks = kRowBytes / 16;       // 72 chunks of 16 bytes
 constexpr int kTail = kChunks - 64;           // 8 chunks taken by lanes 0..7
 constexpr int kMaxBlocks = 2048;              // 8 workgroups per CU on 256 CUs
 constexpr float kE4M3Max = 448.f;
 
-// fp32 -> e4m3fn (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
-// infinities, largest magnitude 448), round to nearest, ties to even, the
-// magnitude clamped to 448 first.
-__device__ __forceinline__ uint32_t to_e4m3(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), kE4M3Max);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // below 2^-6 the grid is k * 2^-9, k = 0..7; k = 8 is the smallest normal
-    code = uint32_t(__builtin_rintf(a * 512.f));
-  } else {
-    const uint32_t v = __float_as_uint(a);
-    const uint32_t m = v & 0x7FFFFFu;
-    code = (((v >> 23) - 120u) << 3) | (m >> 20);   // exponent rebiased 127 -> 7
-    const uint32_t rest = m & 0xFFFFFu;               // the 20 dropped mantissa bits
-    // a carry out of the mantissa moves to the next binade, as it should
-    code += (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) ? 1u : 0u;
-  }
-  return sign | code;
+// Magnitude in [0, 448] -> e4m3fn code (4 exponent bits with bias 7, 3
+// mantissa bits; no infinities, largest magnitude 448), round to nearest with
+// ties to even; branch-free.
+__device__ __forceinline__ uint32_t e4m3_magnitude(float a) {
+  // below 2^-6 the grid is k * 2^-9, k = 0..7 (k = 8 is the smallest normal)
+  const uint32_t sub = uint32_t(__builtin_rintf(a * 512.f));
+  // from 2^-6 up: cut the fp32 mantissa to 3 bits, round half to even on the
+  // 20 dropped bits (a carry moves to the next binade), rebias 127 -> 7
+  const uint32_t v = __float_as_uint(a);
+  const uint32_t nrm = ((v + 0x7FFFFu + ((v >> 20) & 1u)) >> 20) - (120u << 3);
+  return a < 0.015625f ? sub : nrm;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -67,58 +71,91 @@ __device__ __forceinline__ float chunk_amax(u32x4 c) {
   return m;
 }
 
+// |x| / s as the correctly rounded fp32 quotient, given y = RN(1 / s).
+__device__ __forceinline__ float quotient(float ax, float s, float y, bool exact_div) {
+  if (exact_div) return ax / s;
+  const float q0 = ax * y;
+  return fmaf(fmaf(-q0, s, ax), y, q0);
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float s, float y, bool exact_div) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  return sign | e4m3_magnitude(fminf(quotient(fabsf(x), s, y, exact_div), kE4M3Max));
+}
+
 // 8 bf16 values -> 8 e4m3 codes (byte j of the result = value j)
-__device__ __forceinline__ u32x2 chunk_codes(u32x4 c, float scale) {
+__device__ __forceinline__ u32x2 chunk_codes(u32x4 c, float s, float y, bool exact_div) {
   u32x2 r;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const uint32_t c0 = to_e4m3(bf16_lo(c[2 * w]) / scale);
-    const uint32_t c1 = to_e4m3(bf16_hi(c[2 * w]) / scale);
-    const uint32_t c2 = to_e4m3(bf16_lo(c[2 * w + 1]) / scale);
-    const uint32_t c3 = to_e4m3(bf16_hi(c[2 * w + 1]) / scale);
+    const uint32_t c0 = code_of(bf16_lo(c[2 * w]), s, y, exact_div);
+    const uint32_t c1 = code_of(bf16_hi(c[2 * w]), s, y, exact_div);
+    const uint32_t c2 = code_of(bf16_lo(c[2 * w + 1]), s, y, exact_div);
+    const uint32_t c3 = code_of(bf16_hi(c[2 * w + 1]), s, y, exact_div);
     r[w] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
   }
   return r;
 }
 
+// Destination row (cache slot) of source row r, or -1 when r is padding;
+// counts a row whose slot lies outside the pool and returns -1 for it too.
+__device__ __forceinline__ int64_t dest_slot(const AppendArgs& a, int r, int lane) {
+  const int b = r / a.max_new;            // B * max_new < 2^31 (checked on the host)
+  const int t = r - b * a.max_new;
+  const int n = a.new_lens ? a.new_lens[b] : a.max_new;
+  if (t >= n) return -1;                                    // padding row
+  const int64_t pos = int64_t(a.kv_lens[b]) - n + t;
+  int page = -1;
+  if (n <= a.max_new && pos >= 0 && pos < (int64_t(a.max_pages) << a.page_shift))
+    page = a.block_table[int64_t(b) * a.max_pages + (pos >> a.page_shift)];
+  if (page < 0 || page >= a.num_pages) {
+    if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);
+    return -1;
+  }
+  return (int64_t(page) << a.page_shift) + (pos & ((int64_t(1) << a.page_shift) - 1));
+}
+
 template <int KVD>
 __global__ __launch_bounds__(kWaves * 64) void mla_kv_append_kernel(const AppendArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t rows = int64_t(a.batch) * a.max_new;
-  const int64_t stride = int64_t(gridDim.x) * kWaves;
-  const int64_t pmask = (int64_t(1) << a.page_shift) - 1;
-  // r is uniform over the wave, so every branch below is too
-  for (int64_t r = int64_t(blockIdx.x) * kWaves + (threadIdx.x >> 6); r < rows; r += stride) {
-    const int b = int(r / a.max_new);
-    const int t = int(r - int64_t(b) * a.max_new);
-    const int n = a.new_lens ? a.new_lens[b] : a.max_new;
-    if (t >= n) continue;                                   // padding row
-    const int64_t pos = int64_t(a.kv_lens[b]) - n + t;
-    int page = -1;
-    if (n <= a.max_new && pos >= 0 && pos < (int64_t(a.max_pages) << a.page_shift))
-      page = a.block_table[int64_t(b) * a.max_pages + (pos >> a.page_shift)];
-    if (page < 0 || page >= a.num_pages) {
-      if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);
-      continue;
-    }
-    const int64_t slot = (int64_t(page) << a.page_shift) + (pos & pmask);
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.src + r * kRowBytes);
-    const u32x4 c0 = src[lane];
-    const u32x4 c1 = lane < kTail ? src[64 + lane] : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (KVD == 0) {
-      u32x4* dst = reinterpret_cast<u32x4*>(a.kv + slot * kRowBytes);
-      dst[lane] = c0;
-      if (lane < kTail) dst[64 + lane] = c1;
-    } else {
-      float amax = fmaxf(chunk_amax(c0), chunk_amax(c1));   // c1 is zero past the tail
+  const int64_t rows = int64_t(a.batch) * a.max_new;   // < 2^31 (checked on the host)
+  const int64_t stride = int64_t(gridDim.x) * kWaves * kRowsPerWave;
+  // every row index below is uniform over the wave, so every branch is too
+  for (int64_t r0 = (int64_t(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * kRowsPerWave;
+       r0 < rows; r0 += stride) {
+    int64_t slot[kRowsPerWave];
+    u32x4 c0[kRowsPerWave], c1[kRowsPerWave];
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      float scale = amax / kE4M3Max;
-      if (!(scale > 0.f)) scale = 1.f;
-      uint8_t* dst = a.kv + slot * kDQK;
-      *reinterpret_cast<u32x2*>(dst + 8 * lane) = chunk_codes(c0, scale);
-      if (lane < kTail) *reinterpret_cast<u32x2*>(dst + 8 * (64 + lane)) = chunk_codes(c1, scale);
-      if (lane == 0) a.kv_scale[slot] = scale;
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      slot[u] = r0 + u < rows ? dest_slot(a, int(r0 + u), lane) : -1;
+      c0[u] = c1[u] = u32x4{0u, 0u, 0u, 0u};
+      if (slot[u] >= 0) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.src + int64_t(r0 + u) * kRowBytes);
+        c0[u] = src[lane];
+        if (lane < kTail) c1[u] = src[64 + lane];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      if (slot[u] < 0) continue;
+      if constexpr (KVD == 0) {
+        u32x4* dst = reinterpret_cast<u32x4*>(a.kv + slot[u] * kRowBytes);
+        dst[lane] = c0[u];
+        if (lane < kTail) dst[64 + lane] = c1[u];
+      } else {
+        float amax = fmaxf(chunk_amax(c0[u]), chunk_amax(c1[u]));   // c1 is zero past the tail
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+        float s = amax / kE4M3Max;
+        if (!(s > 0.f)) s = 1.f;
+        const bool exact_div = s < 5.421010862427522e-20f;       // 2^-64
+        const float y = 1.f / s;
+        uint8_t* dst = a.kv + slot[u] * kDQK;
+        *reinterpret_cast<u32x2*>(dst + 8 * lane) = chunk_codes(c0[u], s, y, exact_div);
+        if (lane < kTail)
+          *reinterpret_cast<u32x2*>(dst + 8 * (64 + lane)) = chunk_codes(c1[u], s, y, exact_div);
+        if (lane == 0) a.kv_scale[slot[u]] = s;
+      }
     }
   }
 }
@@ -128,7 +165,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kv_append_kernel(const Append
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, hipStream_t stream) {
   const int64_t rows = int64_t(a.batch) * a.max_new;
   if (rows <= 0) return hipSuccess;
-  const int blocks = int(std::min<int64_t>((rows + kWaves - 1) / kWaves, kMaxBlocks));
+  const int64_t per_block = int64_t(kWaves) * kRowsPerWave;
+  const int blocks = int(std::min<int64_t>((rows + per_block - 1) / per_block, kMaxBlocks));
   if (kv_dtype == 0)
     hipLaunchKernelGGL((mla_kv_append_kernel<0>), dim3(blocks), dim3(kWaves * 64), 0, stream, a);
   else

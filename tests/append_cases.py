@@ -11,9 +11,13 @@ def _bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+N_SPECIAL = 7
+
+
 def special_rows(n_rows, rng):
-    """Rows that reach every branch of the encoder: all zero, one spike, x/s on
-    exact midpoints between codes (s = 1), the subnormal range, wide spreads."""
+    """Rows that reach every path of the quantizer: all zero, one spike, x/s on
+    exact midpoints between codes (s = 1), the subnormal range, wide spreads,
+    scales on both sides of 2^-64, bf16 subnormal inputs; then random rows."""
     rows = []
     z = np.zeros(576, np.float32)
     rows.append(z)
@@ -29,6 +33,13 @@ def special_rows(n_rows, rng):
         ties[2 + 2 * i] = -m
     rows.append(ties)
     rows.append((rng.standard_normal(576) * np.exp2(rng.integers(-24, 10, 576))).astype(np.float32))
+    # scales below 2^-64 (a true division in the kernel), and just above it
+    rows.append((rng.standard_normal(576) * 1e-19).astype(np.float32))
+    rows.append((rng.standard_normal(576) * 2e-17).astype(np.float32))
+    # bf16 subnormals next to a normal maximum
+    sub = (rng.standard_normal(576) * 1e-39).astype(np.float32)
+    sub[5] = 3.0
+    rows.append(sub)
     while len(rows) < n_rows:
         rows.append((rng.standard_normal(576) * rng.choice([0.5, 1e-3, 30.0])).astype(np.float32))
     return _bf16_bits(np.stack(rows[:n_rows]))
@@ -56,8 +67,13 @@ def make_append_case(kv_lens, new_lens, page_size, kv_dtype, seed, max_new=None,
         kv = rng.integers(0, 256, (pool, page_size, 576), dtype=np.uint8)
         sc = rng.standard_normal((pool, page_size)).astype(np.float32)
     rows = special_rows(B * max_new, rng).reshape(B, max_new, 576)
-    # the first new token of every sequence is one of the special rows
-    specials = special_rows(4, rng)
-    rows[:, 0] = specials[np.arange(B) % 4]
+    # the special rows go to the first new tokens that are written
+    specials = special_rows(N_SPECIAL, rng)
+    k = 0
+    for b in range(B):
+        for t in range(min(int(new_lens[b]), max_new)):
+            if k < N_SPECIAL:
+                rows[b, t] = specials[k]
+                k += 1
     return dict(kv=kv, kv_scale=sc, block_table=bt, kv_lens=kv_lens, new_lens=new_lens,
                 new_rows_bits=rows, page_size=page_size, kv_dtype=kv_dtype)

@@ -63,5 +63,27 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
     return binary
 
 
+def build_exhaustive() -> str:
+    """Host binary of append_exhaustive.cpp (the cache-append kernel's
+    arithmetic checked over all inputs), optimized; linked with the emulator
+    runtime, which needs the AddressSanitizer fiber interface."""
+    out = os.path.join(OUT, "exhaustive")
+    src = os.path.join(out, "src")
+    os.makedirs(src, exist_ok=True)
+    for f in KERNEL_FILES:
+        shutil.copyfile(os.path.join(CSRC, f), os.path.join(src, f))
+    shutil.copyfile(os.path.join(HERE, "gfx950_asm.h"), os.path.join(src, "gfx950_asm.h"))
+    flags = ["-std=c++20", "-O2", "-pthread", "-ffp-contract=off", "-fsanitize=address",
+             f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument",
+             "-Wno-psabi"]
+    binary = os.path.join(out, "append_exhaustive")
+    cmd = [compiler(), *flags, "-x", "c++", os.path.join(HERE, "append_exhaustive.cpp"),
+           "-x", "c++", os.path.join(HERE, "emu_runtime.cpp"), "-o", binary]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"exhaustive check build failed:\n{res.stderr[-4000:]}")
+    return binary
+
+
 if __name__ == "__main__":
     print(build())

@@ -70,3 +70,17 @@ def test_prompt_sized_append_strides_the_grid():
 def test_prompt_sized_e4m3_append():
     c = make_append_case([900, 1000], [900, 333], 128, "fp8_e4m3", seed=7, max_new=900)
     assert _compare(c) == 0
+
+
+def test_fast_paths_match_plain_arithmetic_exhaustively():
+    # the kernel's branch-free encoder over every fp32 value in [0, 448], and
+    # its reciprocal + correction quotient over every pair of bf16 values
+    # (|x| <= max|x|, scale >= 2^-64), against the plain forms
+    import os
+    import subprocess
+    from tests.simt_emu import build as _b
+    binary = _b.build_exhaustive()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    res = subprocess.run([binary], capture_output=True, text=True, timeout=600, env=env)
+    assert res.returncode == 0, res.stdout + res.stderr[-2000:]
+    assert "0 differ" in res.stdout and "0 codes differ" in res.stdout
