@@ -26,6 +26,9 @@
 // the quotient is below 2^-49 and its code is 0 either way.  A check over
 // every pair of bf16 values (|x| <= max|x|) with s >= 2^-64 finds the same
 // codes as true division; rows with smaller scales take a true division.
+// The rounding to e4m3 itself is the hardware conversion v_cvt_pk_fp8_f32 on
+// values clamped to +-448, checked against the format's definition for every
+// fp32 value in that range by the GPU check of tests/gpu_checks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,19 +51,6 @@ constexpr int kTail = kChunks - 64;           // 8 chunks taken by lanes 0..7
 constexpr int kMaxBlocks = 2048;              // 8 workgroups per CU on 256 CUs
 constexpr float kE4M3Max = 448.f;
 
-// Magnitude in [0, 448] -> e4m3fn code (4 exponent bits with bias 7, 3
-// mantissa bits; no infinities, largest magnitude 448), round to nearest with
-// ties to even; branch-free.
-__device__ __forceinline__ uint32_t e4m3_magnitude(float a) {
-  // below 2^-6 the grid is k * 2^-9, k = 0..7 (k = 8 is the smallest normal)
-  const uint32_t sub = uint32_t(__builtin_rintf(a * 512.f));
-  // from 2^-6 up: cut the fp32 mantissa to 3 bits, round half to even on the
-  // 20 dropped bits (a carry moves to the next binade), rebias 127 -> 7
-  const uint32_t v = __float_as_uint(a);
-  const uint32_t nrm = ((v + 0x7FFFFu + ((v >> 20) & 1u)) >> 20) - (120u << 3);
-  return a < 0.015625f ? sub : nrm;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -78,23 +68,39 @@ __device__ __forceinline__ float quotient(float ax, float s, float y, bool exact
   return fmaf(fmaf(-q0, s, ax), y, q0);
 }
 
-__device__ __forceinline__ uint32_t code_of(float x, float s, float y, bool exact_div) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  return sign | e4m3_magnitude(fminf(quotient(fabsf(x), s, y, exact_div), kE4M3Max));
+// x / s rounded to fp32 (correctly), clamped to [-448, 448], sign of x kept
+// (also for -0).  v_cvt_pk_fp8_f32 then rounds it to the nearest e4m3 code,
+// ties to even; values within +-448 never reach its overflow handling.
+template <bool kExactDiv>
+__device__ __forceinline__ float scaled(float x, float s, float y) {
+  const float q = fminf(quotient(fabsf(x), s, y, kExactDiv), kE4M3Max);
+  return __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
 }
 
 // 8 bf16 values -> 8 e4m3 codes (byte j of the result = value j)
-__device__ __forceinline__ u32x2 chunk_codes(u32x4 c, float s, float y, bool exact_div) {
+template <bool kExactDiv>
+__device__ __forceinline__ u32x2 chunk_codes(u32x4 c, float s, float y) {
   u32x2 r;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const uint32_t c0 = code_of(bf16_lo(c[2 * w]), s, y, exact_div);
-    const uint32_t c1 = code_of(bf16_hi(c[2 * w]), s, y, exact_div);
-    const uint32_t c2 = code_of(bf16_lo(c[2 * w + 1]), s, y, exact_div);
-    const uint32_t c3 = code_of(bf16_hi(c[2 * w + 1]), s, y, exact_div);
-    r[w] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(scaled<kExactDiv>(bf16_lo(c[2 * w]), s, y),
+                                                   scaled<kExactDiv>(bf16_hi(c[2 * w]), s, y),
+                                                   0, false);
+    r[w] = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(
+        scaled<kExactDiv>(bf16_lo(c[2 * w + 1]), s, y),
+        scaled<kExactDiv>(bf16_hi(c[2 * w + 1]), s, y), lo, true));
   }
   return r;
+}
+
+// Quantize one row (this lane's chunks) and store codes and scale.
+template <bool kExactDiv>
+__device__ __forceinline__ void store_e4m3_row(uint8_t* dst, float* scale_dst, u32x4 c0, u32x4 c1,
+                                               float s, int lane) {
+  const float y = 1.f / s;
+  *reinterpret_cast<u32x2*>(dst + 8 * lane) = chunk_codes<kExactDiv>(c0, s, y);
+  if (lane < kTail) *reinterpret_cast<u32x2*>(dst + 8 * (64 + lane)) = chunk_codes<kExactDiv>(c1, s, y);
+  if (lane == 0) *scale_dst = s;
 }
 
 // Destination row (cache slot) of source row r, or -1 when r is padding;
@@ -148,13 +154,11 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kv_append_kernel(const Append
         for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
         float s = amax / kE4M3Max;
         if (!(s > 0.f)) s = 1.f;
-        const bool exact_div = s < 5.421010862427522e-20f;       // 2^-64
-        const float y = 1.f / s;
         uint8_t* dst = a.kv + slot[u] * kDQK;
-        *reinterpret_cast<u32x2*>(dst + 8 * lane) = chunk_codes(c0[u], s, y, exact_div);
-        if (lane < kTail)
-          *reinterpret_cast<u32x2*>(dst + 8 * (64 + lane)) = chunk_codes(c1[u], s, y, exact_div);
-        if (lane == 0) a.kv_scale[slot[u]] = s;
+        if (s < 5.421010862427522e-20f)                           // 2^-64: true division
+          store_e4m3_row<true>(dst, a.kv_scale + slot[u], c0[u], c1[u], s, lane);
+        else
+          store_e4m3_row<false>(dst, a.kv_scale + slot[u], c0[u], c1[u], s, lane);
       }
     }
   }

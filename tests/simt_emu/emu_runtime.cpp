@@ -420,6 +420,22 @@ static float e4m3_to_f32(unsigned v) {
   return s ? -x : x;
 }
 
+// Nearest e4m3 code by search over the codes' values (monotone in the code
+// for codes 0..126), ties to the even code; the sign is carried over.
+uint32_t e4m3_rne(float x) {
+  if (!(std::fabs(x) <= 448.f)) fail("e4m3 conversion of a value outside +-448 (or NaN)");
+  const float a = std::fabs(x);
+  unsigned lo = 0, hi = 126;                 // value(lo) <= a <= value(hi)
+  while (hi - lo > 1) {
+    const unsigned mid = (lo + hi) / 2;
+    if (e4m3_to_f32(mid) <= a) lo = mid; else hi = mid;
+  }
+  const double dl = double(a) - e4m3_to_f32(lo), dh = double(e4m3_to_f32(hi)) - a;
+  unsigned c = dl < dh ? lo : dh < dl ? hi : ((lo & 1u) ? hi : lo);
+  if (a == e4m3_to_f32(hi)) c = hi;
+  return c | (std::signbit(x) ? 0x80u : 0u);
+}
+
 emu_f32x2 cvt_pk_f32_fp8(int v, bool hi) {
   const unsigned u = unsigned(v) >> (hi ? 16 : 0);
   emu_f32x2 r;

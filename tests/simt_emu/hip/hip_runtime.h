@@ -69,6 +69,13 @@ emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c);
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p);
 emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p);
 emu_f32x2 cvt_pk_f32_fp8(int v, bool hi);
+// fp32 -> OCP e4m3fn, round to nearest with ties to even.  The model covers
+// the range the kernels use, |x| <= 448; anything else stops the run.
+uint32_t e4m3_rne(float x);
+inline int cvt_pk_fp8_f32(float a, float b, int old, bool hi) {
+  const uint32_t w = e4m3_rne(a) | (e4m3_rne(b) << 8), o = uint32_t(old);
+  return int(hi ? (o & 0xFFFFu) | (w << 16) : (o & 0xFFFF0000u) | w);
+}
 inline unsigned long long memtime() {
   static unsigned long long t = 0;
   return ++t;
@@ -86,6 +93,7 @@ inline unsigned long long memtime() {
 #define __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p) emu::ds_read_tr16_b64((const emu_bf16x4*)(p))
 #define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) emu::ds_read_tr8_b64((const emu_i32x2*)(p))
 #define __builtin_amdgcn_cvt_pk_f32_fp8(v, hi) emu::cvt_pk_f32_fp8((v), (hi))
+#define __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, hi) emu::cvt_pk_fp8_f32((a), (b), (old), (hi))
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
 #define __builtin_amdgcn_sched_group_barrier(a, b, c) ((void)0)
 #define __builtin_amdgcn_sched_barrier(a) ((void)0)

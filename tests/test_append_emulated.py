@@ -73,9 +73,9 @@ def test_prompt_sized_e4m3_append():
 
 
 def test_fast_paths_match_plain_arithmetic_exhaustively():
-    # the kernel's branch-free encoder over every fp32 value in [0, 448], and
-    # its reciprocal + correction quotient over every pair of bf16 values
-    # (|x| <= max|x|, scale >= 2^-64), against the plain forms
+    # the kernel's reciprocal + correction quotient over every pair of bf16
+    # values (|x| <= max|x|, scale >= 2^-64) against true division, and the
+    # emulator's e4m3 conversion model against a plain encoder
     import os
     import subprocess
     from tests.simt_emu import build as _b

@@ -23,6 +23,26 @@ import mla_paged_decode_absorbed_amd as mla  # noqa: E402
 DEV = "cuda"
 
 
+def test_hardware_e4m3_conversion_matches_definition():
+    # v_cvt_pk_fp8_f32, which the kernel rounds with, against a plain encoder
+    # of the e4m3 definition for every fp32 value in [-448, 448]
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_checks",
+                        "libe4m3_convert_check.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.e4m3_convert_check.restype = ctypes.c_int
+    lib.e4m3_convert_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    bad = torch.zeros(1, dtype=torch.int64, device=DEV)
+    first = torch.full((16,), -1, dtype=torch.int32, device=DEV)
+    stream = torch.cuda.current_stream()
+    assert lib.e4m3_convert_check(bad.data_ptr(), first.data_ptr(), stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0, [hex(v & 0xFFFFFFFF) for v in first.cpu().tolist()]
+
+
 def _shape(c, batch=None):
     return mla.Shape.make(batch=batch if batch is not None else len(c["kv_lens"]), num_heads=1,
                           max_q_len=1, page_size=c["page_size"], num_pages=c["kv"].shape[0],
