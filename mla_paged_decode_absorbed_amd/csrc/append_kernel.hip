@@ -42,6 +42,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;                     // waves per workgroup
 constexpr int kRowsPerWave = 4;               // rows a wave loads before it stores any
@@ -50,15 +51,32 @@ constexpr int kChunks = kRowBytes / 16;       // 72 chunks of 16 bytes
 constexpr int kTail = kChunks - 64;           // 8 chunks taken by lanes 0..7
 constexpr int kMaxBlocks = 2048;              // 8 workgroups per CU on 256 CUs
 constexpr float kE4M3Max = 448.f;
+static_assert(kRowsPerWave == 4, "the e4m3 path packs the maxima of rows 0-1 and 2-3");
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float chunk_amax(u32x4 c) {
-  float m = 0.f;
+// Largest |x| of this lane's 16 bf16 values of a row, as the bit pattern of
+// the magnitude (for finite values, magnitudes order like their patterns).
+__device__ __forceinline__ uint32_t row_max_bits(u32x4 c0, u32x4 c1) {
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(c[e])), fabsf(bf16_hi(c[e]))));
-  return m;
+  for (int e = 0; e < 4; ++e) {
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, c0[e] & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, c1[e] & 0x7FFF7FFFu));
+  }
+  return m[0] > m[1] ? m[0] : m[1];
+}
+
+// Per-halfword maximum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t w) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    const uint32_t o = uint32_t(__shfl_xor(int(w), k));
+    w = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, w),
+                                                               __builtin_bit_cast(u16x2, o)));
+  }
+  return w;
 }
 
 // |x| / s as the correctly rounded fp32 quotient, given y = RN(1 / s).
@@ -96,8 +114,7 @@ __device__ __forceinline__ u32x2 chunk_codes(u32x4 c, float s, float y) {
 // Quantize one row (this lane's chunks) and store codes and scale.
 template <bool kExactDiv>
 __device__ __forceinline__ void store_e4m3_row(uint8_t* dst, float* scale_dst, u32x4 c0, u32x4 c1,
-                                               float s, int lane) {
-  const float y = 1.f / s;
+                                               float s, float y, int lane) {
   *reinterpret_cast<u32x2*>(dst + 8 * lane) = chunk_codes<kExactDiv>(c0, s, y);
   if (lane < kTail) *reinterpret_cast<u32x2*>(dst + 8 * (64 + lane)) = chunk_codes<kExactDiv>(c1, s, y);
   if (lane == 0) *scale_dst = s;
@@ -141,24 +158,37 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kv_append_kernel(const Append
         if (lane < kTail) c1[u] = src[64 + lane];
       }
     }
+    if constexpr (KVD == 0) {
 #pragma unroll
-    for (int u = 0; u < kRowsPerWave; ++u) {
-      if (slot[u] < 0) continue;
-      if constexpr (KVD == 0) {
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        if (slot[u] < 0) continue;
         u32x4* dst = reinterpret_cast<u32x4*>(a.kv + slot[u] * kRowBytes);
         dst[lane] = c0[u];
         if (lane < kTail) dst[64 + lane] = c1[u];
-      } else {
-        float amax = fmaxf(chunk_amax(c0[u]), chunk_amax(c1[u]));   // c1 is zero past the tail
+      }
+    } else {
+      // max|x| of the four rows: two rows per 32-bit word, reduced over the
+      // wave with packed 16-bit maxima (c1 is zero past the tail; rows not
+      // written are zero too)
+      const uint32_t w01 = row_max_bits(c0[0], c1[0]) | (row_max_bits(c0[1], c1[1]) << 16);
+      const uint32_t w23 = row_max_bits(c0[2], c1[2]) | (row_max_bits(c0[3], c1[3]) << 16);
+      const uint32_t m01 = wave_max_u16x2(w01), m23 = wave_max_u16x2(w23);
+      // lane l works out row (l & 3)'s scale and reciprocal; lane u hands them out
+      const int mine = lane & 3;
+      const uint32_t mb = ((mine < 2 ? m01 : m23) >> (16 * (mine & 1))) & 0xFFFFu;
+      float s = __uint_as_float(mb << 16) / kE4M3Max;
+      if (!(s > 0.f)) s = 1.f;
+      const float y = 1.f / s;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-        float s = amax / kE4M3Max;
-        if (!(s > 0.f)) s = 1.f;
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        if (slot[u] < 0) continue;
+        const float su = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), u));
+        const float yu = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(y), u));
         uint8_t* dst = a.kv + slot[u] * kDQK;
-        if (s < 5.421010862427522e-20f)                           // 2^-64: true division
-          store_e4m3_row<true>(dst, a.kv_scale + slot[u], c0[u], c1[u], s, lane);
+        if (su < 5.421010862427522e-20f)                          // 2^-64: true division
+          store_e4m3_row<true>(dst, a.kv_scale + slot[u], c0[u], c1[u], su, yu, lane);
         else
-          store_e4m3_row<false>(dst, a.kv_scale + slot[u], c0[u], c1[u], s, lane);
+          store_e4m3_row<false>(dst, a.kv_scale + slot[u], c0[u], c1[u], su, yu, lane);
       }
     }
   }

@@ -311,6 +311,10 @@ void block_barrier() { wait_on(S.block_bar); }
 uint32_t readfirstlane(uint32_t v) {
   return wave_op(v, [](int, auto get) { return get(0); });
 }
+uint32_t readlane(uint32_t v, int lane) {
+  if (lane < 0 || lane > 63) fail("readlane of a lane outside the wave");
+  return wave_op(v, [lane](int, auto get) { return get(lane); });
+}
 
 int shfl_xor(int v, int mask) {
   return wave_op(v, [mask](int l, auto get) { return get((l ^ mask) & 63); });

@@ -59,6 +59,7 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, A... args) {
 
 // wave-level operations (every lane of the wave must call them)
 uint32_t readfirstlane(uint32_t v);
+uint32_t readlane(uint32_t v, int lane);
 int shfl_xor(int v, int mask);
 float shfl_xor(float v, int mask);
 int any(int pred);
@@ -84,6 +85,7 @@ inline unsigned long long memtime() {
 
 #define hipLaunchKernelGGL(K, G, B, SH, ST, ...) emu::launch(K, dim3(G), dim3(B), __VA_ARGS__)
 #define __builtin_amdgcn_readfirstlane(x) emu::readfirstlane((uint32_t)(x))
+#define __builtin_amdgcn_readlane(x, l) emu::readlane((uint32_t)(x), (l))
 #define __shfl_xor(v, m) emu::shfl_xor((v), (m))
 #define __any(p) emu::any((p))
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) emu::permlane16_swap((a), (b))
