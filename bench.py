@@ -47,10 +47,13 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+APPEND_SOURCES = ("append_kernel.hip", "append.h", "plan_layout.h")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -79,10 +82,10 @@ def workload_counts(case):
                 kv_tokens=kv_tokens, rows=rows)
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch of the decode kernel from the committed counter
-    summary, or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"{DECODE_KERNEL}_{workload}_traffic.txt")
+def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of a kernel from the committed counter summary, or
+    None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -91,7 +94,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -158,18 +161,19 @@ def append_counts(B, n, kv_dtype, page_size=64):
 
 
 def append_cpu_baseline(rows_np, kv_dtype, seconds: float):
-    """The oracle's append on a bounded sample: chunks of 256 rows of the
-    workload, taken in order, each appended as one sequence's new tokens into
-    a 4-page cache, until ``seconds`` pass."""
+    """The oracle's append on a bounded sample: chunks of (up to) 256 rows of
+    the workload, taken in order, each appended as one sequence's new tokens
+    into a cache of that many slots, until ``seconds`` pass."""
     import numpy as np
 
     from oracle import append_ref
 
-    P, chunk = 64, 256
     n = rows_np.shape[0]
-    kv = np.zeros((chunk // P, P, 576), np.uint16 if kv_dtype == "bf16" else np.uint8)
-    sc = None if kv_dtype == "bf16" else np.zeros((chunk // P, P), np.float32)
-    bt = np.arange(chunk // P, dtype=np.int32)[None, :]
+    P, chunk = 64, min(256, n)
+    pages = (chunk + P - 1) // P
+    kv = np.zeros((pages, P, 576), np.uint16 if kv_dtype == "bf16" else np.uint8)
+    sc = None if kv_dtype == "bf16" else np.zeros((pages, P), np.float32)
+    bt = np.arange(pages, dtype=np.int32)[None, :]
     lens = np.array([chunk], np.int32)
     done = 0
     t0 = time.perf_counter()
@@ -185,7 +189,7 @@ def append_cpu_baseline(rows_np, kv_dtype, seconds: float):
         "value": round(rows_done * (1152 + written) / el / 1e9, 4), "unit": "GB/s", "cores": 1,
         "kind": "oracle",
         "sample": (f"numpy oracle append, {rows_done} rows of the workload in chunks of "
-                   f"{chunk}, each into a 4-page cache, in {el:.1f} s"),
+                   f"{chunk}, each into a {pages}-page cache, in {el:.1f} s"),
     }
 
 
@@ -250,6 +254,7 @@ def main_append(args) -> int:
     t = avg_ms * 1e-3
     achieved = cnt["alg_bytes"] / t / 1e9
     log(f"timed {K} appends: avg {avg_ms * 1e3:.2f} us, {achieved:.1f} GB/s")
+    traffic = read_traffic(args.workload, APPEND_KERNEL, APPEND_SOURCES)
     res = {
         "metric": "MLA cache append µs/call and HBM GB/s",
         "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -260,9 +265,11 @@ def main_append(args) -> int:
                    "kv_len": L, "page_size": P, "kv_dtype": kv_dtype},
         "us_per_call": round(avg_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
                      "kernel": APPEND_KERNEL, "alg_bytes_per_launch": cnt["alg_bytes"]},
-        "wall_s_timed": round(wall, 4), "input_sets": nsets, "cpu_baseline": None,
+        "wall_s_timed": round(wall, 4), "input_sets": nsets,
+        "kernel_source_sha256": kernel_source_hash(APPEND_SOURCES), "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle append for about {args.cpu_seconds:.0f} s")
