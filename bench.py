@@ -287,6 +287,9 @@ def main() -> int:
     ap.add_argument("--workload", default="v3_decode_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time mla_decode_fwd + mla_combine replayed from HIP graphs "
+                         "captured with a fixed-shape plan (us_per_call_graph)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")
@@ -403,6 +406,38 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_avg = sum(warm[k][0].elapsed_time(warm[k][1]) for k in range(K)) / K
 
+    graph_avg = None
+    if args.graph:
+        # one graph per input set, each capturing fwd + combine with the
+        # fixed-shape plan of the same lengths (same split, all workgroups)
+        plf = mla.plan(shape, case.kv_lens, case.q_lens, device=dev, fixed=True)
+        wsf = torch.empty(plf.info.workspace_bytes, dtype=torch.uint8, device=dev)
+        graphs = []
+        for k in range(nsets):
+            q, kv, sc, bt, kvl, ql, out, lse = sets[k]
+            mla.decode_fwd(shape, plf, q, kv, bt, kvl, ql, case.sm_scale, out, lse, wsf,
+                           kv_scale=sc)
+            mla.combine(shape, plf, wsf, ql, out, lse)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                mla.decode_fwd(shape, plf, q, kv, bt, kvl, ql, case.sm_scale, out, lse, wsf,
+                               kv_scale=sc)
+                mla.combine(shape, plf, wsf, ql, out, lse)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for k in range(args.warmup):
+            graphs[k % nsets].replay()
+        torch.cuda.synchronize()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for k in range(K):
+            gev[k][0].record(stream)
+            graphs[k % nsets].replay()
+            gev[k][1].record(stream)
+        torch.cuda.synchronize()
+        graph_avg = sum(gev[k][0].elapsed_time(gev[k][1]) for k in range(K)) / K
+        log(f"graph replays: avg {graph_avg * 1e3:.2f} us per fwd + combine")
+
     t_step = step_avg * 1e-3
     t_fwd = fwd_avg * 1e-3
     kv_gbs = cnt["kv_bytes"] / t_step / 1e9
@@ -438,6 +473,7 @@ def main() -> int:
         "us_per_call": round(step_avg * 1e3, 2),
         "us_fwd_kernel": round(fwd_avg * 1e3, 2),
         "us_per_call_warm": round(warm_avg * 1e3, 2),
+        "us_per_call_graph": None if graph_avg is None else round(graph_avg * 1e3, 2),
         "tflops": round(tflops, 2),
         "pct_roofline_call": round(100 * max(t_hbm, t_mfma) / t_step, 1),
         "roofline": {

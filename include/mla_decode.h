@@ -153,6 +153,30 @@ mla_status mla_decode_plan(const mla_shape* shape, const int32_t* kv_lens_host,
                            void* plan_host, uint64_t plan_bytes, mla_plan_info* info);
 
 /*
+ * Planner for a fixed launch shape, for callers that capture mla_decode_fwd +
+ * mla_combine once (a HIP graph) and replay them with new lengths.
+ *
+ * Same arguments, errors and split as mla_decode_plan, with two differences:
+ *   - the plan image always has num_workgroups workgroups (rounded down to a
+ *     multiple of info->phases); those the split does not need get no items;
+ *   - *info holds launch bounds that every lengths of this shape satisfy, not
+ *     this plan's counts: num_workgroups as above, num_partials =
+ *     2 * num_workgroups (each processor boundary cuts at most one unit, and
+ *     a cut unit has one partial per piece), num_combine = B * ceil(max_q_len
+ *     * H / 128), workspace_bytes and plan_bytes for those bounds.
+ * The plan image records its real counts, and the kernels read them on the
+ * device.  So one info, one plan buffer of info->plan_bytes and one workspace
+ * serve every call of the shape: before each replay copy info->plan_bytes
+ * bytes of the new plan_host into the same device buffer (words past the
+ * image are never read), and keep kv_lens/q_lens in the same device buffers.
+ * phases come from MLA_PHASES as for mla_decode_plan and must not change
+ * between the capture and the replays.
+ */
+mla_status mla_decode_plan_fixed(const mla_shape* shape, const int32_t* kv_lens_host,
+                                 const int32_t* q_lens_host, int32_t num_workgroups,
+                                 void* plan_host, uint64_t plan_bytes, mla_plan_info* info);
+
+/*
  * Main decode kernel launch.
  *
  *   plan_dev     device copy of the plan image described by *info.

@@ -37,7 +37,7 @@ D_ROPE = 64
 EXPORTED_SYMBOLS = (
     "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
-    "mla_decode_fwd", "mla_combine", "mla_kv_append",
+    "mla_decode_fwd", "mla_combine", "mla_kv_append", "mla_decode_plan_fixed",
 )
 
 
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_device_num_cus.argtypes = [I32]
     lib.mla_decode_plan.restype = I32
     lib.mla_decode_plan.argtypes = [sp, P, P, I32, P, U64, ip]
+    lib.mla_decode_plan_fixed.restype = I32
+    lib.mla_decode_plan_fixed.argtypes = [sp, P, P, I32, P, U64, ip]
     lib.mla_decode_fwd.restype = I32
     lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
     lib.mla_combine.restype = I32
@@ -154,8 +156,12 @@ class Plan:
 
 
 def plan(shape: Shape, kv_lens_host, q_lens_host=None, num_workgroups: Optional[int] = None,
-         device=None, upload: bool = True) -> Plan:
-    """Run the host planner and (optionally) copy the plan image to the GPU."""
+         device=None, upload: bool = True, fixed: bool = False) -> Plan:
+    """Run the host planner and (optionally) copy the plan image to the GPU.
+
+    ``fixed=True`` uses ``mla_decode_plan_fixed``: the info then holds launch
+    bounds shared by every lengths of the shape (for graph capture), and the
+    image is padded to ``info.plan_bytes``."""
     lib = load_library()
     kv = np.ascontiguousarray(np.asarray(kv_lens_host, dtype=np.int32))
     ql = None if q_lens_host is None else np.ascontiguousarray(np.asarray(q_lens_host, np.int32))
@@ -173,10 +179,11 @@ def plan(shape: Shape, kv_lens_host, q_lens_host=None, num_workgroups: Optional[
         nbytes = 64
     host = np.zeros((nbytes + 3) // 4, dtype=np.int32)
     info = PlanInfo()
-    st = lib.mla_decode_plan(ctypes.byref(shape), kv.ctypes.data if kv.size else None,
-                             None if ql is None else ql.ctypes.data, int(num_workgroups),
-                             host.ctypes.data, host.nbytes, ctypes.byref(info))
-    _check(st, "mla_decode_plan")
+    fn = lib.mla_decode_plan_fixed if fixed else lib.mla_decode_plan
+    st = fn(ctypes.byref(shape), kv.ctypes.data if kv.size else None,
+            None if ql is None else ql.ctypes.data, int(num_workgroups),
+            host.ctypes.data, host.nbytes, ctypes.byref(info))
+    _check(st, "mla_decode_plan_fixed" if fixed else "mla_decode_plan")
     host = host[: info.plan_bytes // 4].copy()
     dev_t = None
     if upload:

@@ -19,6 +19,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kRowsPerCta = 4;
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineArgs a) {
+  // the grid may be a bound (plans for a fixed launch shape): the plan image
+  // holds the real number of entries
+  if (int(blockIdx.x) >= a.plan[kWNumCombine]) return;
   const int32_t* comb = a.plan + a.plan[kWOffCombine] + blockIdx.x * kCombineWords;
   const int b = comb[0], row0 = comb[1], first = comb[2], n = comb[3];
   const int rb = blockIdx.y * kRowsPerCta + (threadIdx.x >> 6);   // row inside the block

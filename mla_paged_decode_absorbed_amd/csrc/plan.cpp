@@ -87,7 +87,8 @@ uint64_t partial_bytes(int64_t n_partials) {
 }
 
 mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t* q_lens,
-                      int32_t G, int32_t* out, uint64_t out_words, mla_plan_info* info) {
+                      int32_t G, int32_t* out, uint64_t out_words, mla_plan_info* info,
+                      bool fixed_shape) {
   std::vector<Unit> units = make_units(s, kv_lens, q_lens);
 
   const int force_wg = env_int("MLA_NUM_WORKGROUPS", 0);
@@ -142,7 +143,8 @@ mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t*
   while (fill(per_proc, false) > P) ++per_proc;
   const int32_t P_eff = std::max<int32_t>(1, int32_t(fill(per_proc, true)));
   unit_first_piece[units.size()] = int32_t(pieces.size());
-  const int32_t G_eff = P_eff * PH;
+  // a fixed launch shape keeps all P processors (those past P_eff get no items)
+  const int32_t G_eff = (fixed_shape ? P : P_eff) * PH;
 
   // Slots and combine entries (per unit with more than one piece).
   std::vector<int32_t> slot(pieces.size(), -1);
@@ -213,6 +215,19 @@ mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t*
   info->phases = PH;
   info->plan_bytes = uint64_t(words) * sizeof(int32_t);
   info->workspace_bytes = partial_bytes(n_partials);
+  if (fixed_shape) {
+    // launch bounds that hold for every lengths of this shape: at most
+    // 2 (P - 1) partials (a cut at each processor boundary adds at most two)
+    // and one combine entry per 128-row unit; the kernels read the plan's
+    // own counts on the device
+    const int64_t rows = int64_t(s.max_q_len) * s.num_heads;
+    const int64_t unit_bound = int64_t(s.batch) * ((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    info->num_items = int32_t(std::max<int64_t>(N, 1));
+    info->num_partials = 2 * G_eff;
+    info->num_combine = int32_t(unit_bound);
+    info->plan_bytes = plan_words_bound(s, G_eff) * sizeof(int32_t);
+    info->workspace_bytes = partial_bytes(2 * int64_t(G_eff));
+  }
   return MLA_OK;
 }
 

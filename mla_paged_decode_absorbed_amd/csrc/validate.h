@@ -45,6 +45,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 uint64_t plan_words_bound(const mla_shape& s, int32_t G);
 uint64_t partial_bytes(int64_t n_partials);
 mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t* q_lens,
-                      int32_t G, int32_t* out, uint64_t out_words, mla_plan_info* info);
+                      int32_t G, int32_t* out, uint64_t out_words, mla_plan_info* info,
+                      bool fixed_shape);
 
 }  // namespace mla

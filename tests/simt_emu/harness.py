@@ -31,12 +31,13 @@ def _stale() -> bool:
 
 
 def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
-        env_extra: dict | None = None, binary: str | None = None):
-    """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta)."""
+        env_extra: dict | None = None, binary: str | None = None, fixed: bool = False):
+    """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta).
+    ``fixed`` plans with mla_decode_plan_fixed (launch bounds, padded plan)."""
     B, H, qmax = case.batch, case.num_heads, case.max_q_len
     kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
     hdr = np.array([MAGIC, B, H, qmax, case.page_size, case.num_pages, case.max_pages, kv_dtype,
-                    int(case.causal), num_workgroups, 1, 0], dtype=np.int32)
+                    int(case.causal), num_workgroups, 1, int(fixed)], dtype=np.int32)
     with tempfile.TemporaryDirectory() as d:
         fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
         with open(fin, "wb") as f:

@@ -5,7 +5,8 @@
 //
 // usage: run_case <in.bin> <out.bin>
 //   in.bin : int32 header[12] = {magic, B, H, qmax, page_size, num_pages,
-//            max_pages, kv_dtype, causal, num_workgroups, has_q_lens, 0},
+//            max_pages, kv_dtype, causal, num_workgroups, has_q_lens,
+//            fixed_shape (1: plan with mla_decode_plan_fixed)},
 //            float scale, then q (B*qmax*H*576 bf16), kv cache (pages*P*576
 //            elements), kv scales (pages*P fp32, e4m3 only), block table
 //            (B*max_pages int32), kv_lens (B int32), q_lens (B int32, if any)
@@ -148,7 +149,10 @@ int main(int argc, char** argv) {
   if (bound == 0) die("shape rejected by mla_plan_bytes_bound");
   std::vector<int32_t> host_plan(bound / 4 + 1);
   mla_plan_info info{};
-  mla_status st = mla_decode_plan(&s, kvl, ql, nwg, host_plan.data(), host_plan.size() * 4, &info);
+  mla_status st = hd[11] ? mla_decode_plan_fixed(&s, kvl, ql, nwg, host_plan.data(),
+                                                  host_plan.size() * 4, &info)
+                         : mla_decode_plan(&s, kvl, ql, nwg, host_plan.data(),
+                                           host_plan.size() * 4, &info);
   if (st != MLA_OK) die("mla_decode_plan failed");
   // the "device" plan image: exactly plan_bytes long
   void* plan = exact_alloc(info.plan_bytes);

@@ -91,8 +91,9 @@ def _check_partition(shape, pl, kv_lens, q_lens):
             assert n == len(ranges)
             assert [p[2] for p in ranges] == list(range(first, first + n))
             used_slots += [p[2] for p in ranges]
-    assert sorted(used_slots) == list(range(pl.info.num_partials))
-    assert pl.info.num_combine == len(comb)
+    # the image's own counts (a fixed-shape plan's info holds launch bounds)
+    assert sorted(used_slots) == list(range(int(pl.host[5])))
+    assert int(pl.host[4]) == len(comb)
     return items
 
 
@@ -113,6 +114,7 @@ def test_plan_partitions_and_balances(seed, B, qmax, lo, hi, kvd):
     shape = _shape(B=B, qmax=qmax, pages=int(((kv + 63) // 64).sum()), maxp=maxp, kvd=kvd)
     pl = mla.plan(shape, kv, ql, num_workgroups=256, upload=False)
     items = _check_partition(shape, pl, kv, ql)
+    assert (pl.info.num_partials, pl.info.num_combine) == (int(pl.host[5]), int(pl.host[4]))
     # balance: per-workgroup round cost within one item cost (+ a cut's slack) of the mean
     ws = pl.wg_start()
     cost = [sum((int(it[3]) - int(it[2]) + 63) // 64 + 2 for it in items[ws[g]:ws[g + 1]])
@@ -270,3 +272,61 @@ def test_kv_append_validates_before_any_launch(lib):
     with pytest.raises(ValueError, match="skipped"):
         mla.kv_append(small, rows, bt, torch.zeros(2, dtype=torch.int32), kv,
                       skipped=torch.zeros(1, dtype=torch.int64))
+
+
+def _plan_contents(pl):
+    """(per-workgroup item lists, combine entries, image counts) of a plan."""
+    h = pl.host
+    G, N, C, NP = int(h[2]), int(h[3]), int(h[4]), int(h[5])
+    ws = h[int(h[8]):int(h[8]) + G + 1]
+    items = h[int(h[9]):int(h[9]) + 8 * N].reshape(N, 8)
+    per_wg = [items[ws[g]:ws[g + 1]].tolist() for g in range(G)]
+    comb = h[int(h[10]):int(h[10]) + 4 * C].reshape(C, 4).tolist()
+    return per_wg, comb, (N, C, NP, int(h[11]))
+
+
+@pytest.mark.parametrize("seed,B,qmax,G,phases", [
+    (0, 64, 1, 256, 1), (1, 128, 2, 256, 1), (2, 16, 1, 256, 1), (3, 7, 2, 64, 2),
+    (4, 300, 1, 256, 4), (5, 3, 8, 256, 1), (6, 1, 1, 256, 1), (7, 40, 2, 96, 4),
+])
+def test_fixed_shape_plan_is_the_plan_padded(monkeypatch, seed, B, qmax, G, phases):
+    monkeypatch.setenv("MLA_PHASES", str(phases))
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(1, 5000, size=B, endpoint=True).astype(np.int32)
+    ql = rng.integers(0, qmax, size=B, endpoint=True).astype(np.int32)
+    kv = np.maximum(kv, ql).astype(np.int32)
+    maxp = int((kv.max() + 63) // 64)
+    shape = _shape(B=B, qmax=qmax, pages=int(((kv + 63) // 64).sum()) + 1, maxp=maxp)
+    a = mla.plan(shape, kv, ql, num_workgroups=G, upload=False)
+    f = mla.plan(shape, kv, ql, num_workgroups=G, upload=False, fixed=True)
+    wa, ca, na = _plan_contents(a)
+    wf, cf, nf = _plan_contents(f)
+    P = G // a.info.phases
+    assert f.info.num_workgroups == len(wf) == P * a.info.phases
+    assert wf[:len(wa)] == wa and all(not w for w in wf[len(wa):])
+    assert cf == ca and nf == na
+    _check_partition(shape, f, kv, ql)
+    # the launch bounds hold for this plan and for every lengths of the shape
+    units = B * ((qmax * shape.num_heads + 127) // 128)
+    assert f.info.num_combine == units >= na[1]
+    assert f.info.num_partials == 2 * f.info.num_workgroups >= na[2]
+    assert na[2] <= 2 * (P - 1)
+    lib = mla.load_library()
+    assert f.info.plan_bytes == lib.mla_plan_bytes_bound(ctypes.byref(shape), G)
+    assert f.info.workspace_bytes == lib.mla_workspace_bytes_bound(ctypes.byref(shape), G)
+
+
+def test_partials_bound_over_many_lengths():
+    # the fixed-shape workspace holds 2 * G partials: the planner never needs more
+    rng = np.random.default_rng(17)
+    for trial in range(300):
+        B = int(rng.integers(1, 200))
+        G = int(rng.choice([8, 16, 64, 100, 256]))
+        qmax = int(rng.integers(1, 9))
+        kv = rng.integers(1, int(rng.choice([64, 2000, 40000])), size=B).astype(np.int32)
+        ql = rng.integers(0, qmax, size=B, endpoint=True).astype(np.int32)
+        kv = np.maximum(kv, ql).astype(np.int32)
+        shape = _shape(B=B, qmax=qmax, H=int(rng.choice([16, 128])),
+                       pages=int(((kv + 63) // 64).sum()) + 1, maxp=int((kv.max() + 63) // 64))
+        pl = mla.plan(shape, kv, ql, num_workgroups=G, upload=False)
+        assert pl.info.num_partials <= 2 * (pl.info.num_workgroups - 1), (trial, B, G)

@@ -93,6 +93,21 @@ def test_emulated_kernels_match_oracle(kv_lens, q_lens, nwg, phases, kv_dtype, m
     _check(case, out, lse)
 
 
+@pytest.mark.parametrize("kv_lens,q_lens,nwg,phases", [
+    ([700, 130, 5], [2, 2, 1], 8, 1),       # splits and combine entries; padded workgroups
+    ([900, 70], [1, 2], 16, 4),
+    ([0, 200, 64], [0, 2, 1], 12, 1),
+])
+def test_emulated_fixed_shape_plans(kv_lens, q_lens, nwg, phases):
+    # plans for a fixed launch shape: the decode grid is every workgroup, the
+    # combine grid a bound, and the kernels read the real counts from the plan
+    case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=43, sm_scale=1 / math.sqrt(192),
+                     max_q_len=2)
+    out, lse, meta = harness.run(case, nwg, phases, fixed=True,
+                                 env_extra=MODES["issue-drift"])
+    _check(case, out, lse)
+
+
 def test_emulation_catches_a_missing_barrier(tmp_path):
     # the library kernel with its per-round workgroup barrier taken out: a
     # wave refills ring stages other waves still read.  Runs on the CPU only.
