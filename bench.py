@@ -406,7 +406,7 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_avg = sum(warm[k][0].elapsed_time(warm[k][1]) for k in range(K)) / K
 
-    graph_avg = None
+    graph_avg = plan_dev_us = None
     if args.graph:
         # one graph per input set, each capturing fwd + combine with the
         # fixed-shape plan of the same lengths (same split, all workgroups)
@@ -437,6 +437,20 @@ def main() -> int:
         torch.cuda.synchronize()
         graph_avg = sum(gev[k][0].elapsed_time(gev[k][1]) for k in range(K)) / K
         log(f"graph replays: avg {graph_avg * 1e3:.2f} us per fwd + combine")
+        # the device-side planner on the same lengths (one workgroup)
+        kvl0, ql0 = sets[0][4], sets[0][5]
+        dp = mla.plan_device(shape, kvl0, ql0)
+        for _ in range(3):
+            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        for k in range(20):
+            pev[k][0].record(stream)
+            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device)
+            pev[k][1].record(stream)
+        torch.cuda.synchronize()
+        plan_dev_us = sum(pev[k][0].elapsed_time(pev[k][1]) for k in range(20)) / 20 * 1e3
+        log(f"device planner: avg {plan_dev_us:.2f} us")
 
     t_step = step_avg * 1e-3
     t_fwd = fwd_avg * 1e-3
@@ -483,7 +497,9 @@ def main() -> int:
             "kernel": DECODE_KERNEL,
             "alg_bytes_per_launch": cnt["alg_bytes"], "flops_per_launch": cnt["flops"],
         },
-        "plan": {"host_us": round(plan_us, 1), "workgroups": pl.info.num_workgroups,
+        "plan": {"host_us": round(plan_us, 1),
+                 "device_us": None if plan_dev_us is None else round(plan_dev_us, 1),
+                 "workgroups": pl.info.num_workgroups,
                  "items": pl.info.num_items, "partials": pl.info.num_partials,
                  "combine_blocks": pl.info.num_combine},
         "wall_s_timed": round(wall, 4),

@@ -177,6 +177,34 @@ mla_status mla_decode_plan_fixed(const mla_shape* shape, const int32_t* kv_lens_
                                  void* plan_host, uint64_t plan_bytes, mla_plan_info* info);
 
 /*
+ * Device-side planner: the plan mla_decode_plan_fixed would make, built on the
+ * GPU from device-resident lengths (for lengths produced on the GPU, such as
+ * accepted draft tokens, so that they need not be copied to the host).
+ *
+ *   kv_lens, q_lens  [B] int32 device arrays as for mla_decode_fwd (q_lens may
+ *                    be NULL: every sequence has max_q_len tokens).
+ *   plan_dev         device buffer of plan_bytes >= the info->plan_bytes this
+ *                    call returns (mla_plan_bytes_bound), 16-byte aligned;
+ *                    receives the plan image (stream-ordered).
+ *   status           optional int32 device word: MLA_OK, or MLA_ERR_BAD_SHAPE
+ *                    when a length fails the checks of mla_decode_plan (then
+ *                    the plan has no items and the decode writes nothing).
+ *   info             receives the fixed-shape launch bounds (host side, at
+ *                    once), identical to mla_decode_plan_fixed's.
+ *
+ * One workgroup runs the host planner's loops, so the image equals the host
+ * one bit for bit.  Its time grows with the number of 128-row units (tens of
+ * microseconds at a few hundred); a decode step plans once for all layers.
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED, PLAN_TOO_SMALL, UNSUPPORTED (the
+ * shape's lengths, units and pieces exceed the planner's 128 KB of LDS:
+ * about 2000 units), HIP.
+ */
+mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups,
+                                  const int32_t* kv_lens, const int32_t* q_lens, void* plan_dev,
+                                  uint64_t plan_bytes, int32_t* status, mla_plan_info* info,
+                                  mla_stream_t stream);
+
+/*
  * Main decode kernel launch.
  *
  *   plan_dev     device copy of the plan image described by *info.

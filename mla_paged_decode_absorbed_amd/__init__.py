@@ -23,7 +23,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "decode_fwd", "combine",
+    "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "plan_device", "decode_fwd",
+    "combine",
     "decode", "kv_append", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
 ]
 
@@ -38,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
     "mla_decode_fwd", "mla_combine", "mla_kv_append", "mla_decode_plan_fixed",
+    "mla_decode_plan_device",
 )
 
 
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan.argtypes = [sp, P, P, I32, P, U64, ip]
     lib.mla_decode_plan_fixed.restype = I32
     lib.mla_decode_plan_fixed.argtypes = [sp, P, P, I32, P, U64, ip]
+    lib.mla_decode_plan_device.restype = I32
+    lib.mla_decode_plan_device.argtypes = [sp, I32, P, P, P, U64, P, ip, P]
     lib.mla_decode_fwd.restype = I32
     lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
     lib.mla_combine.restype = I32
@@ -190,6 +194,39 @@ def plan(shape: Shape, kv_lens_host, q_lens_host=None, num_workgroups: Optional[
         import torch
         dev_t = torch.from_numpy(host).to(device or "cuda")
     return Plan(info=info, host=host, device=dev_t)
+
+
+def plan_device(shape: Shape, kv_lens, q_lens=None, plan_buf=None, status=None,
+                num_workgroups: Optional[int] = None, stream=None) -> Plan:
+    """Build the fixed-shape plan on the GPU from device length tensors
+    (``mla_decode_plan_device``).  ``plan_buf`` (int32, at least
+    ``info.plan_bytes``) is reused when given; ``status`` (one int32 on the
+    device) receives the plan's status.  The returned Plan has no host image."""
+    import torch
+    lib = load_library()
+    dev = kv_lens.device
+    if num_workgroups is None:
+        num_workgroups = lib.mla_device_num_cus(dev.index or 0)
+        if num_workgroups <= 0:
+            raise MLAError(-num_workgroups, "mla_device_num_cus")
+    for name, t in (("kv_lens", kv_lens), ("q_lens", q_lens), ("status", status)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous int32 tensor on {dev}")
+    if kv_lens.numel() != shape.batch or (q_lens is not None and q_lens.numel() != shape.batch):
+        raise ValueError("kv_lens / q_lens must hold batch elements")
+    if status is not None and status.numel() != 1:
+        raise ValueError("status must hold one element")
+    nbytes = lib.mla_plan_bytes_bound(ctypes.byref(shape), int(num_workgroups))
+    if plan_buf is None:
+        plan_buf = torch.empty((max(nbytes, 64) + 3) // 4, dtype=torch.int32, device=dev)
+    if plan_buf.dtype != torch.int32 or not plan_buf.is_contiguous() or plan_buf.device != dev:
+        raise ValueError(f"plan_buf must be a contiguous int32 tensor on {dev}")
+    info = PlanInfo()
+    st = lib.mla_decode_plan_device(ctypes.byref(shape), int(num_workgroups), _ptr(kv_lens),
+                                    _ptr(q_lens), _ptr(plan_buf), plan_buf.numel() * 4,
+                                    _ptr(status), ctypes.byref(info), _stream(stream))
+    _check(st, "mla_decode_plan_device")
+    return Plan(info=info, host=None, device=plan_buf)
 
 
 def _stream(stream):

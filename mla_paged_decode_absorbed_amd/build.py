@@ -19,7 +19,8 @@ LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "plan.cpp", "decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
+           "plan_kernel.hip"]
 ARCH = "gfx950"
 
 

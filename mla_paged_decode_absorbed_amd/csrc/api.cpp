@@ -9,6 +9,7 @@
 #include "append.h"
 #include "kernels.h"
 #include "mla_decode.h"
+#include "plan_device.h"
 #include "plan_layout.h"
 #include "validate.h"
 
@@ -96,6 +97,43 @@ mla_status mla_decode_plan_fixed(const mla_shape* shape, const int32_t* kv_lens_
   if (st != MLA_OK) return st;
   return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
                     static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info, true);
+}
+
+mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups,
+                                  const int32_t* kv_lens, const int32_t* q_lens, void* plan_dev,
+                                  uint64_t plan_bytes, int32_t* status, mla_plan_info* info,
+                                  mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!plan_dev || !info || (shape->batch > 0 && !kv_lens)) return MLA_ERR_NULL_ARG;
+  if (num_workgroups < 1) return MLA_ERR_BAD_SHAPE;
+  if (!aligned16(plan_dev) || (status && (reinterpret_cast<uintptr_t>(status) & 3u)))
+    return MLA_ERR_MISALIGNED;
+  int32_t G = num_workgroups, PH = 1, item_cost = 0;
+  plan_launch_params(&G, &PH, &item_cost);
+  mla_plan_info bounds{};
+  fixed_launch_info(*shape, G, PH, &bounds);
+  if (plan_bytes < bounds.plan_bytes) return MLA_ERR_PLAN_TOO_SMALL;
+  const int64_t P = bounds.num_workgroups / PH;
+  if (plan_lds_bytes(shape->batch, max_units(*shape), P) > kPlanLdsBytes) return MLA_ERR_UNSUPPORTED;
+  PlanDeviceArgs a{};
+  a.kv_lens = kv_lens;
+  a.q_lens = q_lens;
+  a.plan = static_cast<int32_t*>(plan_dev);
+  a.status = status;
+  a.plan_words = int64_t(bounds.plan_bytes / sizeof(int32_t));
+  a.batch = shape->batch;
+  a.num_heads = shape->num_heads;
+  a.max_q_len = shape->max_q_len;
+  a.causal = shape->causal;
+  a.cap = shape->max_pages_per_seq * shape->page_size;
+  a.P = int32_t(P);
+  a.PH = PH;
+  a.item_cost = item_cost;
+  if (launch_plan(a, max_units(*shape), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  *info = bounds;
+  return MLA_OK;
 }
 
 mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, const void* plan_dev,

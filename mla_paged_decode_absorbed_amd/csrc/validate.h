@@ -47,5 +47,12 @@ uint64_t partial_bytes(int64_t n_partials);
 mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t* q_lens,
                       int32_t G, int32_t* out, uint64_t out_words, mla_plan_info* info,
                       bool fixed_shape);
+// Most 128-row units any lengths of the shape can have.
+int64_t max_units(const mla_shape& s);
+// Workgroups (MLA_NUM_WORKGROUPS may force them), phases (MLA_PHASES) and the
+// per-piece cost (MLA_ITEM_COST_ROUNDS) the planners use.
+void plan_launch_params(int32_t* G, int32_t* PH, int32_t* item_cost);
+// The launch bounds of a fixed-shape plan (see mla_decode_plan_fixed).
+void fixed_launch_info(const mla_shape& s, int32_t G, int32_t PH, mla_plan_info* info);
 
 }  // namespace mla

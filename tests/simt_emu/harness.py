@@ -107,5 +107,33 @@ def run_append(kv, kv_scale, block_table, kv_lens, new_lens, new_rows_bits, page
     return kv_out, sc_out, (skipped if with_counter else None)
 
 
+PLAN_MAGIC = 0x4D4C4150
+
+
+def run_plan_device(batch, num_heads, max_q_len, page_size, num_pages, max_pages, causal,
+                    kv_lens, q_lens, num_workgroups, env_extra=None, timeout: float = 600.0):
+    """mla_decode_plan_device on the emulator.  Returns (call status, plan
+    status, image words of the plan-size bound)."""
+    hdr = np.array([PLAN_MAGIC, batch, num_heads, max_q_len, page_size, num_pages, max_pages,
+                    int(causal), num_workgroups, int(q_lens is not None), 0, 0], dtype=np.int32)
+    with tempfile.TemporaryDirectory() as d:
+        fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
+        with open(fin, "wb") as f:
+            f.write(hdr.tobytes())
+            f.write(np.ascontiguousarray(kv_lens, dtype=np.int32).tobytes())
+            if q_lens is not None:
+                f.write(np.ascontiguousarray(q_lens, dtype=np.int32).tobytes())
+        env = dict(os.environ)
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+        if env_extra:
+            env.update(env_extra)
+        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+                             timeout=timeout, env=env)
+        if res.returncode != 0:
+            raise RuntimeError(f"emulated planner failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
+        raw = np.fromfile(fout, dtype=np.int32)
+    return int(raw[0]), int(raw[1]), raw[3:3 + int(raw[2])].copy()
+
+
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -84,6 +84,10 @@ inline unsigned long long memtime() {
 }  // namespace emu
 
 #define hipLaunchKernelGGL(K, G, B, SH, ST, ...) emu::launch(K, dim3(G), dim3(B), __VA_ARGS__)
+namespace emu {
+void block_barrier();
+}
+#define __syncthreads() emu::block_barrier()
 #define __builtin_amdgcn_readfirstlane(x) emu::readfirstlane((uint32_t)(x))
 #define __builtin_amdgcn_readlane(x, l) emu::readlane((uint32_t)(x), (l))
 #define __shfl_xor(v, m) emu::shfl_xor((v), (m))

@@ -13,6 +13,12 @@
 //   out.bin: int32 {num_items, num_partials, num_combine, phases}, then O
 //            (B*qmax*H*512 bf16) and LSE (B*qmax*H fp32)
 //
+// A device-planner case (mla_decode_plan_device) has its own magic:
+//   in.bin : int32 header[12] = {magic, B, H, qmax, page_size, num_pages,
+//            max_pages, causal, num_workgroups, has_q_lens, 0, 0}, then
+//            kv_lens, q_lens (if any)
+//   out.bin: int32 call status, plan status, image words, then the image
+//
 // A cache-append case (mla_kv_append) has its own magic:
 //   in.bin : int32 header[12] = {magic, B, max_new, page_size, num_pages,
 //            max_pages, kv_dtype, has_new_lens, has_skipped, 0, 0, 0}, then
@@ -100,6 +106,49 @@ int run_append(FILE* f, const int32_t* hd, const char* out_path) {
   return 0;
 }
 
+int run_plan(FILE* f, const int32_t* hd, const char* out_path) {
+  mla_shape s{};
+  s.batch = hd[1];
+  s.num_heads = hd[2];
+  s.max_q_len = hd[3];
+  s.d_latent = 512;
+  s.d_rope = 64;
+  s.page_size = hd[4];
+  s.num_pages = hd[5];
+  s.max_pages_per_seq = hd[6];
+  s.kv_dtype = MLA_KV_BF16;
+  s.causal = hd[7];
+  const int nwg = hd[8];
+  const bool has_ql = hd[9] != 0;
+  int32_t* kvl = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4));
+  int32_t* ql = has_ql ? static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4)) : nullptr;
+  read_into(f, kvl, size_t(s.batch) * 4);
+  if (ql) read_into(f, ql, size_t(s.batch) * 4);
+  std::fclose(f);
+  const uint64_t bound = mla_plan_bytes_bound(&s, nwg);
+  if (bound == 0) die("shape rejected by mla_plan_bytes_bound");
+  // the "device" plan buffer, exactly the bound, filled with a pattern
+  int32_t* plan = static_cast<int32_t*>(exact_alloc((bound + 15) / 16 * 16, 16));
+  for (uint64_t w = 0; w < (bound + 15) / 16 * 4; ++w) plan[w] = 0x5A5A5A5A;
+  int32_t* status = static_cast<int32_t*>(exact_alloc(4, 4));
+  *status = -1;
+  mla_plan_info info{};
+  const mla_status st = mla_decode_plan_device(&s, nwg, kvl, ql, plan, (bound + 15) / 16 * 16,
+                                               status, &info, nullptr);
+  FILE* g = std::fopen(out_path, "wb");
+  if (!g) die("cannot open output");
+  const int32_t words = int32_t(bound / 4);
+  const int32_t meta[3] = {int32_t(st), *status, words};
+  std::fwrite(meta, 1, sizeof meta, g);
+  std::fwrite(plan, 1, size_t(words) * 4, g);
+  std::fclose(g);
+  std::free(kvl);
+  std::free(ql);
+  std::free(plan);
+  std::free(status);
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -110,6 +159,7 @@ int main(int argc, char** argv) {
   float scale;
   read_into(f, hd, sizeof hd);
   if (hd[0] == 0x4d4c4141) return run_append(f, hd, argv[2]);
+  if (hd[0] == 0x4d4c4150) return run_plan(f, hd, argv[2]);
   read_into(f, &scale, sizeof scale);
   if (hd[0] != 0x4d4c4145) die("bad magic");
   mla_shape s{};
