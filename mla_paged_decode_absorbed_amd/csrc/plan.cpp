@@ -100,20 +100,33 @@ mla_status build_plan(const mla_shape& s, const int32_t* kv_lens, const int32_t*
   }
   const int32_t n_units = int32_t(units.size());
 
-  const int64_t per_proc = plan_per_proc(units.data(), n_units, item_cost, P);
+  auto unit_at = [&](int32_t i) { return units[size_t(i)]; };
+  const int64_t total = plan_total(unit_at, n_units, item_cost);
+  const int64_t per_proc = plan_per_proc<int64_t>(unit_at, n_units, total, item_cost, P);
   std::vector<PlanPiece> pieces(size_t(n_units) + P + 1);
   std::vector<int32_t> unit_first_piece(size_t(n_units) + 1, 0);
-  int32_t n_pieces = 0;
-  const int64_t used = plan_fill(units.data(), n_units, per_proc, item_cost, P, true,
-                                 pieces.data(), &n_pieces, unit_first_piece.data());
+  const int64_t used = plan_fill<int64_t>(
+      unit_at, n_units, per_proc, item_cost, P, true,
+      [&](int32_t i, const PlanPiece& pc) { pieces[size_t(i)] = pc; },
+      [&](int32_t u, int32_t i) { unit_first_piece[size_t(u)] = i; });
+  const int32_t n_pieces = unit_first_piece[size_t(n_units)];
   const int32_t P_eff = std::max<int32_t>(1, int32_t(used));
   // a fixed launch shape keeps all P processors (those past P_eff get no items)
   const int32_t G_out = (fixed_shape ? P : P_eff) * PH;
 
   std::vector<int32_t> slot(size_t(n_pieces) + 1), comb(size_t(n_units) * kCombineWords + 1);
   int32_t C = 0, n_partials = 0;
-  plan_slots(units.data(), n_units, unit_first_piece.data(), slot.data(), comb.data(), &C,
-             &n_partials);
+  plan_slots(
+      unit_at, [&](int32_t u) { return unit_first_piece[size_t(u)]; }, n_units,
+      [&](int32_t p, int32_t v) { slot[size_t(p)] = v; },
+      [&](int32_t e, int32_t b, int32_t row0, int32_t first, int32_t n) {
+        int32_t* c = comb.data() + size_t(e) * kCombineWords;
+        c[0] = b;
+        c[1] = row0;
+        c[2] = first;
+        c[3] = n;
+      },
+      &C, &n_partials);
   const int64_t words = plan_write_image(units.data(), pieces.data(), n_pieces, slot.data(),
                                          comb.data(), C, n_partials, PH, G_out, out,
                                          int64_t(out_words));

@@ -38,6 +38,25 @@ constexpr int kMinPieceRounds = 2;
 
 __host__ __device__ inline int64_t plan_round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 
+// A value every lane of the device planner's wave holds alike: on the GPU it
+// is read from the first lane, so the loops below run on the scalar unit.
+__host__ __device__ inline int32_t plan_uniform(int32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(v);
+#else
+  return v;
+#endif
+}
+
+__host__ __device__ inline PlanUnit plan_load(const PlanUnit& u) {
+  return {plan_uniform(u.b), plan_uniform(u.row0), plan_uniform(u.rows), plan_uniform(u.L),
+          plan_uniform(u.rounds)};
+}
+
+__host__ __device__ inline PlanPiece plan_load(const PlanPiece& p) {
+  return {plan_uniform(p.proc), plan_uniform(p.unit), plan_uniform(p.k0), plan_uniform(p.k1)};
+}
+
 // Units of sequence b (q query tokens, L keys): ceil(q * H / 128) of them.
 // Writes them to out (if not null) and returns their number.
 __host__ __device__ inline int32_t plan_units_of(int32_t b, int32_t q, int32_t L, int32_t H,
@@ -51,35 +70,42 @@ __host__ __device__ inline int32_t plan_units_of(int32_t b, int32_t q, int32_t L
   return n;
 }
 
+// The loops below read units through unit_at(i) and write results through
+// put_*(...) callables, so the host can run them over plain arrays and the
+// device planner over arrays it caches in registers.
+
 // Greedy fill with a budget of per_proc per processor.  Returns the number
 // of processors used; without recording it stops early and returns P + 2 as
-// soon as more than P are needed.  Recording writes the pieces (in unit
-// order, so also in processor order), their count, and the first piece of
-// every unit (unit_first_piece[n_units] = the piece count).
-__host__ __device__ inline int64_t plan_fill(const PlanUnit* units, int32_t n_units,
-                                             int64_t per_proc, int32_t item_cost, int64_t P,
-                                             bool record, PlanPiece* pieces, int32_t* n_pieces,
-                                             int32_t* unit_first_piece) {
-  int64_t proc = 0;
-  int64_t budget = per_proc;
+// soon as more than P are needed.  Recording passes the pieces (in unit
+// order, so also in processor order) to put_piece(index, piece) and the
+// first piece of every unit to put_first(unit, index), with
+// put_first(n_units, piece count) last.
+// I is the integer type of the budgets: int64_t always works; int32_t (fast
+// scalar compares on the GPU) when the total cost of all units fits in it.
+template <class I, class UnitAt, class PutPiece, class PutFirst>
+__host__ __device__ inline I plan_fill(UnitAt&& unit_at, int32_t n_units, I per_proc,
+                                       int32_t item_cost, I P, bool record,
+                                       PutPiece&& put_piece, PutFirst&& put_first) {
+  I proc = 0;
+  I budget = per_proc;
   int32_t np = 0;
   for (int32_t ui = 0; ui < n_units; ++ui) {
-    const PlanUnit u = units[ui];
-    if (record) unit_first_piece[ui] = np;
+    const PlanUnit u = unit_at(ui);
+    if (record) put_first(ui, np);
     int32_t k = 0;   // rounds of u already placed
     for (;;) {
-      const int32_t rem = u.rounds - k;
-      const int64_t avail = budget - item_cost;
+      const I rem = u.rounds - k;
+      const I avail = budget - item_cost;
       if (rem <= avail + kMinPieceRounds / 2) {
-        if (record) pieces[np++] = {int32_t(proc), ui, k * kRoundTokens, u.L};
+        if (record) put_piece(np++, PlanPiece{int32_t(proc), ui, k * kRoundTokens, u.L});
         budget -= rem + item_cost;
         break;
       }
       if (avail >= kMinPieceRounds && rem - avail >= kMinPieceRounds) {
         if (record) {
-          const int64_t k1 = (k + avail) * kRoundTokens;
-          pieces[np++] = {int32_t(proc), ui, k * kRoundTokens,
-                          int32_t(k1 < u.L ? k1 : u.L)};
+          const int64_t k1 = (int64_t(k) + avail) * kRoundTokens;
+          put_piece(np++, PlanPiece{int32_t(proc), ui, k * kRoundTokens,
+                                    int32_t(k1 < u.L ? k1 : u.L)});
         }
         k += int32_t(avail);
       }
@@ -92,45 +118,53 @@ __host__ __device__ inline int64_t plan_fill(const PlanUnit* units, int32_t n_un
       budget = per_proc;
     }
   }
-  if (record) {
-    *n_pieces = np;
-    unit_first_piece[n_units] = np;
-  }
+  if (record) put_first(n_units, np);
   return proc + (budget < per_proc ? 1 : 0);
 }
 
-// The smallest budget, from the even share up, whose fill fits P processors.
-__host__ __device__ inline int64_t plan_per_proc(const PlanUnit* units, int32_t n_units,
-                                                 int32_t item_cost, int64_t P) {
+// Total cost of all units: rounds plus the per-piece cost of one piece each.
+template <class UnitAt>
+__host__ __device__ inline int64_t plan_total(UnitAt&& unit_at, int32_t n_units,
+                                              int32_t item_cost) {
   int64_t total = 0;
-  for (int32_t ui = 0; ui < n_units; ++ui) total += units[ui].rounds + item_cost;
+  for (int32_t ui = 0; ui < n_units; ++ui) total += unit_at(ui).rounds + item_cost;
+  return total;
+}
+
+// The smallest budget, from the even share up, whose fill fits P processors.
+template <class I, class UnitAt>
+__host__ __device__ inline I plan_per_proc(UnitAt&& unit_at, int32_t n_units, int64_t total,
+                                           int32_t item_cost, I P) {
   const int64_t Pd = P > 1 ? P : 1;
-  int64_t per_proc = (total + Pd - 1) / Pd;
+  I per_proc = I((total + Pd - 1) / Pd);
   if (per_proc < item_cost + kMinPieceRounds) per_proc = item_cost + kMinPieceRounds;
-  while (plan_fill(units, n_units, per_proc, item_cost, P, false, nullptr, nullptr, nullptr) > P)
+  auto none = [](int32_t, auto) {};
+  while (plan_fill<I>(unit_at, n_units, per_proc, item_cost, P, false, none, none) > P)
     ++per_proc;
   return per_proc;
 }
 
-// Partial slots (per piece; -1 for a unit in one piece) and combine entries
-// {b, row0, first slot, pieces} of the units cut in several pieces, both in
-// unit order.
-__host__ __device__ inline void plan_slots(const PlanUnit* units, int32_t n_units,
-                                           const int32_t* unit_first_piece, int32_t* slot,
-                                           int32_t* comb, int32_t* n_comb, int32_t* n_partials) {
+// Partial slots and combine entries, both in unit order: the pieces of a unit
+// cut in several get consecutive slots (put_slot(piece, slot)) and the unit a
+// combine entry put_comb(entry, b, row0, first slot, pieces); a unit in one
+// piece gets slot -1.  first_at(u) is the unit's first piece (first_at(n_units)
+// the piece count).
+template <class UnitAt, class FirstAt, class PutSlot, class PutComb>
+__host__ __device__ inline void plan_slots(UnitAt&& unit_at, FirstAt&& first_at, int32_t n_units,
+                                           PutSlot&& put_slot, PutComb&& put_comb,
+                                           int32_t* n_comb, int32_t* n_partials) {
   int32_t np = 0, nc = 0;
+  int32_t p0 = n_units > 0 ? first_at(0) : 0;
   for (int32_t ui = 0; ui < n_units; ++ui) {
-    const int32_t p0 = unit_first_piece[ui], p1 = unit_first_piece[ui + 1];
+    const int32_t p1 = first_at(ui + 1);
     if (p1 - p0 <= 1) {
-      for (int32_t p = p0; p < p1; ++p) slot[p] = -1;
-      continue;
+      for (int32_t p = p0; p < p1; ++p) put_slot(p, -1);
+    } else {
+      const PlanUnit u = unit_at(ui);
+      put_comb(nc++, u.b, u.row0, np, p1 - p0);
+      for (int32_t p = p0; p < p1; ++p) put_slot(p, np++);
     }
-    int32_t* c = comb + int64_t(nc++) * kCombineWords;
-    c[0] = units[ui].b;
-    c[1] = units[ui].row0;
-    c[2] = np;
-    c[3] = p1 - p0;
-    for (int32_t p = p0; p < p1; ++p) slot[p] = np++;
+    p0 = p1;
   }
   *n_comb = nc;
   *n_partials = np;
@@ -146,8 +180,10 @@ __host__ __device__ inline int64_t plan_write_image(
     int32_t* out, int64_t out_words) {
   const int32_t rows_per_item = kRowsPerBlock / PH;
   int64_t N = 0;
-  for (int32_t i = 0; i < n_pieces; ++i)
-    for (int32_t k = 0; k < PH && k * rows_per_item < units[pieces[i].unit].rows; ++k) ++N;
+  for (int32_t i = 0; i < n_pieces; ++i) {
+    const int32_t rows = plan_uniform(units[plan_uniform(pieces[i].unit)].rows);
+    for (int32_t k = 0; k < PH && k * rows_per_item < rows; ++k) ++N;
+  }
   const int64_t off_wg = kHeaderWords;
   const int64_t off_items = off_wg + plan_round_up8(G_out + 1);
   const int64_t off_comb = off_items + N * kItemWords;
@@ -171,19 +207,20 @@ __host__ __device__ inline int64_t plan_write_image(
   int32_t n = 0, i = 0;
   for (int32_t p = 0; p < G_out / PH; ++p) {
     const int32_t i0 = i;
-    while (i < n_pieces && pieces[i].proc == p) ++i;
+    while (i < n_pieces && plan_uniform(pieces[i].proc) == p) ++i;
     for (int32_t k = 0; k < PH; ++k) {
       wg_start[p * PH + k] = n;
       for (int32_t j = i0; j < i; ++j) {
-        const PlanUnit& u = units[pieces[j].unit];
+        const PlanPiece pc = plan_load(pieces[j]);
+        const PlanUnit u = plan_load(units[pc.unit]);
         const int32_t off = k * rows_per_item;
         if (off >= u.rows) continue;
         int32_t* it = items + int64_t(n++) * kItemWords;
         it[0] = u.b;
         it[1] = u.row0 + off;
-        it[2] = pieces[j].k0;
-        it[3] = pieces[j].k1;
-        it[4] = slot[j];
+        it[2] = pc.k0;
+        it[3] = pc.k1;
+        it[4] = plan_uniform(slot[j]);
         it[5] = off;
         it[6] = 0;
         it[7] = 0;
@@ -191,7 +228,8 @@ __host__ __device__ inline int64_t plan_write_image(
     }
   }
   for (int32_t g = (G_out / PH) * PH; g <= G_out; ++g) wg_start[g] = n;
-  for (int64_t w = 0; w < int64_t(n_comb) * kCombineWords; ++w) out[off_comb + w] = comb[w];
+  for (int64_t w = 0; w < int64_t(n_comb) * kCombineWords; ++w)
+    out[off_comb + w] = plan_uniform(comb[w]);
   return words;
 }
 
