@@ -33,6 +33,21 @@ mla_status check_info(const mla_shape* s, const mla_plan_info* info) {
   return MLA_OK;
 }
 
+mla_status host_plan(const mla_shape* shape, const int32_t* kv_lens_host,
+                     const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
+                     uint64_t plan_bytes, mla_plan_info* info, bool fixed_shape) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  if ((shape->batch > 0 && !kv_lens_host) || !plan_host || !info) return MLA_ERR_NULL_ARG;
+  if (num_workgroups < 1) return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(plan_host) & 3u) != 0) return MLA_ERR_MISALIGNED;
+  st = validate_lengths(shape, kv_lens_host, q_lens_host);
+  if (st != MLA_OK) return st;
+  return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
+                    static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info,
+                    fixed_shape);
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,29 +89,15 @@ int32_t mla_device_num_cus(int32_t device) {
 mla_status mla_decode_plan(const mla_shape* shape, const int32_t* kv_lens_host,
                            const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
                            uint64_t plan_bytes, mla_plan_info* info) {
-  mla_status st = validate_shape(shape);
-  if (st != MLA_OK) return st;
-  if ((shape->batch > 0 && !kv_lens_host) || !plan_host || !info) return MLA_ERR_NULL_ARG;
-  if (num_workgroups < 1) return MLA_ERR_BAD_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(plan_host) & 3u) != 0) return MLA_ERR_MISALIGNED;
-  st = validate_lengths(shape, kv_lens_host, q_lens_host);
-  if (st != MLA_OK) return st;
-  return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
-                    static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info, false);
+  return host_plan(shape, kv_lens_host, q_lens_host, num_workgroups, plan_host, plan_bytes, info,
+                   false);
 }
 
 mla_status mla_decode_plan_fixed(const mla_shape* shape, const int32_t* kv_lens_host,
                                  const int32_t* q_lens_host, int32_t num_workgroups,
                                  void* plan_host, uint64_t plan_bytes, mla_plan_info* info) {
-  mla_status st = validate_shape(shape);
-  if (st != MLA_OK) return st;
-  if ((shape->batch > 0 && !kv_lens_host) || !plan_host || !info) return MLA_ERR_NULL_ARG;
-  if (num_workgroups < 1) return MLA_ERR_BAD_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(plan_host) & 3u) != 0) return MLA_ERR_MISALIGNED;
-  st = validate_lengths(shape, kv_lens_host, q_lens_host);
-  if (st != MLA_OK) return st;
-  return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
-                    static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info, true);
+  return host_plan(shape, kv_lens_host, q_lens_host, num_workgroups, plan_host, plan_bytes, info,
+                   true);
 }
 
 mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups,

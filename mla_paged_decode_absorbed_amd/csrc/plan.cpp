@@ -7,7 +7,6 @@
 // fetched from HBM once and the other reads hit that XCD's L2.
 #include <algorithm>
 #include <cstdlib>
-#include <cstring>
 #include <vector>
 
 #include "mla_decode.h"
@@ -31,7 +30,7 @@ int env_int(const char* name, int dflt) {
 // the partials, for every shape tried (DeepSeek-V3 decode 126 vs 181 us/call,
 // long-context e4m3 255 vs 1383 us/call), so 1 is the default; MLA_PHASES=2
 // or 4 selects the shared-key schedule.
-int choose_phases(int64_t /*n_units*/, int32_t G) {
+int choose_phases(int32_t G) {
   const int forced = env_int("MLA_PHASES", 0);
   if ((forced == 2 || forced == 4) && G % forced == 0) return forced;
   return 1;
@@ -40,8 +39,7 @@ int choose_phases(int64_t /*n_units*/, int32_t G) {
 }  // namespace
 
 uint64_t plan_words_bound(const mla_shape& s, int32_t G) {
-  const int64_t rows = int64_t(s.max_q_len) * s.num_heads;
-  const int64_t units = int64_t(s.batch) * ((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t units = max_units(s);
   // pieces <= units + processors; every piece expands to at most 4 items
   return uint64_t(kHeaderWords + round_up8(G + 1) + 4 * (units + G) * kItemWords +
                   (units + G) * kCombineWords + 8);
@@ -80,7 +78,7 @@ int64_t max_units(const mla_shape& s) {
 void plan_launch_params(int32_t* G, int32_t* PH, int32_t* item_cost) {
   const int force_wg = env_int("MLA_NUM_WORKGROUPS", 0);
   if (force_wg > 0) *G = force_wg;
-  *PH = choose_phases(0, *G);
+  *PH = choose_phases(*G);
   *item_cost = std::max(0, env_int("MLA_ITEM_COST_ROUNDS", kItemCostRounds));
 }
 
