@@ -30,9 +30,13 @@ What it computes, and where the pages state it:
   3.0 page on low-bit KV cache).
 * Writing a step's new tokens into their page slots, quantizing them with
   that per-token scale for an e4m3 cache (``append_ref``).
+* Tree-shaped drafts: each draft token sees the cached prefix and the drafts
+  its mask names (``tree_ref``; EAGLE-style drafts of the Dewu deployment
+  slides, verified in one pass as on the PaddlePaddle 3.0 page).
 
 Every function below is pinned by ``tests/test_oracle_pins.py`` (the
-append by ``tests/test_oracle_append_pins.py``) against something other than
+append by ``tests/test_oracle_append_pins.py``, the tree drafts by
+``tests/test_oracle_tree_pins.py``) against something other than
 itself (closed forms, the non-absorbed identity, brute force, library casts,
 invariants); see each docstring.
 """
@@ -53,3 +57,4 @@ from .append_ref import (  # noqa: F401
     kv_append_ref,
     quantize_rows_e4m3,
 )
+from .tree_ref import mla_decode_tree_ref, tree_visible_keys  # noqa: F401
