@@ -102,9 +102,10 @@ def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOUR
         return None
 
 
-def cpu_baseline(case, seconds: float, kv_bytes_total: int):
+def cpu_baseline(case, seconds: float, kv_bytes_total: int, seq_fn=None):
     """Time the float64 oracle on the sequences of the same workload, taken in
-    order (and cycling) until ``seconds`` have passed."""
+    order (and cycling) until ``seconds`` have passed.  ``seq_fn(b)`` replaces
+    the decode oracle of one sequence (the tree-draft oracle, for instance)."""
     import numpy as np
 
     import oracle
@@ -119,7 +120,10 @@ def cpu_baseline(case, seconds: float, kv_bytes_total: int):
     t0 = time.perf_counter()
     while order and time.perf_counter() - t0 < seconds:
         b = order[done % len(order)]
-        oracle.mla_decode_ref_seq(case, b)
+        if seq_fn is None:
+            oracle.mla_decode_ref_seq(case, b)
+        else:
+            seq_fn(b)
         done += 1
         tokens += int(case.kv_lens[b])
     el = time.perf_counter() - t0
@@ -328,7 +332,16 @@ def main() -> int:
 
     log(f"workload {args.workload}: generating inputs")
     case = workload(args.workload)
+    full = case
+    tree = case.meta.get("tree_mask")
+    if tree is not None:
+        # tree-shaped drafts: the decode kernels run over the cached prefix
+        # (kv_len - q_len keys, non-causal) and mla_tree_attend adds the drafts
+        import dataclasses
+        case = dataclasses.replace(full, kv_lens=(full.kv_lens - full.q_lens).astype(np.int32),
+                                   causal=False)
     cnt = workload_counts(case)
+    kv_total = workload_counts(full)["kv_bytes"]
     kvd = mla.KV_BF16 if case.kv_dtype == "bf16" else mla.KV_FP8_E4M3
     shape = mla.Shape.make(batch=case.batch, num_heads=case.num_heads, max_q_len=case.max_q_len,
                            page_size=case.page_size, num_pages=case.num_pages,
@@ -358,6 +371,9 @@ def main() -> int:
         lse = torch.empty((case.batch, case.max_q_len, case.num_heads), dtype=torch.float32,
                           device=dev)
         sets.append((q, kv, sc, bt, kvl, ql, out, lse))
+    if tree is not None:
+        kvl_full = torch.from_numpy(full.kv_lens).to(dev)
+        mask_d = torch.from_numpy(np.asarray(tree, np.uint32).view(np.int32)).to(dev)
     ws = mla.alloc_workspace(pl, dev) if pl.info.num_partials > 0 else None
     stream = torch.cuda.current_stream()
     log(f"plan: {pl.info.num_workgroups} workgroups, {pl.info.num_items} items, "
@@ -371,6 +387,9 @@ def main() -> int:
     def step_combine(k):
         q, kv, sc, bt, kvl, ql, out, lse = sets[k % nsets]
         mla.combine(shape, pl, ws, ql, out, lse, stream=stream)
+        if tree is not None:
+            mla.tree_attend(shape, q, kv, bt, kvl_full, ql, mask_d, case.sm_scale, out, lse,
+                            kv_scale=sc, stream=stream)
 
     for k in range(args.warmup):
         step(k)
@@ -406,8 +425,21 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_avg = sum(warm[k][0].elapsed_time(warm[k][1]) for k in range(K)) / K
 
+    tree_avg = None
+    if tree is not None:
+        tev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for k in range(K):
+            q, kv, sc, bt, kvl, ql, out, lse = sets[k % nsets]
+            tev[k][0].record(stream)
+            mla.tree_attend(shape, q, kv, bt, kvl_full, ql, mask_d, case.sm_scale, out, lse,
+                            kv_scale=sc, stream=stream)
+            tev[k][1].record(stream)
+        torch.cuda.synchronize()
+        tree_avg = sum(tev[k][0].elapsed_time(tev[k][1]) for k in range(K)) / K
+        log(f"tree merge: avg {tree_avg * 1e3:.2f} us")
+
     graph_avg = plan_dev_us = None
-    if args.graph:
+    if args.graph and tree is None:
         # one graph per input set, each capturing fwd + combine with the
         # fixed-shape plan of the same lengths (same split, all workgroups)
         plf = mla.plan(shape, case.kv_lens, case.q_lens, device=dev, fixed=True)
@@ -454,7 +486,7 @@ def main() -> int:
 
     t_step = step_avg * 1e-3
     t_fwd = fwd_avg * 1e-3
-    kv_gbs = cnt["kv_bytes"] / t_step / 1e9
+    kv_gbs = kv_total / t_step / 1e9
     tflops = cnt["flops"] / t_step / 1e12
     t_hbm = cnt["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = cnt["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
@@ -482,12 +514,15 @@ def main() -> int:
             "workload": args.workload, "batch": case.batch, "num_heads": case.num_heads,
             "d_qk": case.d_qk, "d_v": case.d_latent, "q_len_max": case.max_q_len,
             "page_size": case.page_size, "kv_dtype": case.kv_dtype,
-            "kv_tokens": cnt["kv_tokens"], "kv_len_mean": round(float(case.kv_lens.mean()), 1),
+            "kv_tokens": int(full.kv_lens.astype("int64").sum()),
+            "kv_len_mean": round(float(full.kv_lens.mean()), 1),
+            "tree_drafts": tree is not None,
         },
         "us_per_call": round(step_avg * 1e3, 2),
         "us_fwd_kernel": round(fwd_avg * 1e3, 2),
         "us_per_call_warm": round(warm_avg * 1e3, 2),
         "us_per_call_graph": None if graph_avg is None else round(graph_avg * 1e3, 2),
+        "us_tree_merge": None if tree_avg is None else round(tree_avg * 1e3, 2),
         "tflops": round(tflops, 2),
         "pct_roofline_call": round(100 * max(t_hbm, t_mfma) / t_step, 1),
         "roofline": {
@@ -509,7 +544,11 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: float64 oracle for about {args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, cnt["kv_bytes"])
+        seq_fn = None
+        if tree is not None:
+            from oracle import tree_ref
+            seq_fn = lambda b: tree_ref.mla_decode_tree_ref_seq(full, tree, b)  # noqa: E731
+        res["cpu_baseline"] = cpu_baseline(full, args.cpu_seconds, kv_total, seq_fn)
     print(json.dumps(res), flush=True)
     return 0
 

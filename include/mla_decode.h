@@ -250,6 +250,39 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info,
                        void* o, float* lse, mla_stream_t stream);
 
 /*
+ * Tree-shaped drafts: the draft tokens' part of the attention, merged into
+ * the result of a decode over the cached prefix.
+ *
+ * With EAGLE-style speculative decoding (top-k candidates per step) the
+ * q_b draft tokens of sequence b form a tree and are verified in one pass:
+ * token t sees the L_b - q_b cached prefix keys and the drafts on its branch.
+ * tree_mask [B, max_q_len] uint32 (device): bit k of word t set means token t
+ * sees draft k (cache position L_b - q_b + k); bits k >= q_b are ignored.
+ * A lower-triangular mask is the ordinary causal decode.
+ *
+ * Calling sequence for one step (all on one stream):
+ *   1. plan and run mla_decode_fwd + mla_combine over the prefix only: the
+ *      same shape with causal = 0, kv_lens_prefix[b] = kv_lens[b] - q_lens[b],
+ *      and lse not NULL;
+ *   2. mla_tree_attend with the full kv_lens: for every row (b, t < q_b, h)
+ *      it computes the scores of the visible drafts, and replaces O and LSE
+ *      (read from step 1) by the log-sum-exp merge of both parts:
+ *        LSE = ln(e^LSE_prefix + sum_k e^(s_k)),
+ *        O   = e^(LSE_prefix - LSE) O_prefix + sum_k e^(s_k - LSE) latent_k.
+ *      Rows t >= q_b are untouched; a row whose mask names no draft keeps the
+ *      prefix result.  Draft positions or pages outside the pool are skipped.
+ * The merge reads the prefix O as bf16, so the result carries one extra bf16
+ * rounding of the prefix part.
+ *
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP.
+ */
+mla_status mla_tree_attend(const mla_shape* shape, const void* q, const void* kv_cache,
+                           const float* kv_scale, const int32_t* block_table,
+                           const int32_t* kv_lens, const int32_t* q_lens,
+                           const uint32_t* tree_mask, float softmax_scale, void* o, float* lse,
+                           mla_stream_t stream);
+
+/*
  * Cache append: writes this step's new tokens into the paged cache, the
  * write that precedes the decode of every step.
  *

@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "plan_device", "decode_fwd",
-    "combine",
+    "combine", "tree_attend", "decode_tree",
     "decode", "kv_append", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
 ]
 
@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
     "mla_decode_fwd", "mla_combine", "mla_kv_append", "mla_decode_plan_fixed",
-    "mla_decode_plan_device",
+    "mla_decode_plan_device", "mla_tree_attend",
 )
 
 
@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan_fixed.argtypes = [sp, P, P, I32, P, U64, ip]
     lib.mla_decode_plan_device.restype = I32
     lib.mla_decode_plan_device.argtypes = [sp, I32, P, P, P, U64, P, ip, P]
+    lib.mla_tree_attend.restype = I32
+    lib.mla_tree_attend.argtypes = [sp, P, P, P, P, P, P, P, F32, P, P, P]
     lib.mla_decode_fwd.restype = I32
     lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
     lib.mla_combine.restype = I32
@@ -331,3 +333,48 @@ def kv_append(shape: Shape, new_rows, block_table, kv_lens, kv_cache, *, new_len
                            _ptr(new_lens), _ptr(block_table), _ptr(kv_lens), _ptr(kv_cache),
                            _ptr(kv_scale), _ptr(skipped), _stream(stream))
     _check(st, "mla_kv_append")
+
+
+def tree_attend(shape: Shape, q, kv_cache, block_table, kv_lens, q_lens, tree_mask, sm_scale: float,
+                out, lse, kv_scale=None, stream=None):
+    """Merge the tree-masked draft keys into a prefix decode's (out, lse) in
+    place (``mla_tree_attend``).  tree_mask [B, max_q_len] int32/uint32 on the
+    device: bit k of word t lets draft token t see draft k."""
+    import torch
+    lib = load_library()
+    B, qmax = shape.batch, shape.max_q_len
+    if tuple(tree_mask.shape) != (B, qmax) or tree_mask.element_size() != 4:
+        raise ValueError("tree_mask must be a [batch, max_q_len] tensor of 32-bit words")
+    if lse is None or lse.dtype != torch.float32:
+        raise ValueError("lse (the prefix decode's) is required")
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("kv_lens", kv_lens), ("tree_mask", tree_mask), ("out", out), ("lse", lse)):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous and on {q.device}")
+    st = lib.mla_tree_attend(ctypes.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(kv_scale),
+                             _ptr(block_table), _ptr(kv_lens), _ptr(q_lens), _ptr(tree_mask),
+                             float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "mla_tree_attend")
+
+
+def decode_tree(shape: Shape, q, kv_cache, block_table, kv_lens_host, q_lens_host, kv_lens,
+                q_lens, tree_mask, sm_scale: float, *, kv_scale=None, num_workgroups=None,
+                stream=None):
+    """Decode with tree-shaped drafts: a non-causal decode over the cached
+    prefix (kv_len - q_len keys), then ``tree_attend``.  Host lengths plan the
+    prefix decode; kv_lens / q_lens are their device copies (full kv_lens)."""
+    import torch
+    kv_h = np.asarray(kv_lens_host, np.int32)
+    ql_h = np.asarray(q_lens_host, np.int32)
+    prefix_h = (kv_h - ql_h).astype(np.int32)
+    pshape = Shape.make(batch=shape.batch, num_heads=shape.num_heads, max_q_len=shape.max_q_len,
+                        page_size=shape.page_size, num_pages=shape.num_pages,
+                        max_pages_per_seq=shape.max_pages_per_seq, kv_dtype=shape.kv_dtype,
+                        causal=False)
+    pl = plan(pshape, prefix_h, ql_h, num_workgroups=num_workgroups, device=q.device)
+    prefix = torch.from_numpy(prefix_h).to(q.device)
+    out, lse = decode(pshape, pl, q, kv_cache, block_table, prefix, q_lens, sm_scale,
+                      kv_scale=kv_scale, stream=stream)
+    tree_attend(shape, q, kv_cache, block_table, kv_lens, q_lens, tree_mask, sm_scale, out, lse,
+                kv_scale=kv_scale, stream=stream)
+    return out, lse

@@ -11,6 +11,7 @@
 #include "mla_decode.h"
 #include "plan_device.h"
 #include "plan_layout.h"
+#include "tree.h"
 #include "validate.h"
 
 using namespace mla;
@@ -248,6 +249,44 @@ mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const v
   return launch_append(a, shape->kv_dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
+}
+
+mla_status mla_tree_attend(const mla_shape* shape, const void* q, const void* kv_cache,
+                           const float* kv_scale, const int32_t* block_table,
+                           const int32_t* kv_lens, const int32_t* q_lens,
+                           const uint32_t* tree_mask, float softmax_scale, void* o, float* lse,
+                           mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  if (shape->batch == 0) return MLA_OK;
+  if (!q || !kv_cache || !block_table || !kv_lens || !tree_mask || !o || !lse)
+    return MLA_ERR_NULL_ARG;
+  if (shape->kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale) return MLA_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(tree_mask) & 3u) ||
+      (kv_scale && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)))
+    return MLA_ERR_MISALIGNED;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+  TreeArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.q_lens = q_lens;
+  a.tree_mask = tree_mask;
+  a.o = static_cast<uint8_t*>(o);
+  a.lse = lse;
+  a.sm_scale = softmax_scale;
+  a.batch = shape->batch;
+  a.num_heads = shape->num_heads;
+  a.max_q_len = shape->max_q_len;
+  a.page_shift = ilog2(shape->page_size);
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.kv_dtype = shape->kv_dtype;
+  return launch_tree(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
+                                                                             : MLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -57,4 +57,4 @@ from .append_ref import (  # noqa: F401
     kv_append_ref,
     quantize_rows_e4m3,
 )
-from .tree_ref import mla_decode_tree_ref, tree_visible_keys  # noqa: F401
+from .tree_ref import mla_decode_tree_ref, mla_decode_tree_ref_seq, tree_visible_keys  # noqa: F401

@@ -37,6 +37,20 @@ def tree_visible_keys(kv_len: int, q_len: int, mask_word: int) -> np.ndarray:
     return np.array(list(range(max(prefix, 0))) + drafts, dtype=np.int64)
 
 
+def mla_decode_tree_ref_seq(case, tree_mask, b: int):
+    """One sequence b: (O [q_b, H, Dv], LSE [q_b, H])."""
+    L, qb = int(case.kv_lens[b]), int(case.q_lens[b])
+    Dv = case.d_latent
+    K = gather_latent(case.kv, case.block_table[b], L, case.page_size, case.kv_dtype,
+                      case.kv_scale)
+    O = np.zeros((qb, case.num_heads, Dv))
+    LSE = np.zeros((qb, case.num_heads))
+    for t in range(qb):
+        vis = tree_visible_keys(L, qb, int(tree_mask[b][t]))
+        O[t], LSE[t] = attend_rows(_q_f64(case.q[b, t]), K[vis], K[vis, :Dv], case.sm_scale)
+    return O, LSE
+
+
 def mla_decode_tree_ref(case, tree_mask, seqs=None):
     """O [B, q_max, H, Dv] and LSE [B, q_max, H] for tree-masked drafts;
     tree_mask [B, q_max] uint32.  Rows not computed are NaN."""
@@ -45,13 +59,8 @@ def mla_decode_tree_ref(case, tree_mask, seqs=None):
     LSE = np.full((B, qmax, H), np.nan)
     mask = np.asarray(tree_mask, dtype=np.uint32)
     for b in (range(B) if seqs is None else seqs):
-        L, qb = int(case.kv_lens[b]), int(case.q_lens[b])
+        qb = int(case.q_lens[b])
         if qb == 0:
             continue
-        K = gather_latent(case.kv, case.block_table[b], L, case.page_size, case.kv_dtype,
-                          case.kv_scale)
-        for t in range(qb):
-            vis = tree_visible_keys(L, qb, int(mask[b, t]))
-            O[b, t], LSE[b, t] = attend_rows(_q_f64(case.q[b, t]), K[vis], K[vis, :Dv],
-                                             case.sm_scale)
+        O[b, :qb], LSE[b, :qb] = mla_decode_tree_ref_seq(case, mask, b)
     return O, LSE

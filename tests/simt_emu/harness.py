@@ -11,6 +11,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 BIN = os.path.join(HERE, "_build", "run_case")
 MAGIC = 0x4D4C4145
+TREE_MAGIC = 0x4D4C4154
 APPEND_MAGIC = 0x4D4C4141
 
 
@@ -31,12 +32,15 @@ def _stale() -> bool:
 
 
 def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
-        env_extra: dict | None = None, binary: str | None = None, fixed: bool = False):
+        env_extra: dict | None = None, binary: str | None = None, fixed: bool = False,
+        tree_mask=None):
     """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta).
-    ``fixed`` plans with mla_decode_plan_fixed (launch bounds, padded plan)."""
+    ``fixed`` plans with mla_decode_plan_fixed (launch bounds, padded plan);
+    ``tree_mask`` [B, qmax] runs the tree-draft path (prefix decode + merge)."""
     B, H, qmax = case.batch, case.num_heads, case.max_q_len
     kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
-    hdr = np.array([MAGIC, B, H, qmax, case.page_size, case.num_pages, case.max_pages, kv_dtype,
+    magic = MAGIC if tree_mask is None else TREE_MAGIC
+    hdr = np.array([magic, B, H, qmax, case.page_size, case.num_pages, case.max_pages, kv_dtype,
                     int(case.causal), num_workgroups, 1, int(fixed)], dtype=np.int32)
     with tempfile.TemporaryDirectory() as d:
         fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
@@ -50,6 +54,8 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
             f.write(np.ascontiguousarray(case.block_table, dtype=np.int32).tobytes())
             f.write(np.ascontiguousarray(case.kv_lens, dtype=np.int32).tobytes())
             f.write(np.ascontiguousarray(case.q_lens, dtype=np.int32).tobytes())
+            if tree_mask is not None:
+                f.write(np.ascontiguousarray(tree_mask, dtype=np.uint32).tobytes())
         env = dict(os.environ)
         env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
         if phases is not None:

@@ -13,6 +13,11 @@
 //   out.bin: int32 {num_items, num_partials, num_combine, phases}, then O
 //            (B*qmax*H*512 bf16) and LSE (B*qmax*H fp32)
 //
+// A tree-draft case has its own magic and the decode layout, followed by the
+// tree mask words (B*qmax uint32): the prefix (kv_len - q_len keys) goes
+// through plan + mla_decode_fwd + mla_combine, non-causal, and
+// mla_tree_attend merges the drafts; the output is as for a decode case.
+//
 // A device-planner case (mla_decode_plan_device) has its own magic:
 //   in.bin : int32 header[12] = {magic, B, H, qmax, page_size, num_pages,
 //            max_pages, causal, num_workgroups, has_q_lens, 0, 0}, then
@@ -161,7 +166,8 @@ int main(int argc, char** argv) {
   if (hd[0] == 0x4d4c4141) return run_append(f, hd, argv[2]);
   if (hd[0] == 0x4d4c4150) return run_plan(f, hd, argv[2]);
   read_into(f, &scale, sizeof scale);
-  if (hd[0] != 0x4d4c4145) die("bad magic");
+  const bool tree = hd[0] == 0x4d4c4154;
+  if (hd[0] != 0x4d4c4145 && !tree) die("bad magic");
   mla_shape s{};
   s.batch = hd[1];
   s.num_heads = hd[2];
@@ -193,6 +199,18 @@ int main(int argc, char** argv) {
   read_into(f, bt, size_t(s.batch) * s.max_pages_per_seq * 4);
   read_into(f, kvl, size_t(s.batch) * 4);
   if (ql) read_into(f, ql, size_t(s.batch) * 4);
+  uint32_t* mask = nullptr;
+  int32_t* full_kvl = nullptr;
+  if (tree) {
+    if (!ql) die("a tree case needs q_lens");
+    mask = static_cast<uint32_t*>(exact_alloc(size_t(s.batch) * s.max_q_len * 4, 4));
+    read_into(f, mask, size_t(s.batch) * s.max_q_len * 4);
+    // the decode runs over the prefix: kv_len - q_len keys, non-causal
+    full_kvl = kvl;
+    kvl = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * 4, 4));
+    for (int b = 0; b < s.batch; ++b) kvl[b] = full_kvl[b] - ql[b];
+    s.causal = 0;
+  }
   std::fclose(f);
 
   const uint64_t bound = mla_plan_bytes_bound(&s, nwg);
@@ -220,6 +238,10 @@ int main(int argc, char** argv) {
   if (st != MLA_OK) die("mla_decode_fwd failed");
   st = mla_combine(&s, &info, plan, ws, info.workspace_bytes, ql, o, lse, nullptr);
   if (st != MLA_OK) die("mla_combine failed");
+  if (tree) {
+    st = mla_tree_attend(&s, q, kv, ksc, bt, full_kvl, ql, mask, scale, o, lse, nullptr);
+    if (st != MLA_OK) die("mla_tree_attend failed");
+  }
 
   FILE* g = std::fopen(argv[2], "wb");
   if (!g) die("cannot open output");
@@ -233,6 +255,8 @@ int main(int argc, char** argv) {
   std::free(ksc);
   std::free(bt);
   std::free(kvl);
+  std::free(full_kvl);
+  std::free(mask);
   std::free(ql);
   std::free(plan);
   std::free(ws);

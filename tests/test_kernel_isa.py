@@ -204,16 +204,20 @@ def test_append_kernel_machine_code(append_isa):
     assert sum(i.startswith("v_div_fixup_f32") for i in fp8) >= 17
 
 
-def test_device_planner_machine_code(tmp_path):
-    out = tmp_path / "plan_kernel.s"
+@pytest.mark.parametrize("src,kernel", [("plan_kernel.hip", "mla_plan_kernel"),
+                                        ("tree_kernel.hip", "mla_tree_kernel")])
+def test_small_kernels_machine_code(tmp_path, src, kernel):
+    # the device planner and the tree-draft merge: no scratch, no scalar
+    # stores, LDS within the 160 KB a workgroup may use
+    out = tmp_path / "k.s"
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument", os.path.join(CSRC, "plan_kernel.hip"), "-o", str(out)]
+           "-Wno-unused-command-line-argument", os.path.join(CSRC, src), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
     text = out.read_text()
-    body = text[text.index("mla_plan_kernel"):]
+    body = text[text.index(kernel):]
     ins = [l.split(";")[0].strip() for l in body.splitlines()]
     assert not [i for i in ins if i.startswith("scratch_")]
     assert not [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)]

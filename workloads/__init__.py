@@ -185,6 +185,7 @@ WORKLOADS = {
     "mtp_verify_bf16": (3, "B 128, H 128, kv U[512,8192], q 2 causal, P 64, bf16"),
     "long_ctx_fp8": (4, "B 16, H 128, kv U[16384,32768], q 1, P 64, e4m3 KV + fp32 per-token scale"),
     "ragged_serving_bf16": (5, "256 seqs, log-normal kv (mean 2790, clip [64,32768]), half q 1 / half q 2, P 64, bf16"),
+    "tree_verify_bf16": (6, "B 128, H 128, kv U[512,8192], 4 tree-shaped drafts (random branches), P 64, bf16"),
 }
 
 
@@ -225,4 +226,43 @@ def workload(name: str, *, batch_override: Optional[int] = None) -> MLACase:
         q_lens[two] = 2
         return make_case(name=name, kv_lens=kv_lens, q_lens=q_lens, sm_scale=sm192,
                          rng=rng, seed=seed, causal=True)
+    if name == "tree_verify_bf16":
+        # EAGLE-style drafts: 4 draft tokens per sequence on random branches
+        B = batch_override or 128
+        kv_lens = rng.integers(512, 8192, size=B, endpoint=True).astype(np.int32)
+        q_lens = np.full(B, 4, np.int32)
+        case = make_case(name=name, kv_lens=kv_lens, q_lens=q_lens, sm_scale=sm192,
+                         rng=rng, seed=seed, causal=True)
+        case.meta["tree_mask"] = tree_masks(q_lens, 4, "branch", seed=seed)
+        return case
     raise KeyError(name)
+
+
+def tree_masks(q_lens, max_q_len, kind, seed=0):
+    """[B, max_q_len] uint32 mask words.  kind: causal (each token sees the
+    drafts up to itself), diag (itself only), none (no draft), branch (token t
+    sees itself and a random chain of earlier drafts: a random tree), random
+    (any subset of the drafts, the token itself not always included)."""
+    rng = np.random.default_rng(seed)
+    B = len(q_lens)
+    m = np.zeros((B, max_q_len), np.uint32)
+    for b in range(B):
+        q = int(q_lens[b])
+        parent = [-1] * q
+        for t in range(q):
+            if kind == "causal":
+                m[b, t] = (1 << (t + 1)) - 1
+            elif kind == "diag":
+                m[b, t] = 1 << t
+            elif kind == "none":
+                m[b, t] = 0
+            elif kind == "branch":
+                parent[t] = int(rng.integers(-1, t)) if t > 0 else -1
+                word, p = 1 << t, parent[t]
+                while p >= 0:
+                    word |= 1 << p
+                    p = parent[p]
+                m[b, t] = word
+            elif kind == "random":
+                m[b, t] = int(rng.integers(0, 1 << q))
+    return m
