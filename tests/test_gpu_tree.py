@@ -72,6 +72,15 @@ def test_tree_dtypes_and_heads(dtype, H):
     check_tree(case, mask, out, lse)
 
 
+@pytest.mark.parametrize("H,qmax", [(20, 4), (8, 3), (128, 8)])
+def test_tree_head_groups(H, qmax):
+    case = make_case(kv_lens=[90, 3, 400, 5000], q_lens=[qmax, 3, 2, qmax], seed=64, num_heads=H,
+                     sm_scale=1 / math.sqrt(192), max_q_len=qmax)
+    mask = tree_masks(case.q_lens, case.max_q_len, "random", seed=7)
+    out, lse = run_tree(case, mask)
+    check_tree(case, mask, out, lse)
+
+
 def test_causal_mask_matches_the_causal_decode():
     case = make_case(kv_lens=[700, 130, 2000], q_lens=[4, 2, 3], seed=63,
                      sm_scale=1 / math.sqrt(192), max_q_len=4)

@@ -62,3 +62,14 @@ def test_tree_full_heads_and_e4m3():
         mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=3)
         out, lse, _ = harness.run(case, 8, 1, tree_mask=mask)
         check_tree(case, mask, out, lse)
+
+
+@pytest.mark.parametrize("H,qmax", [(20, 4), (8, 3)])
+def test_tree_partial_head_groups(H, qmax):
+    # 20 heads: a second head group with one busy wave (24 workgroups, dealt
+    # to XCDs); 8 heads, 3 tokens: a grid of 9, taken in plain order
+    case = make_case(kv_lens=[90, 3, 400], q_lens=[qmax, 3, 2], seed=54, num_heads=H,
+                     page_size=16, sm_scale=1 / math.sqrt(192), max_q_len=qmax)
+    mask = tree_masks(case.q_lens, case.max_q_len, "random", seed=6)
+    out, lse, _ = harness.run(case, 5, 1, tree_mask=mask)
+    check_tree(case, mask, out, lse)
