@@ -153,7 +153,8 @@ def test_bf16_mixed_q_lens_and_empty_sequence(phases):
 
 
 @pytest.mark.parametrize("phases", [1, 4])
-@pytest.mark.parametrize("H,q", [(16, 1), (16, 2), (64, 2), (32, 4), (128, 4)])
+@pytest.mark.parametrize("H,q", [(16, 1), (16, 2), (64, 2), (128, 3), (32, 4), (128, 4),
+                                 (128, 5)])
 def test_head_counts_and_longer_drafts(H, q, phases):
     case = make_case(kv_lens=[97, 640, 4], q_lens=[q, q, q], num_heads=H, seed=14,
                      sm_scale=1 / math.sqrt(192))
