@@ -33,10 +33,14 @@ What it computes, and where the pages state it:
 * Tree-shaped drafts: each draft token sees the cached prefix and the drafts
   its mask names (``tree_ref``; EAGLE-style drafts of the Dewu deployment
   slides, verified in one pass as on the PaddlePaddle 3.0 page).
+* SageAttention-style quantized causal prefill: INT8 Q and K, FP8 V and P,
+  blocked online softmax (``prefill_ref``; PaddlePaddle 3.0 page, the
+  long-sequence SageAttention paragraph).
 
 Every function below is pinned by ``tests/test_oracle_pins.py`` (the
 append by ``tests/test_oracle_append_pins.py``, the tree drafts by
-``tests/test_oracle_tree_pins.py``) against something other than
+``tests/test_oracle_tree_pins.py``, the prefill by
+``tests/test_oracle_prefill_pins.py``) against something other than
 itself (closed forms, the non-absorbed identity, brute force, library casts,
 invariants); see each docstring.
 """
@@ -58,3 +62,6 @@ from .append_ref import (  # noqa: F401
     quantize_rows_e4m3,
 )
 from .tree_ref import mla_decode_tree_ref, mla_decode_tree_ref_seq, tree_visible_keys  # noqa: F401
+from .prefill_ref import (  # noqa: F401
+    quantize_case, quantize_p, quantize_rows_int8, quantize_v_blocks, sage_prefill_ref,
+)
