@@ -327,6 +327,85 @@ mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const v
                          const int32_t* kv_lens, void* kv_cache, float* kv_scale,
                          int32_t* skipped, mla_stream_t stream);
 
+/*
+ * Quantized causal prefill, SageAttention style (PaddlePaddle 3.0 inference
+ * page, long-sequence inference: Q and K quantized to INT8 and V to FP8 on the
+ * fly, the INT32 products converted to FP32 and dequantized, an online softmax,
+ * P quantized to FP8 and multiplied with the FP8 V, V's scale taken off
+ * afterwards; head dim 192 for Q and K, 128 for V, as in DeepSeek's prefill).
+ *
+ * Sequences are packed along the token axis: sequence s owns tokens
+ * cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (N_s of them), and token i of a
+ * sequence sees keys 0..i of the same sequence.  For each (token, head):
+ *
+ *   s_j = (qc . kc_j) * q_scale * k_scale_j * softmax_scale     (INT32 exact)
+ *   keys taken in blocks of 128 from the sequence start; per block
+ *     m' = max(m, max s_j),  a = e^(m - m'),  P_j = e^(s_j - m'),
+ *     l = a l + sum_j P_j,   acc = a acc + sum_j e4m3(448 P_j) * vc_j * v_scale(block)
+ *   O = acc / (448 l)  (bf16, round to nearest even),  LSE = m + ln l (fp32)
+ *
+ * Calling sequence: mla_prefill_quantize, then mla_prefill_attn, on one
+ * stream.  Blocks: a sequence has ceil(N_s / 128) 128-token blocks; they are
+ * numbered over all sequences in order (num_blocks in total, see
+ * mla_prefill_num_blocks).
+ */
+typedef struct mla_prefill_shape {
+  int32_t num_seqs;    /* S >= 0 */
+  int32_t num_tokens;  /* T = cu_seqlens[S] */
+  int32_t num_heads;   /* H >= 1 */
+  int32_t d_qk;        /* 192 */
+  int32_t d_v;         /* 128 */
+  int32_t num_blocks;  /* sum_s ceil(N_s / 128) */
+} mla_prefill_shape;
+
+/* Number of 128-token blocks of S sequences with host lengths seqlens[S]
+ * (>= 0); -1 if a length is negative or the sum overflows int32. */
+int32_t mla_prefill_num_blocks(const int32_t* seqlens, int32_t num_seqs);
+
+/*
+ * Quantizes packed bf16 Q, K, V (all device pointers, 16-byte aligned).
+ *
+ *   cu_seqlens  [S + 1] int32, device: 0 = cu[0] <= cu[1] <= ... <= cu[S] = T.
+ *   q, k        [T, H, 192] bf16;  v  [T, H, 128] bf16.  Values must be finite.
+ *   q_codes, k_codes  [T, H, 192] int8: code = RNE(x / s) clamped to +-127,
+ *               with one scale per (token, head) row s = max|x| / 127 in fp32
+ *               (1 for an all-zero row), written to q_scale / k_scale [T, H] fp32.
+ *   v_codes     [num_blocks, H, 128 channels, 128 keys] e4m3 bytes: for block
+ *               b of a sequence and channel c, code = the e4m3 value nearest
+ *               (ties to even) to v / s with s = max|v| / 448 over the block's
+ *               tokens in channel c (1 if zero), written to
+ *               v_scale [num_blocks, H, 128] fp32.  Within a (block, head,
+ *               channel) row of 128 bytes, key k = 16 a + 4 g + r
+ *               (a < 8, g < 4, r < 4) sits at byte 32 g + 4 a + r: the order
+ *               in which the PV matrix instruction takes them.  Keys past
+ *               the sequence's end hold code 0.
+ *
+ * Quotients are correctly rounded fp32 divisions.  Errors: NULL_ARG,
+ * BAD_SHAPE (negative sizes, d_qk != 192 or d_v != 128 is UNSUPPORTED),
+ * MISALIGNED, HIP.  Blocks of a sequence whose cu_seqlens entries are out of
+ * order or past T, or past num_blocks, are not written.  T = 0 is a no-op.
+ */
+mla_status mla_prefill_quantize(const mla_prefill_shape* shape, const int32_t* cu_seqlens,
+                                const void* q, const void* k, const void* v, int8_t* q_codes,
+                                float* q_scale, int8_t* k_codes, float* k_scale,
+                                uint8_t* v_codes, float* v_scale, mla_stream_t stream);
+
+/*
+ * The attention of the formula above, from mla_prefill_quantize's outputs.
+ *
+ *   o    [T, H, 128] bf16 (device, 16-byte aligned); lse [T, H] fp32 (device).
+ *   softmax_scale  finite.
+ *
+ * One workgroup per (128-token block, head); the P V product runs on e4m3
+ * matrix instructions and the Q K product on INT8 ones.  Errors as for
+ * mla_prefill_quantize; rows of sequences with inconsistent cu_seqlens are
+ * not written.
+ */
+mla_status mla_prefill_attn(const mla_prefill_shape* shape, const int32_t* cu_seqlens,
+                            const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                            const float* k_scale, const uint8_t* v_codes, const float* v_scale,
+                            float softmax_scale, void* o, float* lse, mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

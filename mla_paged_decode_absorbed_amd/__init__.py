@@ -39,8 +39,12 @@ EXPORTED_SYMBOLS = (
     "mla_abi_version", "mla_status_string", "mla_plan_bytes_bound",
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
     "mla_decode_fwd", "mla_combine", "mla_kv_append", "mla_decode_plan_fixed",
-    "mla_decode_plan_device", "mla_tree_attend",
+    "mla_decode_plan_device", "mla_tree_attend", "mla_prefill_num_blocks",
+    "mla_prefill_quantize", "mla_prefill_attn",
 )
+PREFILL_D_QK = 192
+PREFILL_D_V = 128
+PREFILL_BLOCK = 128
 
 
 class MLAError(RuntimeError):
@@ -62,6 +66,25 @@ class Shape(ctypes.Structure):
              kv_dtype=KV_BF16, causal=True, d_latent=D_LATENT, d_rope=D_ROPE) -> "Shape":
         return cls(batch, num_heads, max_q_len, d_latent, d_rope, page_size, num_pages,
                    max_pages_per_seq, kv_dtype, int(bool(causal)))
+
+
+class PrefillShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, seqlens, num_heads: int) -> "PrefillShape":
+        """From host sequence lengths (the block count comes from the library)."""
+        lens = np.ascontiguousarray(seqlens, dtype=np.int32)
+        nb = load_library().mla_prefill_num_blocks(
+            lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(lens.size))
+        if nb < 0:
+            raise ValueError("bad sequence lengths")
+        return cls(int(lens.size), int(lens.sum()), int(num_heads), PREFILL_D_QK, PREFILL_D_V,
+                   int(nb))
 
 
 class PlanInfo(ctypes.Structure):
@@ -111,6 +134,13 @@ def load_library(path: str = LIB_PATH):
     lib.mla_combine.argtypes = [sp, ip, P, P, U64, P, P, P, P]
     lib.mla_kv_append.restype = I32
     lib.mla_kv_append.argtypes = [sp, I32, P, P, P, P, P, P, P, P]
+    pp = ctypes.POINTER(PrefillShape)
+    lib.mla_prefill_num_blocks.restype = I32
+    lib.mla_prefill_num_blocks.argtypes = [ctypes.POINTER(ctypes.c_int32), I32]
+    lib.mla_prefill_quantize.restype = I32
+    lib.mla_prefill_quantize.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, P]
+    lib.mla_prefill_attn.restype = I32
+    lib.mla_prefill_attn.argtypes = [pp, P, P, P, P, P, P, P, F32, P, P, P]
     _lib = lib
     return lib
 
@@ -378,3 +408,78 @@ def decode_tree(shape: Shape, q, kv_cache, block_table, kv_lens_host, q_lens_hos
     tree_attend(shape, q, kv_cache, block_table, kv_lens, q_lens, tree_mask, sm_scale, out, lse,
                 kv_scale=kv_scale, stream=stream)
     return out, lse
+
+
+# ------------------------------------------------------------- quantized prefill
+
+@dataclass
+class PrefillQuant:
+    """mla_prefill_quantize's outputs (torch device tensors)."""
+    q_codes: object       # [T, H, 192] int8
+    q_scale: object       # [T, H] fp32
+    k_codes: object
+    k_scale: object
+    v_codes: object       # [blocks, H, 128, 128] uint8 (e4m3, PV operand key order)
+    v_scale: object       # [blocks, H, 128] fp32
+
+
+def prefill_alloc_quant(shape: PrefillShape, device) -> PrefillQuant:
+    import torch
+    T, H, nb = shape.num_tokens, shape.num_heads, shape.num_blocks
+    return PrefillQuant(
+        q_codes=torch.empty((T, H, PREFILL_D_QK), dtype=torch.int8, device=device),
+        q_scale=torch.empty((T, H), dtype=torch.float32, device=device),
+        k_codes=torch.empty((T, H, PREFILL_D_QK), dtype=torch.int8, device=device),
+        k_scale=torch.empty((T, H), dtype=torch.float32, device=device),
+        v_codes=torch.empty((nb, H, PREFILL_D_V, PREFILL_BLOCK), dtype=torch.uint8, device=device),
+        v_scale=torch.empty((nb, H, PREFILL_D_V), dtype=torch.float32, device=device))
+
+
+def _prefill_tensors_ok(dev, named):
+    for name, t in named:
+        if t is None or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+
+
+def prefill_quantize(shape: PrefillShape, cu_seqlens, q, k, v, quant: PrefillQuant = None,
+                     stream=None) -> PrefillQuant:
+    """``mla_prefill_quantize``: packed bf16 q, k [T, H, 192] and v [T, H, 128]
+    to INT8 / e4m3 codes and scales; cu_seqlens [S + 1] int32 on the device."""
+    lib = load_library()
+    quant = prefill_alloc_quant(shape, q.device) if quant is None else quant
+    _prefill_tensors_ok(q.device, [("cu_seqlens", cu_seqlens), ("q", q), ("k", k), ("v", v),
+                                   ("q_codes", quant.q_codes), ("k_codes", quant.k_codes),
+                                   ("v_codes", quant.v_codes)])
+    st = lib.mla_prefill_quantize(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(quant.q_codes), _ptr(quant.q_scale), _ptr(quant.k_codes),
+                                  _ptr(quant.k_scale), _ptr(quant.v_codes), _ptr(quant.v_scale),
+                                  _stream(stream))
+    _check(st, "mla_prefill_quantize")
+    return quant
+
+
+def prefill_attn(shape: PrefillShape, cu_seqlens, quant: PrefillQuant, sm_scale: float, out=None,
+                 lse=None, stream=None):
+    """``mla_prefill_attn``: causal attention from the quantized inputs.
+    Returns (O [T, H, 128] bf16, LSE [T, H] fp32)."""
+    import torch
+    lib = load_library()
+    dev = quant.q_codes.device
+    T, H = shape.num_tokens, shape.num_heads
+    if out is None:
+        out = torch.empty((T, H, PREFILL_D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _prefill_tensors_ok(dev, [("cu_seqlens", cu_seqlens), ("out", out), ("lse", lse)])
+    st = lib.mla_prefill_attn(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(quant.q_codes),
+                              _ptr(quant.q_scale), _ptr(quant.k_codes), _ptr(quant.k_scale),
+                              _ptr(quant.v_codes), _ptr(quant.v_scale), float(sm_scale), _ptr(out),
+                              _ptr(lse), _stream(stream))
+    _check(st, "mla_prefill_attn")
+    return out, lse
+
+
+def prefill(shape: PrefillShape, cu_seqlens, q, k, v, sm_scale: float, stream=None):
+    """Quantize, then attend: the whole SageAttention-style prefill."""
+    quant = prefill_quantize(shape, cu_seqlens, q, k, v, stream=stream)
+    return prefill_attn(shape, cu_seqlens, quant, sm_scale, stream=stream)

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "plan.cpp", "decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
-           "plan_kernel.hip", "tree_kernel.hip"]
+           "plan_kernel.hip", "tree_kernel.hip", "prefill_quant_kernel.hip",
+           "prefill_attn_kernel.hip"]
 ARCH = "gfx950"
 
 

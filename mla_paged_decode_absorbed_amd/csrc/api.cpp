@@ -11,6 +11,7 @@
 #include "mla_decode.h"
 #include "plan_device.h"
 #include "plan_layout.h"
+#include "prefill.h"
 #include "tree.h"
 #include "validate.h"
 
@@ -287,6 +288,103 @@ mla_status mla_tree_attend(const mla_shape* shape, const void* q, const void* kv
   a.kv_dtype = shape->kv_dtype;
   return launch_tree(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
                                                                              : MLA_ERR_HIP;
+}
+
+// Shape checks shared by the two prefill entry points.
+static mla_status validate_prefill(const mla_prefill_shape* s) {
+  if (!s) return MLA_ERR_NULL_ARG;
+  if (s->num_seqs < 0 || s->num_tokens < 0 || s->num_heads < 1 || s->num_blocks < 0)
+    return MLA_ERR_BAD_SHAPE;
+  if (s->d_qk != kPfDQK || s->d_v != kPfDV) return MLA_ERR_UNSUPPORTED;
+  // a sequence holds at least one token per block it counts, and the packed
+  // row and block indices stay in 32 bits inside the kernels
+  if (int64_t(s->num_blocks) > int64_t(s->num_tokens) ||
+      int64_t(s->num_tokens) * s->num_heads >= (int64_t(1) << 31) ||
+      int64_t(s->num_blocks) * s->num_heads >= (int64_t(1) << 31))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int32_t mla_prefill_num_blocks(const int32_t* seqlens, int32_t num_seqs) {
+  if (num_seqs < 0 || (num_seqs > 0 && !seqlens)) return -1;
+  int64_t n = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (seqlens[s] < 0) return -1;
+    n += (int64_t(seqlens[s]) + kPfBlock - 1) / kPfBlock;
+    if (n > INT32_MAX) return -1;
+  }
+  return int32_t(n);
+}
+
+mla_status mla_prefill_quantize(const mla_prefill_shape* shape, const int32_t* cu_seqlens,
+                                const void* q, const void* k, const void* v, int8_t* q_codes,
+                                float* q_scale, int8_t* k_codes, float* k_scale,
+                                uint8_t* v_codes, float* v_scale, mla_stream_t stream) {
+  mla_status st = validate_prefill(shape);
+  if (st != MLA_OK) return st;
+  if (shape->num_tokens == 0) return MLA_OK;
+  if (!cu_seqlens || !q || !k || !v || !q_codes || !q_scale || !k_codes || !k_scale ||
+      (shape->num_blocks > 0 && (!v_codes || !v_scale)))
+    return MLA_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_codes) ||
+      !aligned16(k_codes) || (v_codes && !aligned16(v_codes)) ||
+      ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+        reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(cu_seqlens)) & 3u))
+    return MLA_ERR_MISALIGNED;
+  PrefillQuantArgs a{};
+  a.cu = cu_seqlens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.qc = q_codes;
+  a.qs = q_scale;
+  a.kc = k_codes;
+  a.ks = k_scale;
+  a.vc = v_codes;
+  a.vs = v_scale;
+  a.num_seqs = shape->num_seqs;
+  a.num_tokens = shape->num_tokens;
+  a.num_heads = shape->num_heads;
+  a.num_blocks = shape->num_blocks;
+  return launch_prefill_quant(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status mla_prefill_attn(const mla_prefill_shape* shape, const int32_t* cu_seqlens,
+                            const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                            const float* k_scale, const uint8_t* v_codes, const float* v_scale,
+                            float softmax_scale, void* o, float* lse, mla_stream_t stream) {
+  mla_status st = validate_prefill(shape);
+  if (st != MLA_OK) return st;
+  if (shape->num_tokens == 0 || shape->num_blocks == 0) return MLA_OK;
+  if (!cu_seqlens || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale ||
+      !o || !lse)
+    return MLA_ERR_NULL_ARG;
+  if (!aligned16(q_codes) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o) ||
+      ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+        reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(lse) |
+        reinterpret_cast<uintptr_t>(cu_seqlens)) & 3u))
+    return MLA_ERR_MISALIGNED;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+  PrefillAttnArgs a{};
+  a.cu = cu_seqlens;
+  a.qc = q_codes;
+  a.qs = q_scale;
+  a.kc = k_codes;
+  a.ks = k_scale;
+  a.vc = v_codes;
+  a.vs = v_scale;
+  a.o = static_cast<uint8_t*>(o);
+  a.lse = lse;
+  a.sm_scale = softmax_scale;
+  a.num_seqs = shape->num_seqs;
+  a.num_tokens = shape->num_tokens;
+  a.num_heads = shape->num_heads;
+  a.num_blocks = shape->num_blocks;
+  return launch_prefill_attn(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
 }
 
 }  // extern "C"

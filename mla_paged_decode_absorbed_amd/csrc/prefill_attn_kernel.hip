@@ -1,0 +1,220 @@
+// SageAttention-style causal prefill attention (PaddlePaddle 3.0 inference
+// page, long-sequence inference): INT8 Q K^T on the INT8 matrix cores, the
+// INT32 scores dequantized in fp32, an online softmax, P quantized to e4m3
+// and multiplied with the e4m3 V on the fp8 matrix cores, V's per-channel
+// scale taken off each block's product.
+//
+// A workgroup takes one 128-token query block of one head; each of its 4
+// waves 32 queries (two 16-query tiles).  Key blocks of 128 (the same blocks
+// that carry V's scales) are staged in LDS in turn, up to the diagonal:
+//
+//  * scores: S^T[16 keys x 16 queries] = K Q^T on v_mfma_i32_16x16x64_i8,
+//    3 steps over the 192 dims; Q's operands stay in registers.  In the
+//    output, lane l holds keys 4 (l / 16) + r of query l % 16;
+//  * s = S * q_scale * k_scale * softmax_scale (in log2 units), -inf for keys
+//    after the query or past the sequence; the row max takes two lane swaps
+//    (the 4 lanes of a query), the running max, sum and accumulator are
+//    rescaled by 2^(m_old - m_new);
+//  * P = 2^(s - m) times 448 goes to e4m3 (hardware conversion, nearest
+//    even): the 8 score tiles of a lane are exactly the 32 keys
+//    16 a + 4 g + r the lane feeds to the PV instruction, so P never moves;
+//  * O^T[16 channels x 16 queries] += V^T P^T on
+//    v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), V^T read from LDS in
+//    the key order mla_prefill_quantize wrote, then times the channel scales
+//    of the block.
+//
+// The workgroups of the last (most expensive) query blocks start first, and
+// consecutive workgroups are consecutive heads, so with H a multiple of 8
+// every query block of a head runs on one XCD, whose L2 then holds that
+// head's keys and values.  O = acc / (448 l), LSE = m ln 2 + ln l.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "prefill.h"
+
+namespace mla {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKStride = 208;                 // LDS bytes per key row (192 + 16)
+constexpr int kVStride = 144;                 // LDS bytes per channel row (128 + 16)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kPScale = 448.f;
+constexpr int kE8M0One = 127;                 // unit block scale of the fp8 instruction
+
+__global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) int8_t ktile[kPfBlock * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[kPfDV * kVStride];
+  __shared__ __attribute__((aligned(16))) float kscale[kPfBlock];
+  __shared__ __attribute__((aligned(16))) float vscale[kPfDV];
+  const int H = a.num_heads;
+  const int wi = int(blockIdx.x) / H;
+  const int h = int(blockIdx.x) - wi * H;
+  const int i = a.num_blocks - 1 - wi;          // the last blocks carry the most keys
+  PfBlock blk;
+  if (!pf_find_block(a.cu, a.num_seqs, a.num_tokens, a.num_blocks, i, &blk)) return;
+  const int qb = blk.kb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+
+  // this lane's two queries (one per 16-query tile) and their Q operands
+  int qi[2];
+  float qsc[2];
+  i32x4 qop[2][3];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    qi[u] = qb * kPfBlock + wave * 32 + u * 16 + col;
+    qsc[u] = 0.f;
+#pragma unroll
+    for (int sg = 0; sg < 3; ++sg) qop[u][sg] = i32x4{0, 0, 0, 0};
+    if (qi[u] < blk.n) {
+      const int64_t row = int64_t(blk.t0 + qi[u]) * H + h;
+      const i32x4* src = reinterpret_cast<const i32x4*>(a.qc + row * kPfDQK);
+#pragma unroll
+      for (int sg = 0; sg < 3; ++sg) qop[u][sg] = src[4 * sg + g];
+      qsc[u] = a.qs[row] * a.sm_scale * kLog2e;
+    }
+  }
+
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int key0 = kb * kPfBlock;
+    const int nk = min(kPfBlock, blk.n - key0);
+    __syncthreads();                              // the previous block's reads are done
+    for (int c = threadIdx.x; c < kPfBlock * 12; c += 256) {
+      const int key = c / 12, part = c - key * 12;
+      i32x4 val = i32x4{0, 0, 0, 0};
+      if (key < nk)
+        val = reinterpret_cast<const i32x4*>(a.kc + (int64_t(blk.t0 + key0 + key) * H + h) *
+                                                        kPfDQK)[part];
+      *reinterpret_cast<i32x4*>(ktile + key * kKStride + 16 * part) = val;
+    }
+    const uint8_t* vsrc = a.vc + (int64_t(blk.b0 + kb) * H + h) * (kPfDV * kPfBlock);
+    for (int c = threadIdx.x; c < kPfDV * 8; c += 256) {
+      const int ch = c >> 3, part = c & 7;
+      *reinterpret_cast<i32x4*>(vtile + ch * kVStride + 16 * part) =
+          reinterpret_cast<const i32x4*>(vsrc + ch * kPfBlock)[part];
+    }
+    if (threadIdx.x < kPfBlock)
+      kscale[threadIdx.x] = int(threadIdx.x) < nk
+                                ? a.ks[int64_t(blk.t0 + key0 + int(threadIdx.x)) * H + h]
+                                : 0.f;
+    else
+      vscale[threadIdx.x - kPfBlock] =
+          a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x - kPfBlock];
+    __syncthreads();
+
+    // scores S^T: key 16 T + 4 g + r, query col, for both query tiles
+    i32x4 sacc[2][8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      sacc[0][T] = sacc[1][T] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int sg = 0; sg < 3; ++sg) {
+        const i32x4 kop =
+            *reinterpret_cast<const i32x4*>(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
+      }
+    }
+
+    // mask, dequantize, online softmax, P to e4m3
+    float alpha[2];
+    i32x8 pop[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float s[8][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        const f32x4 ksv = *reinterpret_cast<const f32x4*>(kscale + 16 * T + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * T + 4 * g + r;
+          const bool vis = key <= qi[u] && key < blk.n;
+          s[T][r] = vis ? float(sacc[u][T][r]) * qsc[u] * ksv[r] : -INFINITY;
+          mx = fmaxf(mx, s[T][r]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[u], mx);
+      const bool none = mnew == -INFINITY;        // nothing visible yet
+      alpha[u] = none ? 1.f : exp2f(m[u] - mnew);
+      const float base = none ? 0.f : mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = exp2f(s[T][r] - base);
+          ps += p[r];
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
+        pop[u][T] = w;
+      }
+      lsum[u] = lsum[u] * alpha[u] + ps;
+      m[u] = mnew;
+    }
+
+    // O^T += V^T P^T per 16-channel tile, then the block's channel scales
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const i32x4* vr = reinterpret_cast<const i32x4*>(vtile + (16 * ct + col) * kVStride + 32 * g);
+      const i32x4 v0 = vr[0], v1 = vr[1];
+      const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const f32x4 vsc = *reinterpret_cast<const f32x4*>(vscale + 16 * ct + 4 * g);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+        acc[u][ct] = acc[u][ct] * alpha[u] + c * vsc;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float l = lsum[u];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (qi[u] >= blk.n) continue;
+    const int64_t row = int64_t(blk.t0 + qi[u]) * H + h;
+    const float inv = 1.f / (kPScale * l);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const f32x4 o = acc[u][ct] * inv;
+      const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+      *reinterpret_cast<bf16x4*>(a.o + row * (kPfDV * 2) + (16 * ct + 4 * g) * 2) = ob;
+    }
+    if (g == 0) a.lse[row] = m[u] * kLn2 + logf(l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
+  const int64_t wgs = int64_t(a.num_blocks) * a.num_heads;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_prefill_attn_kernel, dim3(unsigned(wgs)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -21,7 +21,7 @@ BIN = os.path.join(OUT, "run_case")
 KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
                 "plan_kernel.hip", "tree_kernel.hip", "api.cpp", "plan.cpp", "kernels.h",
                 "append.h", "plan_core.h", "plan_device.h", "tree.h", "plan_layout.h",
-                "validate.h"]
+                "validate.h", "prefill.h", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip"]
 
 
 def compiler() -> str:
@@ -48,7 +48,8 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
         flags.append("-fsanitize=address")
     units = [os.path.join(src, f) for f in ("decode_kernel.hip", "combine_kernel.hip",
                                              "append_kernel.hip", "plan_kernel.hip",
-                                             "tree_kernel.hip", "api.cpp", "plan.cpp")]
+                                             "tree_kernel.hip", "prefill_quant_kernel.hip",
+                                             "prefill_attn_kernel.hip", "api.cpp", "plan.cpp")]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     objs = []
     for u in units:

@@ -13,6 +13,7 @@ BIN = os.path.join(HERE, "_build", "run_case")
 MAGIC = 0x4D4C4145
 TREE_MAGIC = 0x4D4C4154
 APPEND_MAGIC = 0x4D4C4141
+PREFILL_MAGIC = 0x4D4C5046
 
 
 def ensure_built() -> str:
@@ -143,3 +144,44 @@ def run_plan_device(batch, num_heads, max_q_len, page_size, num_pages, max_pages
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_prefill(case, num_blocks: int, timeout: float = 900.0):
+    """A packed prefill case (``workloads.prefill.PrefillCase``) through
+    mla_prefill_quantize + mla_prefill_attn.  Returns a dict of the outputs:
+    qc, qs, kc, ks [T, H, ...], vc [blocks, H, 128, 128], vs [blocks, H, 128],
+    o (bf16 bits [T, H, 128]), lse [T, H]."""
+    S, T, H = case.num_seqs, case.num_tokens, case.num_heads
+    hdr = np.array([PREFILL_MAGIC, S, T, H, num_blocks, 0, 0, 0, 0, 0, 0, 0], dtype=np.int32)
+    with tempfile.TemporaryDirectory() as d:
+        fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
+        with open(fin, "wb") as f:
+            f.write(hdr.tobytes())
+            f.write(np.float32(case.sm_scale).tobytes())
+            f.write(np.ascontiguousarray(case.cu_seqlens, dtype=np.int32).tobytes())
+            for x in (case.q, case.k, case.v):
+                f.write(np.ascontiguousarray(x).tobytes())
+        env = dict(os.environ)
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+                             timeout=timeout, env=env)
+        if res.returncode != 0:
+            raise RuntimeError(f"emulated run failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
+        raw = np.fromfile(fout, dtype=np.uint8)
+    out, off = {}, 0
+
+    def take(name, n, dtype, shape):
+        nonlocal off
+        out[name] = raw[off:off + n].view(dtype).reshape(shape)
+        off += n
+
+    take("qc", T * H * 192, np.int8, (T, H, 192))
+    take("qs", T * H * 4, np.float32, (T, H))
+    take("kc", T * H * 192, np.int8, (T, H, 192))
+    take("ks", T * H * 4, np.float32, (T, H))
+    take("vc", num_blocks * H * 128 * 128, np.uint8, (num_blocks, H, 128, 128))
+    take("vs", num_blocks * H * 128 * 4, np.float32, (num_blocks, H, 128))
+    take("o", T * H * 128 * 2, np.uint16, (T, H, 128))
+    take("lse", T * H * 4, np.float32, (T, H))
+    assert off == raw.size
+    return out

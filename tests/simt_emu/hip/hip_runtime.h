@@ -45,6 +45,8 @@ typedef __bf16 emu_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 emu_bf16x4 __attribute__((ext_vector_type(4)));
 typedef int emu_i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned emu_u32x2 __attribute__((ext_vector_type(2)));
+typedef int emu_i32x4 __attribute__((ext_vector_type(4)));
+typedef int emu_i32x8 __attribute__((ext_vector_type(8)));
 
 namespace emu {
 // kernel launch: blocks run one after another, each as block.x lane threads
@@ -67,6 +69,9 @@ emu_u32x2 permlane16_swap(uint32_t a, uint32_t b);
 emu_u32x2 permlane32_swap(uint32_t a, uint32_t b);
 emu_f32x4 mfma16x16x32(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c);
 emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c);
+emu_i32x4 mfma_i8_16x16x64(emu_i32x4 a, emu_i32x4 b, emu_i32x4 c);
+emu_f32x4 mfma_f8_16x16x128(emu_i32x8 a, emu_i32x8 b, emu_f32x4 c, int fmt_a, int fmt_b,
+                            int scale_a, int scale_b);
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p);
 emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p);
 emu_f32x2 cvt_pk_f32_fp8(int v, bool hi);
@@ -96,6 +101,9 @@ void block_barrier();
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) emu::permlane32_swap((a), (b))
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) emu::mfma16x16x32((a), (b), (c))
 #define __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, x, y, z) emu::mfma32x32x16((a), (b), (c))
+#define __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, x, y, z) emu::mfma_i8_16x16x64((a), (b), (c))
+#define __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, fa, fb, oa, sa, ob, sb) \
+  emu::mfma_f8_16x16x128((a), (b), (c), (fa), (fb), (sa), (sb))
 #define __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p) emu::ds_read_tr16_b64((const emu_bf16x4*)(p))
 #define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) emu::ds_read_tr8_b64((const emu_i32x2*)(p))
 #define __builtin_amdgcn_cvt_pk_f32_fp8(v, hi) emu::cvt_pk_f32_fp8((v), (hi))

@@ -31,6 +31,14 @@
 //            only), block table, kv_lens, new_lens (if any)
 //   out.bin: int32 skipped count (-1 without a counter), then the kv cache
 //            and, for e4m3, the kv scales
+//
+// A quantized-prefill case (mla_prefill_quantize + mla_prefill_attn) has its
+// own magic:
+//   in.bin : int32 header[12] = {magic, S, T, H, num_blocks, 0, ...}, float
+//            softmax scale, cu_seqlens (S+1 int32), q, k (T*H*192 bf16),
+//            v (T*H*128 bf16)
+//   out.bin: q codes, q scales, k codes, k scales, v codes, v scales, O
+//            (T*H*128 bf16), LSE (T*H fp32), each at its exact size
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -111,6 +119,62 @@ int run_append(FILE* f, const int32_t* hd, const char* out_path) {
   return 0;
 }
 
+int run_prefill(FILE* f, const int32_t* hd, const char* out_path) {
+  mla_prefill_shape s{};
+  s.num_seqs = hd[1];
+  s.num_tokens = hd[2];
+  s.num_heads = hd[3];
+  s.d_qk = 192;
+  s.d_v = 128;
+  s.num_blocks = hd[4];
+  float scale = 0.f;
+  read_into(f, &scale, sizeof scale);
+  const size_t TH = size_t(s.num_tokens) * s.num_heads;
+  const size_t BH = size_t(s.num_blocks) * s.num_heads;
+  int32_t* cu = static_cast<int32_t*>(exact_alloc(size_t(s.num_seqs + 1) * 4, 4));
+  void* q = exact_alloc(TH * 192 * 2);
+  void* k = exact_alloc(TH * 192 * 2);
+  void* v = exact_alloc(TH * 128 * 2);
+  int8_t* qc = static_cast<int8_t*>(exact_alloc(TH * 192));
+  int8_t* kc = static_cast<int8_t*>(exact_alloc(TH * 192));
+  float* qs = static_cast<float*>(exact_alloc(TH * 4, 4));
+  float* ks = static_cast<float*>(exact_alloc(TH * 4, 4));
+  uint8_t* vc = static_cast<uint8_t*>(exact_alloc(BH * 128 * 128));
+  float* vs = static_cast<float*>(exact_alloc(BH * 128 * 4));
+  void* o = exact_alloc(TH * 128 * 2);
+  float* lse = static_cast<float*>(exact_alloc(TH * 4, 4));
+  read_into(f, cu, size_t(s.num_seqs + 1) * 4);
+  read_into(f, q, TH * 192 * 2);
+  read_into(f, k, TH * 192 * 2);
+  read_into(f, v, TH * 128 * 2);
+  std::fclose(f);
+  // sentinels: rows the kernels do not write keep them
+  if (TH) {
+    std::memset(o, 0xC1, TH * 128 * 2);
+    for (size_t i = 0; i < TH; ++i) lse[i] = 12345.f;
+  }
+  mla_status st = mla_prefill_quantize(&s, cu, q, k, v, qc, qs, kc, ks, vc, vs, nullptr);
+  if (st != MLA_OK) die("mla_prefill_quantize failed");
+  st = mla_prefill_attn(&s, cu, qc, qs, kc, ks, vc, vs, scale, o, lse, nullptr);
+  if (st != MLA_OK) die("mla_prefill_attn failed");
+  FILE* g = std::fopen(out_path, "wb");
+  if (!g) die("cannot open output");
+  std::fwrite(qc, 1, TH * 192, g);
+  std::fwrite(qs, 1, TH * 4, g);
+  std::fwrite(kc, 1, TH * 192, g);
+  std::fwrite(ks, 1, TH * 4, g);
+  std::fwrite(vc, 1, BH * 128 * 128, g);
+  std::fwrite(vs, 1, BH * 128 * 4, g);
+  std::fwrite(o, 1, TH * 128 * 2, g);
+  std::fwrite(lse, 1, TH * 4, g);
+  std::fclose(g);
+  for (void* p : {static_cast<void*>(cu), q, k, v, static_cast<void*>(qc),
+                  static_cast<void*>(kc), static_cast<void*>(qs), static_cast<void*>(ks),
+                  static_cast<void*>(vc), static_cast<void*>(vs), o, static_cast<void*>(lse)})
+    std::free(p);
+  return 0;
+}
+
 int run_plan(FILE* f, const int32_t* hd, const char* out_path) {
   mla_shape s{};
   s.batch = hd[1];
@@ -165,6 +229,7 @@ int main(int argc, char** argv) {
   read_into(f, hd, sizeof hd);
   if (hd[0] == 0x4d4c4141) return run_append(f, hd, argv[2]);
   if (hd[0] == 0x4d4c4150) return run_plan(f, hd, argv[2]);
+  if (hd[0] == 0x4d4c5046) return run_prefill(f, hd, argv[2]);
   read_into(f, &scale, sizeof scale);
   const bool tree = hd[0] == 0x4d4c4154;
   if (hd[0] != 0x4d4c4145 && !tree) die("bad magic");

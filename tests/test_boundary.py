@@ -330,3 +330,53 @@ def test_partials_bound_over_many_lengths():
                        pages=int(((kv + 63) // 64).sum()) + 1, maxp=int((kv.max() + 63) // 64))
         pl = mla.plan(shape, kv, ql, num_workgroups=G, upload=False)
         assert pl.info.num_partials <= 2 * (pl.info.num_workgroups - 1), (trial, B, G)
+
+
+def test_prefill_validates_before_any_launch(lib):
+    A = 0x10000   # aligned fake device addresses; never dereferenced on these paths
+    P = mla.PrefillShape
+
+    def quant(s, cu=A, q=A, k=A, v=A, qc=A, qs=A, kc=A, ks=A, vc=A, vs=A):
+        return lib.mla_prefill_quantize(ctypes.byref(s), cu, q, k, v, qc, qs, kc, ks, vc, vs, None)
+
+    def attn(s, cu=A, qc=A, qs=A, kc=A, ks=A, vc=A, vs=A, scale=0.07, o=A, lse=A):
+        return lib.mla_prefill_attn(ctypes.byref(s), cu, qc, qs, kc, ks, vc, vs, scale, o, lse,
+                                    None)
+
+    lens = np.array([300, 1, 0, 129], np.int32)
+    n = lib.mla_prefill_num_blocks(lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 4)
+    assert n == 3 + 1 + 0 + 2
+    neg = np.array([5, -1], np.int32)
+    assert lib.mla_prefill_num_blocks(neg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2) == -1
+    big = np.full(3, 2 ** 31 - 1, np.int32)
+    assert lib.mla_prefill_num_blocks(big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 3) > 0
+    s = P.make(lens, 4)
+    assert (s.num_seqs, s.num_tokens, s.num_blocks, s.d_qk, s.d_v) == (4, 430, 6, 192, 128)
+    for kw in ("cu", "q", "k", "v", "qc", "qs", "kc", "ks", "vc", "vs"):
+        assert quant(s, **{kw: None}) == 1, kw
+    for kw in ("cu", "qc", "qs", "kc", "ks", "vc", "vs", "o", "lse"):
+        assert attn(s, **{kw: None}) == 1, kw
+    for kw in ("q", "k", "v", "qc", "kc", "vc"):
+        assert quant(s, **{kw: A + 8}) == 4, kw
+    for kw in ("qs", "ks", "vs", "cu"):
+        assert quant(s, **{kw: A + 2}) == 4, kw
+    for kw in ("qc", "kc", "vc", "o"):
+        assert attn(s, **{kw: A + 8}) == 4, kw
+    assert attn(s, lse=A + 1) == 4
+    assert attn(s, scale=float("nan")) == 2
+    bad = P.make(lens, 4)
+    bad.d_qk = 128
+    assert quant(bad) == 3 and attn(bad) == 3
+    bad = P.make(lens, 0)
+    assert quant(bad) == 2
+    bad = P.make(lens, 4)
+    bad.num_blocks = bad.num_tokens + 1          # more blocks than tokens
+    assert quant(bad) == 3
+    huge = P(1, 1 << 30, 4, 192, 128, 1)         # T * H past 32-bit indexing
+    assert quant(huge) == 3
+    # no tokens: a no-op that reads no pointer
+    empty = P.make(np.zeros(2, np.int32), 4)
+    assert quant(empty, cu=None, q=None, k=None, v=None, qc=None, qs=None, kc=None, ks=None,
+                 vc=None, vs=None) == 0
+    assert attn(empty, cu=None, qc=None, qs=None, kc=None, ks=None, vc=None, vs=None, o=None,
+                lse=None) == 0

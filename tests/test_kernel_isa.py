@@ -205,10 +205,13 @@ def test_append_kernel_machine_code(append_isa):
 
 
 @pytest.mark.parametrize("src,kernel", [("plan_kernel.hip", "mla_plan_kernel"),
-                                        ("tree_kernel.hip", "mla_tree_kernel")])
+                                        ("tree_kernel.hip", "mla_tree_kernel"),
+                                        ("prefill_quant_kernel.hip", "mla_prefill_quant_qk_kernel"),
+                                        ("prefill_quant_kernel.hip", "mla_prefill_quant_v_kernel"),
+                                        ("prefill_attn_kernel.hip", "mla_prefill_attn_kernel")])
 def test_small_kernels_machine_code(tmp_path, src, kernel):
-    # the device planner and the tree-draft merge: no scratch, no scalar
-    # stores, LDS within the 160 KB a workgroup may use
+    # the device planner, the tree-draft merge and the prefill kernels: no
+    # scratch, no scalar stores, LDS within the 160 KB a workgroup may use
     out = tmp_path / "k.s"
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
@@ -223,3 +226,20 @@ def test_small_kernels_machine_code(tmp_path, src, kernel):
     assert not [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)]
     lds = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", text).group(1))
     assert lds <= 160 * 1024
+
+
+def test_prefill_attention_uses_the_int8_and_fp8_matrix_cores(tmp_path):
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", os.path.join(CSRC, "prefill_attn_kernel.hip"),
+           "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    ins = [l.split(";")[0].strip() for l in out.read_text().splitlines()]
+    # per key block and wave: 8 key tiles x 3 dim steps x 2 query tiles of
+    # INT8 products, 8 channel tiles x 2 query tiles of e4m3 products
+    assert sum(i.startswith("v_mfma_i32_16x16x64_i8") for i in ins) == 48
+    assert sum(re.match(r"v_mfma(_scale)?_f32_16x16x128_f8f6f4", i) is not None for i in ins) == 16
+    assert not [i for i in ins if i.startswith("v_mfma") and "bf16" in i]
