@@ -59,6 +59,16 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+def _blas_threads() -> int:
+    """Threads of numpy's BLAS (the oracle's matrix products), 1 if unknown."""
+    try:
+        import threadpoolctl
+    except ImportError:  # pragma: no cover
+        return 1
+    info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    return int(info[0].get("num_threads", 1)) if info else 1
+
+
 def workload_counts(case):
     """Algorithmic bytes and FLOPs of one decode call.
 
@@ -110,10 +120,6 @@ def cpu_baseline(case, seconds: float, kv_bytes_total: int, seq_fn=None):
 
     import oracle
 
-    try:
-        import threadpoolctl
-    except ImportError:   # pragma: no cover
-        threadpoolctl = None
     done = 0
     tokens = 0
     order = [b for b in range(case.batch) if int(case.q_lens[b]) > 0]
@@ -127,11 +133,7 @@ def cpu_baseline(case, seconds: float, kv_bytes_total: int, seq_fn=None):
         done += 1
         tokens += int(case.kv_lens[b])
     el = time.perf_counter() - t0
-    threads = 1
-    if threadpoolctl is not None:
-        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
-        if info:
-            threads = int(info[0].get("num_threads", 1))
+    threads = _blas_threads()
     row = case.d_qk * 2 if case.kv_dtype == "bf16" else case.d_qk + 4
     gbs = tokens * row / el / 1e9
     frac = tokens * row / kv_bytes_total
@@ -283,6 +285,146 @@ def main_append(args) -> int:
     return 0
 
 
+PREFILL_KERNEL = "mla_prefill_attn_kernel"
+PREFILL_SOURCES = ("prefill_attn_kernel.hip", "prefill.h")
+MFMA_INT8_FP8_PEAK_TOPS = 5000.0   # dense INT8 and FP8 MFMA, MI355X
+
+
+def prefill_counts(seqlens, H):
+    """Work of one quantized causal prefill.
+
+    Ops: every (query, visible key) pair of a head costs 2 * 192 (INT8 QK) +
+    2 * 128 (e4m3 PV).  Quantize bytes: bf16 Q, K, V read once; INT8 codes +
+    fp32 scales of Q and K, e4m3 V codes and per-block channel scales written.
+    Attention bytes: codes and scales read once, bf16 O and fp32 LSE written."""
+    lens = [int(n) for n in seqlens]
+    pairs = sum(n * (n + 1) // 2 for n in lens)
+    T = sum(lens)
+    nb = sum((n + 127) // 128 for n in lens)
+    return {
+        "tokens": T, "blocks": nb, "pairs": pairs * H,
+        "ops": pairs * H * 2 * (192 + 128),
+        "quant_bytes": T * H * (2 * 192 * 2 + 128 * 2) + T * H * 2 * (192 + 4)
+        + nb * H * 128 * (128 + 4),
+        "attn_bytes": T * H * 2 * (192 + 4) + nb * H * 128 * (128 + 4) + T * H * (256 + 4),
+    }
+
+
+def prefill_cpu_baseline(case, seconds: float, ops_total: int):
+    """The float64 oracle on one head of the same prompt: its quantizers, then
+    sampled rows (random tokens), until ``seconds`` have passed; scaled to
+    the whole workload's tokens/s by the share of its ops done."""
+    import numpy as np
+    from oracle import prefill_ref
+    from workloads.prefill import PrefillCase
+    t0 = time.perf_counter()
+    one = PrefillCase(name="one-head", seqlens=case.seqlens, cu_seqlens=case.cu_seqlens,
+                      num_heads=1, sm_scale=case.sm_scale, q=case.q[:, :1], k=case.k[:, :1],
+                      v=case.v[:, :1])
+    quant = prefill_ref.quantize_case(one)
+    rng = np.random.default_rng(0)
+    cu = case.cu_seqlens
+    ops = 0
+    rows = 0
+    while time.perf_counter() - t0 < seconds:
+        t = int(rng.integers(0, case.num_tokens))
+        prefill_ref.sage_prefill_ref(one, rows=[(t, 0)], quantized=quant)
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        ops += (t - int(cu[s]) + 1) * 2 * (192 + 128)
+        rows += 1
+    el = time.perf_counter() - t0
+    return {"value": round(case.num_tokens * (ops / ops_total) / el, 6), "unit": "tokens/s",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"one head of the same prompt quantized, then {rows} random query rows "
+                      f"({ops:.3g} of the workload's {ops_total:.3g} ops) in {el:.1f} s, "
+                      f"scaled by the share of ops done"}
+
+
+def main_prefill(args) -> int:
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_absorbed_amd as mla
+    from workloads.prefill import PREFILL_WORKLOADS, prefill_workload
+
+    dev = torch.device("cuda:0")
+    mla.load_library()
+    log(f"workload {args.workload}: generating inputs")
+    case = prefill_workload(args.workload)
+    H = case.num_heads
+    cnt = prefill_counts(case.seqlens, H)
+    shape = mla.PrefillShape.make(case.seqlens, H)
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf16(case.q), bf16(case.k), bf16(case.v)
+    cu = torch.from_numpy(case.cu_seqlens.astype(np.int32)).to(dev)
+    quant = mla.prefill_alloc_quant(shape, dev)
+    out = torch.empty((case.num_tokens, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.num_tokens, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"{case.num_seqs} prompts, {cnt['tokens']} tokens, {H} heads, {cnt['blocks']} blocks")
+
+    def step():
+        mla.prefill_quantize(shape, cu, q, k, v, quant=quant, stream=stream)
+
+    def step_attn():
+        mla.prefill_attn(shape, cu, quant, case.sm_scale, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+        step_attn()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    w0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+        step_attn()
+        ev[i][2].record(stream)
+        if (i + 1) % 10 == 0:
+            torch.cuda.synchronize()
+            log(f"step {i + 1}/{K}")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    a_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    call_ms = q_ms + a_ms
+    tops = cnt["ops"] / (a_ms * 1e-3) / 1e12
+    quant_gbs = cnt["quant_bytes"] / (q_ms * 1e-3) / 1e9
+    log(f"timed {K} calls: quantize {q_ms:.3f} ms ({quant_gbs:.0f} GB/s), "
+        f"attention {a_ms:.3f} ms ({tops:.1f} TOPS)")
+    traffic = read_traffic(args.workload, PREFILL_KERNEL, PREFILL_SOURCES)
+    res = {
+        "metric": "quantized causal prefill tokens/s (INT8 QK, e4m3 PV, head dim 192/128)",
+        "value": round(cnt["tokens"] / (call_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(call_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+e4m3", "data": "synthetic",
+        "config": {"workload": args.workload, "prompts": case.num_seqs, "tokens": cnt["tokens"],
+                   "num_heads": H, "d_qk": 192, "d_v": 128, "causal": True,
+                   "description": PREFILL_WORKLOADS[args.workload][1]},
+        "ms_quantize": round(q_ms, 4), "ms_attention": round(a_ms, 4),
+        "quantize_GBps": round(quant_gbs, 1), "attention_tops": round(tops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2),
+                     "peak": MFMA_INT8_FP8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(tops / MFMA_INT8_FP8_PEAK_TOPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": PREFILL_KERNEL, "ops_per_launch": cnt["ops"],
+                     "alg_bytes_per_launch": cnt["attn_bytes"]},
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES), "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on one head for about {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_seconds, cnt["ops"])
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +460,9 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.workload in APPEND_WORKLOADS:
         return main_append(args)
+    from workloads.prefill import PREFILL_WORKLOADS
+    if args.workload in PREFILL_WORKLOADS:
+        return main_prefill(args)
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
