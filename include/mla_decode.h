@@ -394,7 +394,7 @@ mla_status mla_prefill_quantize(const mla_prefill_shape* shape, const int32_t* c
  * The attention of the formula above, from mla_prefill_quantize's outputs.
  *
  *   o    [T, H, 128] bf16 (device, 16-byte aligned); lse [T, H] fp32 (device).
- *   softmax_scale  finite.
+ *   softmax_scale  finite and > 0 (BAD_SHAPE otherwise).
  *
  * One workgroup per (128-token block, head); the P V product runs on e4m3
  * matrix instructions and the Q K product on INT8 ones.  Errors as for

@@ -366,7 +366,7 @@ mla_status mla_prefill_attn(const mla_prefill_shape* shape, const int32_t* cu_se
         reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(lse) |
         reinterpret_cast<uintptr_t>(cu_seqlens)) & 3u))
     return MLA_ERR_MISALIGNED;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_BAD_SHAPE;
   PrefillAttnArgs a{};
   a.cu = cu_seqlens;
   a.qc = q_codes;

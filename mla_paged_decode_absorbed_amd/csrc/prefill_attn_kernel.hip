@@ -45,8 +45,151 @@ constexpr int kKStride = 208;                 // LDS bytes per key row (192 + 16
 constexpr int kVStride = 144;                 // LDS bytes per channel row (128 + 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kPScale = 448.f;
+constexpr float kLog2PScale = 8.807354922057604f;   // log2(448)
+constexpr float kLnPScale = 6.104793232414985f;     // ln(448)
 constexpr int kE8M0One = 127;                 // unit block scale of the fp8 instruction
+
+// One key block: scores, online softmax, P V.  kMask: the block holds keys
+// after some query (the diagonal block) or past the sequence's end.
+template <bool kMask>
+__device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t* vtile,
+                                             const float* kscale, const float* vscale,
+                                             const i32x4 (&qop)[2][3], const float (&qsc)[2],
+                                             const int (&qi)[2], int key0, int n, int g, int col,
+                                             float (&m)[2], float (&lsum)[2],
+                                             f32x4 (&acc)[2][8]) {
+  // scores S^T: key 16 T + 4 g + r, query col, for both query tiles
+  i32x4 sacc[2][8];
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    sacc[0][T] = sacc[1][T] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int sg = 0; sg < 3; ++sg) {
+      const i32x4 kop =
+          *reinterpret_cast<const i32x4*>(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
+    }
+  }
+  // t = S * k_scale; with q_scale * softmax_scale * log2(e) = qsc > 0 the
+  // log2-domain score is t * qsc, so the row max is qsc * max t
+  float t[2][8][4];
+  float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    const f32x4 ksv = *reinterpret_cast<const f32x4*>(kscale + 16 * T + 4 * g);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = float(sacc[u][T][r]) * ksv[r];
+        if (kMask) {
+          const int key = key0 + 16 * T + 4 * g + r;
+          if (!(key <= qi[u] && key < n)) v = -INFINITY;
+        }
+        t[u][T][r] = v;
+        mx[u] = fmaxf(mx[u], v);
+      }
+  }
+  float alpha[2];
+  i32x8 pop[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float mt = fmaxf(mx[u], __shfl_xor(mx[u], 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mnew = fmaxf(m[u], mt * qsc[u]);
+    const bool none = mnew == -INFINITY;          // nothing visible yet (padding queries)
+    alpha[u] = none ? 1.f : __builtin_amdgcn_exp2f(m[u] - mnew);
+    // 448 P = 2^(t qsc - (m - log2 448)), straight into e4m3.  mnew rounds
+    // t qsc once more than the fused exponent below does, so the subtracted
+    // max is raised by a bound on that rounding (|m| 2^-20 + 2^-16, under
+    // 1e-5 of P): 448 P then stays below 448, the largest e4m3 value
+    const float mb = none ? 0.f : mnew - kLog2PScale + (fabsf(mnew) * 0x1p-20f + 0x1p-16f);
+    float ps = 0.f;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(t[u][T][r], qsc[u], -mb));
+        if (kMask && t[u][T][r] == -INFINITY) p[r] = 0.f;
+        ps += p[r];
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+      pop[u][T] = w;
+    }
+    lsum[u] = lsum[u] * alpha[u] + ps;
+    m[u] = mnew;
+  }
+  // O^T += V^T P^T per 16-channel tile, times the block's channel scales
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const i32x4* vr = reinterpret_cast<const i32x4*>(vtile + (16 * ct + col) * kVStride + 32 * g);
+    const i32x4 v0 = vr[0], v1 = vr[1];
+    const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const f32x4 vsc = *reinterpret_cast<const f32x4*>(vscale + 16 * ct + 4 * g);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+      acc[u][ct] = acc[u][ct] * alpha[u] + c * vsc;
+    }
+  }
+}
+
+// K codes (6 x 16 B per thread), V codes (4 x 16 B) and the scales of one
+// key block, loaded to registers so the loads of the next block are in
+// flight while this one is computed.
+struct BlockRegs {
+  i32x4 k[6], v[4];
+  float sc;
+};
+
+__device__ __forceinline__ void load_block(const PrefillAttnArgs& a, const PfBlock& blk, int kb,
+                                           int h, BlockRegs& r) {
+  const int H = a.num_heads;
+  const int key0 = kb * kPfBlock;
+  const int nk = min(kPfBlock, blk.n - key0);
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int c = int(threadIdx.x) + 256 * j;
+    const int key = c / 12, part = c - key * 12;
+    r.k[j] = i32x4{0, 0, 0, 0};
+    if (key < nk)
+      r.k[j] = reinterpret_cast<const i32x4*>(a.kc + (int64_t(blk.t0 + key0 + key) * H + h) *
+                                                         kPfDQK)[part];
+  }
+  const i32x4* vsrc =
+      reinterpret_cast<const i32x4*>(a.vc + (int64_t(blk.b0 + kb) * H + h) * (kPfDV * kPfBlock));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.v[j] = vsrc[int(threadIdx.x) + 256 * j];
+  if (threadIdx.x < kPfBlock)
+    r.sc = int(threadIdx.x) < nk ? a.ks[int64_t(blk.t0 + key0 + int(threadIdx.x)) * H + h] : 0.f;
+  else
+    r.sc = a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x - kPfBlock];
+}
+
+__device__ __forceinline__ void store_block(const BlockRegs& r, int8_t* ktile, uint8_t* vtile,
+                                            float* kscale, float* vscale) {
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int c = int(threadIdx.x) + 256 * j;
+    const int key = c / 12, part = c - key * 12;
+    *reinterpret_cast<i32x4*>(ktile + key * kKStride + 16 * part) = r.k[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = int(threadIdx.x) + 256 * j;
+    *reinterpret_cast<i32x4*>(vtile + (c >> 3) * kVStride + 16 * (c & 7)) = r.v[j];
+  }
+  if (threadIdx.x < kPfBlock)
+    kscale[threadIdx.x] = r.sc;
+  else
+    vscale[threadIdx.x - kPfBlock] = r.sc;
+}
 
 __global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t ktile[kPfBlock * kKStride];
@@ -62,6 +205,9 @@ __global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttn
   const int qb = blk.kb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
+
+  BlockRegs regs;
+  load_block(a, blk, 0, h, regs);
 
   // this lane's two queries (one per 16-query tile) and their Q operands
   int qi[2];
@@ -90,120 +236,34 @@ __global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttn
     for (int ct = 0; ct < 8; ++ct) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int kb = 0; kb <= qb; ++kb) {
-    const int key0 = kb * kPfBlock;
-    const int nk = min(kPfBlock, blk.n - key0);
     __syncthreads();                              // the previous block's reads are done
-    for (int c = threadIdx.x; c < kPfBlock * 12; c += 256) {
-      const int key = c / 12, part = c - key * 12;
-      i32x4 val = i32x4{0, 0, 0, 0};
-      if (key < nk)
-        val = reinterpret_cast<const i32x4*>(a.kc + (int64_t(blk.t0 + key0 + key) * H + h) *
-                                                        kPfDQK)[part];
-      *reinterpret_cast<i32x4*>(ktile + key * kKStride + 16 * part) = val;
-    }
-    const uint8_t* vsrc = a.vc + (int64_t(blk.b0 + kb) * H + h) * (kPfDV * kPfBlock);
-    for (int c = threadIdx.x; c < kPfDV * 8; c += 256) {
-      const int ch = c >> 3, part = c & 7;
-      *reinterpret_cast<i32x4*>(vtile + ch * kVStride + 16 * part) =
-          reinterpret_cast<const i32x4*>(vsrc + ch * kPfBlock)[part];
-    }
-    if (threadIdx.x < kPfBlock)
-      kscale[threadIdx.x] = int(threadIdx.x) < nk
-                                ? a.ks[int64_t(blk.t0 + key0 + int(threadIdx.x)) * H + h]
-                                : 0.f;
-    else
-      vscale[threadIdx.x - kPfBlock] =
-          a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x - kPfBlock];
+    store_block(regs, ktile, vtile, kscale, vscale);
     __syncthreads();
-
-    // scores S^T: key 16 T + 4 g + r, query col, for both query tiles
-    i32x4 sacc[2][8];
-#pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      sacc[0][T] = sacc[1][T] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int sg = 0; sg < 3; ++sg) {
-        const i32x4 kop =
-            *reinterpret_cast<const i32x4*>(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
-      }
-    }
-
-    // mask, dequantize, online softmax, P to e4m3
-    float alpha[2];
-    i32x8 pop[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float s[8][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int T = 0; T < 8; ++T) {
-        const f32x4 ksv = *reinterpret_cast<const f32x4*>(kscale + 16 * T + 4 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 16 * T + 4 * g + r;
-          const bool vis = key <= qi[u] && key < blk.n;
-          s[T][r] = vis ? float(sacc[u][T][r]) * qsc[u] * ksv[r] : -INFINITY;
-          mx = fmaxf(mx, s[T][r]);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[u], mx);
-      const bool none = mnew == -INFINITY;        // nothing visible yet
-      alpha[u] = none ? 1.f : exp2f(m[u] - mnew);
-      const float base = none ? 0.f : mnew;
-      float ps = 0.f;
-#pragma unroll
-      for (int T = 0; T < 8; ++T) {
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = exp2f(s[T][r] - base);
-          ps += p[r];
-        }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
-        pop[u][T] = w;
-      }
-      lsum[u] = lsum[u] * alpha[u] + ps;
-      m[u] = mnew;
-    }
-
-    // O^T += V^T P^T per 16-channel tile, then the block's channel scales
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const i32x4* vr = reinterpret_cast<const i32x4*>(vtile + (16 * ct + col) * kVStride + 32 * g);
-      const i32x4 v0 = vr[0], v1 = vr[1];
-      const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      const f32x4 vsc = *reinterpret_cast<const f32x4*>(vscale + 16 * ct + 4 * g);
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
-        acc[u][ct] = acc[u][ct] * alpha[u] + c * vsc;
-      }
-    }
+    if (kb < qb) load_block(a, blk, kb + 1, h, regs);
+    // blocks below the diagonal are whole and wholly visible
+    if (kb < qb)
+      attend_block<false>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
+                          col, m, lsum, acc);
+    else
+      attend_block<true>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
+                         col, m, lsum, acc);
   }
 
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    float l = lsum[u];
+    float l = lsum[u];                            // 448 times the softmax sum
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (qi[u] >= blk.n) continue;
     const int64_t row = int64_t(blk.t0 + qi[u]) * H + h;
-    const float inv = 1.f / (kPScale * l);
+    const float inv = 1.f / l;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const f32x4 o = acc[u][ct] * inv;
       const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
       *reinterpret_cast<bf16x4*>(a.o + row * (kPfDV * 2) + (16 * ct + 4 * g) * 2) = ob;
     }
-    if (g == 0) a.lse[row] = m[u] * kLn2 + logf(l);
+    if (g == 0) a.lse[row] = m[u] * kLn2 + logf(l) - kLnPScale;
   }
 }
 

@@ -364,6 +364,7 @@ def test_prefill_validates_before_any_launch(lib):
         assert attn(s, **{kw: A + 8}) == 4, kw
     assert attn(s, lse=A + 1) == 4
     assert attn(s, scale=float("nan")) == 2
+    assert attn(s, scale=0.0) == 2 and attn(s, scale=-0.1) == 2
     bad = P.make(lens, 4)
     bad.d_qk = 128
     assert quant(bad) == 3 and attn(bad) == 3
