@@ -4,9 +4,12 @@
 // and multiplied with the e4m3 V on the fp8 matrix cores, V's per-channel
 // scale taken off each block's product.
 //
-// A workgroup takes one 128-token query block of one head; each of its 4
-// waves 32 queries (two 16-query tiles).  Key blocks of 128 (the same blocks
-// that carry V's scales) are staged in LDS in turn, up to the diagonal:
+// A workgroup takes one 128-token query block of one head; each of its 8
+// waves one 16-query tile (a smaller register set per wave than two tiles,
+// so more waves share a SIMD and the compiler can hoist the LDS operand
+// reads).  Key blocks of 128 (the same blocks that carry V's scales) are
+// staged in LDS in turn, up to the diagonal, the next block's codes already
+// loading into registers while one is computed:
 //
 //  * scores: S^T[16 keys x 16 queries] = K Q^T on v_mfma_i32_16x16x64_i8,
 //    3 steps over the 192 dims; Q's operands stay in registers.  In the
@@ -48,39 +51,44 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2PScale = 8.807354922057604f;   // log2(448)
 constexpr float kLnPScale = 6.104793232414985f;     // ln(448)
 constexpr int kE8M0One = 127;                 // unit block scale of the fp8 instruction
+constexpr int kWaves = 8;                     // waves per workgroup
+constexpr int kTilesPerWave = 1;              // 16-query tiles per wave
 
 // One key block: scores, online softmax, P V.  kMask: the block holds keys
 // after some query (the diagonal block) or past the sequence's end.
-template <bool kMask>
+template <int kU, bool kMask>
 __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t* vtile,
                                              const float* kscale, const float* vscale,
-                                             const i32x4 (&qop)[2][3], const float (&qsc)[2],
-                                             const int (&qi)[2], int key0, int n, int g, int col,
-                                             float (&m)[2], float (&lsum)[2],
-                                             f32x4 (&acc)[2][8]) {
-  // scores S^T: key 16 T + 4 g + r, query col, for both query tiles
-  i32x4 sacc[2][8];
+                                             const i32x4 (&qop)[kU][3], const float (&qsc)[kU],
+                                             const int (&qi)[kU], int key0, int n, int g, int col,
+                                             float (&m)[kU], float (&lsum)[kU],
+                                             f32x4 (&acc)[kU][8]) {
+  // scores S^T: key 16 T + 4 g + r, query col, for every query tile
+  i32x4 sacc[kU][8];
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
-    sacc[0][T] = sacc[1][T] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kU; ++u) sacc[u][T] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int sg = 0; sg < 3; ++sg) {
       const i32x4 kop =
           *reinterpret_cast<const i32x4*>(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < kU; ++u)
         sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
     }
   }
   // t = S * k_scale; with q_scale * softmax_scale * log2(e) = qsc > 0 the
   // log2-domain score is t * qsc, so the row max is qsc * max t
-  float t[2][8][4];
-  float mx[2] = {-INFINITY, -INFINITY};
+  float t[kU][8][4];
+  float mx[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) mx[u] = -INFINITY;
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
     const f32x4 ksv = *reinterpret_cast<const f32x4*>(kscale + 16 * T + 4 * g);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = float(sacc[u][T][r]) * ksv[r];
@@ -92,10 +100,10 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
         mx[u] = fmaxf(mx[u], v);
       }
   }
-  float alpha[2];
-  i32x8 pop[2];
+  float alpha[kU];
+  i32x8 pop[kU];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kU; ++u) {
     float mt = fmaxf(mx[u], __shfl_xor(mx[u], 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mnew = fmaxf(m[u], mt * qsc[u]);
@@ -132,7 +140,7 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
     const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     const f32x4 vsc = *reinterpret_cast<const f32x4*>(vscale + 16 * ct + 4 * g);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
       acc[u][ct] = acc[u][ct] * alpha[u] + c * vsc;
@@ -140,22 +148,27 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
   }
 }
 
-// K codes (6 x 16 B per thread), V codes (4 x 16 B) and the scales of one
-// key block, loaded to registers so the loads of the next block are in
-// flight while this one is computed.
+// K codes, V codes and the scales of one key block, loaded to registers by
+// the kThreads threads so the loads of the next block are in flight while
+// this one is computed.
+template <int kThreads>
 struct BlockRegs {
-  i32x4 k[6], v[4];
+  static constexpr int kK = kPfBlock * 12 / kThreads;      // 16-byte K chunks per thread
+  static constexpr int kV = kPfDV * 8 / kThreads;          // 16-byte V chunks per thread
+  static_assert(kK * kThreads == kPfBlock * 12 && kV * kThreads == kPfDV * 8, "chunking");
+  i32x4 k[kK], v[kV];
   float sc;
 };
 
+template <int kThreads>
 __device__ __forceinline__ void load_block(const PrefillAttnArgs& a, const PfBlock& blk, int kb,
-                                           int h, BlockRegs& r) {
+                                           int h, BlockRegs<kThreads>& r) {
   const int H = a.num_heads;
   const int key0 = kb * kPfBlock;
   const int nk = min(kPfBlock, blk.n - key0);
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int c = int(threadIdx.x) + 256 * j;
+  for (int j = 0; j < BlockRegs<kThreads>::kK; ++j) {
+    const int c = int(threadIdx.x) + kThreads * j;
     const int key = c / 12, part = c - key * 12;
     r.k[j] = i32x4{0, 0, 0, 0};
     if (key < nk)
@@ -165,33 +178,39 @@ __device__ __forceinline__ void load_block(const PrefillAttnArgs& a, const PfBlo
   const i32x4* vsrc =
       reinterpret_cast<const i32x4*>(a.vc + (int64_t(blk.b0 + kb) * H + h) * (kPfDV * kPfBlock));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) r.v[j] = vsrc[int(threadIdx.x) + 256 * j];
+  for (int j = 0; j < BlockRegs<kThreads>::kV; ++j) r.v[j] = vsrc[int(threadIdx.x) + kThreads * j];
+  r.sc = 0.f;
   if (threadIdx.x < kPfBlock)
     r.sc = int(threadIdx.x) < nk ? a.ks[int64_t(blk.t0 + key0 + int(threadIdx.x)) * H + h] : 0.f;
-  else
+  else if (threadIdx.x < kPfBlock + kPfDV)
     r.sc = a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x - kPfBlock];
 }
 
-__device__ __forceinline__ void store_block(const BlockRegs& r, int8_t* ktile, uint8_t* vtile,
-                                            float* kscale, float* vscale) {
+template <int kThreads>
+__device__ __forceinline__ void store_block(const BlockRegs<kThreads>& r, int8_t* ktile,
+                                            uint8_t* vtile, float* kscale, float* vscale) {
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int c = int(threadIdx.x) + 256 * j;
+  for (int j = 0; j < BlockRegs<kThreads>::kK; ++j) {
+    const int c = int(threadIdx.x) + kThreads * j;
     const int key = c / 12, part = c - key * 12;
     *reinterpret_cast<i32x4*>(ktile + key * kKStride + 16 * part) = r.k[j];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = int(threadIdx.x) + 256 * j;
+  for (int j = 0; j < BlockRegs<kThreads>::kV; ++j) {
+    const int c = int(threadIdx.x) + kThreads * j;
     *reinterpret_cast<i32x4*>(vtile + (c >> 3) * kVStride + 16 * (c & 7)) = r.v[j];
   }
   if (threadIdx.x < kPfBlock)
     kscale[threadIdx.x] = r.sc;
-  else
+  else if (threadIdx.x < kPfBlock + kPfDV)
     vscale[threadIdx.x - kPfBlock] = r.sc;
 }
 
-__global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
+// kW waves of kU 16-query tiles each cover the 128 queries of a block.
+template <int kW, int kU>
+__global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
+  static_assert(kW * kU * 16 == kPfBlock, "a workgroup covers one query block");
+  constexpr int kThreads = kW * 64;
   __shared__ __attribute__((aligned(16))) int8_t ktile[kPfBlock * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kPfDV * kVStride];
   __shared__ __attribute__((aligned(16))) float kscale[kPfBlock];
@@ -206,16 +225,16 @@ __global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttn
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  BlockRegs regs;
-  load_block(a, blk, 0, h, regs);
+  BlockRegs<kThreads> regs;
+  load_block<kThreads>(a, blk, 0, h, regs);
 
-  // this lane's two queries (one per 16-query tile) and their Q operands
-  int qi[2];
-  float qsc[2];
-  i32x4 qop[2][3];
+  // this lane's queries (one per 16-query tile) and their Q operands
+  int qi[kU];
+  float qsc[kU];
+  i32x4 qop[kU][3];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    qi[u] = qb * kPfBlock + wave * 32 + u * 16 + col;
+  for (int u = 0; u < kU; ++u) {
+    qi[u] = qb * kPfBlock + wave * 16 * kU + u * 16 + col;
     qsc[u] = 0.f;
 #pragma unroll
     for (int sg = 0; sg < 3; ++sg) qop[u][sg] = i32x4{0, 0, 0, 0};
@@ -228,29 +247,32 @@ __global__ __launch_bounds__(256) void mla_prefill_attn_kernel(const PrefillAttn
     }
   }
 
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  f32x4 acc[2][8];
+  float m[kU], lsum[kU];
+  f32x4 acc[kU][8];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < kU; ++u) {
+    m[u] = -INFINITY;
+    lsum[u] = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   for (int kb = 0; kb <= qb; ++kb) {
     __syncthreads();                              // the previous block's reads are done
-    store_block(regs, ktile, vtile, kscale, vscale);
+    store_block<kThreads>(regs, ktile, vtile, kscale, vscale);
     __syncthreads();
-    if (kb < qb) load_block(a, blk, kb + 1, h, regs);
+    if (kb < qb) load_block<kThreads>(a, blk, kb + 1, h, regs);
     // blocks below the diagonal are whole and wholly visible
     if (kb < qb)
-      attend_block<false>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
-                          col, m, lsum, acc);
+      attend_block<kU, false>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n,
+                              g, col, m, lsum, acc);
     else
-      attend_block<true>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
-                         col, m, lsum, acc);
+      attend_block<kU, true>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
+                             col, m, lsum, acc);
   }
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kU; ++u) {
     float l = lsum[u];                            // 448 times the softmax sum
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -273,7 +295,8 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   const int64_t wgs = int64_t(a.num_blocks) * a.num_heads;
   if (wgs <= 0) return hipSuccess;
   if (wgs > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_prefill_attn_kernel, dim3(unsigned(wgs)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((mla_prefill_attn_kernel<kWaves, kTilesPerWave>), dim3(unsigned(wgs)),
+                     dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -238,10 +238,10 @@ def test_prefill_attention_uses_the_int8_and_fp8_matrix_cores(tmp_path):
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
     ins = [l.split(";")[0].strip() for l in out.read_text().splitlines()]
-    # per key block and wave: 8 key tiles x 3 dim steps x 2 query tiles of
-    # INT8 products, 8 channel tiles x 2 query tiles of e4m3 products; the
-    # block body exists twice (with and without the causal mask)
-    assert sum(i.startswith("v_mfma_i32_16x16x64_i8") for i in ins) == 2 * 48
-    assert sum(re.match(r"v_mfma(_scale)?_f32_16x16x128_f8f6f4", i) is not None
-               for i in ins) == 2 * 16
+    # per key block, wave and 16-query tile: 8 key tiles x 3 dim steps of
+    # INT8 products and 8 channel tiles of e4m3 products; the block body
+    # exists twice (with and without the causal mask)
+    i8 = sum(i.startswith("v_mfma_i32_16x16x64_i8") for i in ins)
+    f8 = sum(re.match(r"v_mfma(_scale)?_f32_16x16x128_f8f6f4", i) is not None for i in ins)
+    assert i8 > 0 and i8 % (2 * 24) == 0 and f8 * 3 == i8
     assert not [i for i in ins if i.startswith("v_mfma") and "bf16" in i]
