@@ -131,6 +131,17 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
     lsum[u] = lsum[u] * alpha[u] + ps;
     m[u] = mnew;
   }
+  // once no query's max moves (the usual case after the first blocks) the
+  // wave skips the rescale of its accumulators
+  bool moved = false;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) moved = moved || alpha[u] != 1.f;
+  if (__any(moved)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[u][ct] *= alpha[u];
+  }
   // O^T += V^T P^T per 16-channel tile, times the block's channel scales
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -143,7 +154,7 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
     for (int u = 0; u < kU; ++u) {
       const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
-      acc[u][ct] = acc[u][ct] * alpha[u] + c * vsc;
+      acc[u][ct] += c * vsc;
     }
   }
 }
