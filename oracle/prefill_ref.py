@@ -10,14 +10,18 @@ undone afterwards to give O.
 
 Readings (the page fixes no granularity, scale rule or block size):
 
-* Q and K: one symmetric scale per (token, head) row, scale = max|x| / 127 in
-  fp32 (1 for an all-zero row); code = x / scale (correctly rounded fp32
+* Q: one symmetric scale per (token, head) row, scale = max|x| / 127 in fp32
+  (1 for an all-zero row); code = x / scale (correctly rounded fp32
   quotient) rounded to nearest, ties to even, clamped to +-127.
-* V: one scale per (128-token block of a sequence, head, channel),
-  scale = max|v| / 448 over the block's tokens (1 if zero); code = the e4m3
-  code nearest to the correctly rounded fp32 quotient (clamped to +-448).
-  V's quantization is undone after each block's P V product, which is where
-  a per-channel scale can come off.
+* K: the same rule with one scale per (128-token block of a sequence, head),
+  the maximum taken over the block's tokens and all 192 dims: a block's
+  scores then share one key scale.
+* V: one power-of-two scale per (128-token block, head, channel), the
+  smallest 2^e with max|v| / 2^e <= 448 over the block's tokens (e >= -127;
+  2^0 for an all-zero channel); code = the e4m3 code nearest to v / 2^e, an
+  exact quotient.  V's quantization is undone after each block's P V
+  product, which is where a per-channel scale can come off; a power of two
+  is what a block-scaled (e8m0) matrix instruction applies by itself.
 * The online softmax steps over the keys in blocks of 128 from the start of
   the sequence: per block the running max is raised, P = exp(s - m) for the
   block's visible keys, l and the accumulator are rescaled by exp(m_old -
@@ -70,27 +74,58 @@ def num_blocks(seqlens) -> int:
     return int(sum((int(n) + KEY_BLOCK - 1) // KEY_BLOCK for n in seqlens))
 
 
+def _blocks(cu_seqlens):
+    """(t0, t1) of every 128-token block, sequences in order."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [(t0, min(t0 + KEY_BLOCK, int(cu[s + 1])))
+            for s in range(len(cu) - 1) for t0 in range(int(cu[s]), int(cu[s + 1]), KEY_BLOCK)]
+
+
+def quantize_k_blocks(k, cu_seqlens):
+    """K [T, H, D] (bf16 bits or fp32) -> (codes int8 [T, H, D], scales fp32
+    [blocks, H]): one scale per 128-token block and head."""
+    x = _f32(k)
+    T, H, D = x.shape
+    blocks = _blocks(cu_seqlens)
+    codes = np.zeros((T, H, D), np.int8)
+    scales = np.ones((len(blocks), H), np.float32)
+    for bi, (t0, t1) in enumerate(blocks):
+        xb = x[t0:t1]                                       # [n, H, D]
+        amax = np.max(np.abs(xb), axis=(0, 2))
+        sc = (amax / np.float32(INT8_MAX)).astype(np.float32)
+        sc = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        y = (xb / sc[None, :, None]).astype(np.float32)
+        codes[t0:t1] = np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)
+        scales[bi] = sc
+    return codes, scales
+
+
+def pow2_scale_exponent(amax) -> np.ndarray:
+    """Smallest e >= -127 with amax / 2^e <= 448 (0 where amax is 0), exactly:
+    amax = m 2^E with m in [0.5, 1) fits 448 = 0.875 * 2^9 at e = E - 9 when
+    m <= 0.875, else at E - 8."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, E = np.frexp(a)
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    e = np.maximum(e, -127)
+    return np.where(a > 0, e, 0).astype(np.int32)
+
+
 def quantize_v_blocks(v, cu_seqlens):
     """V [T, H, Dv] (bf16 bits or fp32) -> (codes uint8 [T, H, Dv], scales fp32
-    [blocks, H, Dv]); block index = the sequence's first block + key block."""
+    [blocks, H, Dv], powers of two); block index = the sequence's first block
+    + key block."""
     x = _f32(v)
     T, H, Dv = x.shape
-    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    blocks = _blocks(cu_seqlens)
     codes = np.zeros((T, H, Dv), np.uint8)
-    scales = np.ones((num_blocks(np.diff(cu)), H, Dv), np.float32)
-    blk = 0
-    for s in range(len(cu) - 1):
-        for t0 in range(int(cu[s]), int(cu[s + 1]), KEY_BLOCK):
-            t1 = min(t0 + KEY_BLOCK, int(cu[s + 1]))
-            xb = x[t0:t1]                                   # [n, H, Dv]
-            amax = np.max(np.abs(xb), axis=0)
-            sc = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-            sc = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
-            y = (xb / sc[None]).astype(np.float32)
-            y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
-            codes[t0:t1] = encode_e4m3(y)
-            scales[blk] = sc
-            blk += 1
+    scales = np.ones((len(blocks), H, Dv), np.float32)
+    for bi, (t0, t1) in enumerate(blocks):
+        xb = x[t0:t1].astype(np.float64)                    # [n, H, Dv]
+        e = pow2_scale_exponent(np.max(np.abs(xb), axis=0))
+        y = np.clip(np.ldexp(xb, -e[None]), -E4M3_MAX, E4M3_MAX)   # exact
+        codes[t0:t1] = encode_e4m3(y)
+        scales[bi] = np.ldexp(np.float32(1.0), e).astype(np.float32)
     return codes, scales
 
 
@@ -123,7 +158,7 @@ def blocked_attend_row(s, values, quant_p: bool = True, block: int = KEY_BLOCK):
 def quantize_case(case):
     """The three quantizers applied to a prefill case's bf16 inputs."""
     qc, qs = quantize_rows_int8(case.q)
-    kc, ks = quantize_rows_int8(case.k)
+    kc, ks = quantize_k_blocks(case.k, case.cu_seqlens)
     vc, vs = quantize_v_blocks(case.v, case.cu_seqlens)
     return qc, qs, kc, ks, vc, vs
 
@@ -156,7 +191,9 @@ def sage_prefill_ref(case, rows=None, quantized=None):
             vdq_cache = {key: vals}
         vals = vdq_cache[key]
         ints = kc[t0:t + 1, h].astype(np.int64) @ qc[t, h].astype(np.int64)      # exact
-        sc = ints.astype(np.float64) * float(qs[t, h]) * ks[t0:t + 1, h].astype(np.float64)
+        kscale = np.repeat(ks[int(blk0[s]):int(blk0[s + 1]), h].astype(np.float64),
+                           KEY_BLOCK)[:i + 1]
+        sc = ints.astype(np.float64) * float(qs[t, h]) * kscale
         sc = sc * case.sm_scale
         O[t, h], LSE[t, h] = blocked_attend_row(sc, vals[:i + 1])
     return O, LSE

@@ -3,10 +3,11 @@ things other than itself (CPU only):
 
 * the blocked online softmax with P unquantized equals the decode oracle's
   plain softmax attention, for any block size;
-* inputs built to quantize exactly (Q, K rows = integer codes times a power of
-  two with a +-127 element; V = e4m3 values times a power of two with +-448 in
-  every block and channel) make the whole pipeline plain causal attention up
-  to P's rounding, whose effect is bounded by e4m3's relative step;
+* inputs built to quantize exactly (Q rows, and K blocks of 128 tokens, =
+  integer codes times a power of two with a +-127 element; V = e4m3 values
+  times a power of two with +-448 in every block and channel) make the whole
+  pipeline plain causal attention up to P's rounding, whose effect is bounded
+  by e4m3's relative step;
 * closed forms: a sequence's first token returns its own dequantized V row
   and LSE = its one score; zero query rows give the mean of the visible V
   rows and LSE = ln n;
@@ -45,7 +46,14 @@ def _exact_case(seqlens, H=2, seed=0, zero_q_rows=()):
     q = int_rows((T, H, 192))
     for t in zero_q_rows:
         q[t] = 0.0
-    k = int_rows((T, H, 192))
+    # K: one power of two and one +-127 per (128-token block, head)
+    k = rng.integers(-126, 127, size=(T, H, 192)).astype(np.float32)
+    for s in range(len(seqlens)):
+        for t0 in range(int(cu[s]), int(cu[s + 1]), 128):
+            t1 = min(t0 + 128, int(cu[s + 1]))
+            for h in range(H):
+                k[int(rng.integers(t0, t1)), h, int(rng.integers(0, 192))] = 127.0 * rng.choice([-1, 1])
+                k[t0:t1, h] *= np.float32(2.0 ** int(rng.integers(-6, 3)))
     pos = E4M3_VALUES[FINITE & (np.abs(E4M3_VALUES) < 448)]
     v = rng.choice(pos, size=(T, H, 128)).astype(np.float32)
     for s in range(len(seqlens)):
@@ -66,12 +74,12 @@ def check_exact_inputs_quantize_exactly():
     case, q, k, v = _exact_case([200, 7], seed=1)
     qc, qs, kc, ks, vc, vs = prefill_ref.quantize_case(case)
     ok = np.array_equal(qc * qs[..., None].astype(np.float64), q)
-    ok &= np.array_equal(kc * ks[..., None].astype(np.float64), k)
     vdq = oracle.decode_e4m3(vc).astype(np.float64)
     blk = 0
     for s in range(case.num_seqs):
         for t0 in range(int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1]), 128):
             t1 = min(t0 + 128, int(case.cu_seqlens[s + 1]))
+            ok &= np.array_equal(kc[t0:t1] * ks[blk][None, :, None].astype(np.float64), k[t0:t1])
             ok &= np.array_equal(vdq[t0:t1] * vs[blk][None], v[t0:t1])
             blk += 1
     return bool(ok) and blk == vs.shape[0]
@@ -126,7 +134,7 @@ def check_first_token_and_zero_query_closed_forms():
         for h in range(case.num_heads):
             ok &= np.array_equal(O[t0, h], vdq[t0, h] * vs[blk0[s], h])
             s00 = float(int(qc[t0, h].astype(np.int64) @ kc[t0, h].astype(np.int64)))
-            ok &= abs(L[t0, h] - s00 * float(qs[t0, h]) * float(ks[t0, h]) * case.sm_scale) <= 1e-12
+            ok &= abs(L[t0, h] - s00 * float(qs[t0, h]) * float(ks[blk0[s], h]) * case.sm_scale) <= 1e-12
         for t in zero:
             if not t0 <= t < t1:
                 continue
@@ -169,6 +177,34 @@ def check_int8_codes_are_nearest_brute_force():
     return bool(ok)
 
 
+def check_k_codes_are_nearest_per_block():
+    case = make_prefill_case(seqlens=[200, 3], num_heads=2, seed=9)
+    case.k[5, 1] = 0x4700                           # one large key in block 0, head 1
+    case.k[128:200, 0] = 0                          # an all-zero block of head 0
+    codes, scales = prefill_ref.quantize_k_blocks(case.k, case.cu_seqlens)
+    x = oracle.decode_bf16(case.k).astype(np.float32)
+    ok = scales.shape == (3, 2)
+    cand = np.arange(-127, 128)
+    for bi, (t0, t1) in enumerate([(0, 128), (128, 200), (200, 203)]):
+        for h in range(2):
+            amax = np.float32(np.abs(x[t0:t1, h]).max())
+            want = np.float32(amax / np.float32(127)) if amax > 0 else np.float32(1)
+            ok &= scales[bi, h] == want
+            y = (x[t0:t1, h] / want).astype(np.float32).astype(np.float64).ravel()
+            sub = np.linspace(0, y.size - 1, 300).astype(int)       # a sample, plus the max
+            sub = np.append(sub, np.argmax(np.abs(y)))
+            d = np.abs(y[sub][:, None] - cand[None, :])
+            for row, j in enumerate(sub):
+                ties = cand[d[row] == d[row].min()]
+                want_c = ties[0] if len(ties) == 1 else ties[ties % 2 == 0][0]
+                ok &= int(codes[t0:t1, h].ravel()[j]) == int(want_c)
+            if amax > 0:
+                ok &= int(np.abs(codes[t0:t1, h]).max()) == 127
+            else:
+                ok &= not codes[t0:t1, h].any()
+    return bool(ok)
+
+
 def check_v_codes_are_nearest_per_block_and_channel():
     case = make_prefill_case(seqlens=[300, 2], num_heads=2, seed=6)
     case.v[:, 1, 5] = 0                                  # an all-zero channel
@@ -180,11 +216,18 @@ def check_v_codes_are_nearest_per_block_and_channel():
     blocks = [(0, 128), (128, 256), (256, 300), (300, 302)]
     for bi, (t0, t1) in enumerate(blocks):
         for h in range(2):
-            amax = np.abs(x[t0:t1, h]).max(0)
-            want = np.where(amax > 0, (amax / np.float32(448)).astype(np.float32), np.float32(1))
-            ok &= np.array_equal(scales[bi, h], want.astype(np.float32))
+            amax = np.abs(x[t0:t1, h]).max(0).astype(np.float64)
+            # the smallest power of two that brings the channel within 448, by search
+            want = np.ones(128)
+            for c in range(128):
+                if amax[c] > 0:
+                    e = -127
+                    while amax[c] / 2.0 ** e > 448:
+                        e += 1
+                    want[c] = 2.0 ** e
+            ok &= np.array_equal(scales[bi, h].astype(np.float64), want)
             for c in (0, 5, 77):
-                y = np.clip((x[t0:t1, h, c] / want[c]).astype(np.float32), -448, 448)
+                y = np.clip(x[t0:t1, h, c].astype(np.float64) / want[c], -448, 448)
                 for j, yy in enumerate(y.astype(np.float64)):
                     d = np.abs(fin - yy)
                     ties = fcodes[d == d.min()]
@@ -194,7 +237,7 @@ def check_v_codes_are_nearest_per_block_and_channel():
                             ties = ties[(ties & 0x80) == (0x80 if np.signbit(yy) else 0)]
                     ok &= int(codes[t0 + j, h, c]) == int(ties[0])
             m = np.abs(oracle.decode_e4m3(codes[t0:t1, h])).max(0)
-            ok &= bool(np.all((m == 448) | (amax == 0)))
+            ok &= bool(np.all(((m >= 224) & (m <= 448)) | (amax == 0)))
     return bool(ok)
 
 
@@ -213,7 +256,8 @@ def check_p_quantizer():
 CHECKS = [check_exact_inputs_quantize_exactly, check_blocked_softmax_is_plain_softmax,
           check_pipeline_is_causal_attention_up_to_p_rounding,
           check_first_token_and_zero_query_closed_forms, check_int8_codes_are_nearest_brute_force,
-          check_v_codes_are_nearest_per_block_and_channel, check_p_quantizer]
+          check_k_codes_are_nearest_per_block, check_v_codes_are_nearest_per_block_and_channel,
+          check_p_quantizer]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -232,6 +276,7 @@ def _pins_pass():
 
 
 ORIG_INT8 = prefill_ref.quantize_rows_int8
+ORIG_K = prefill_ref.quantize_k_blocks
 ORIG_V = prefill_ref.quantize_v_blocks
 ORIG_P = prefill_ref.quantize_p
 ORIG_ROW = prefill_ref.blocked_attend_row
@@ -251,6 +296,31 @@ def _mut_int8_truncate(x):
 def _mut_v_per_token(v, cu):
     codes, scales = ORIG_V(v, cu)
     return codes, np.full_like(scales, scales.mean())
+
+
+def _mut_v_scale_not_pow2(v, cu):
+    # the plain max / 448 scale in place of the power of two
+    x = prefill_ref._f32(v)
+    codes, scales = ORIG_V(v, cu)
+    blocks = prefill_ref._blocks(cu)
+    for bi, (t0, t1) in enumerate(blocks):
+        amax = np.abs(x[t0:t1]).max(0)
+        sc = np.where(amax > 0, (amax / np.float32(448)).astype(np.float32), np.float32(1))
+        scales[bi] = sc
+        codes[t0:t1] = prefill_ref.encode_e4m3(np.clip((x[t0:t1] / sc).astype(np.float32), -448, 448))
+    return codes, scales
+
+
+def _mut_k_first_token_scale(k, cu):
+    # the block's scale taken from its first token only
+    x = prefill_ref._f32(k)
+    codes, scales = ORIG_K(k, cu)
+    for bi, (t0, t1) in enumerate(prefill_ref._blocks(cu)):
+        sc = (np.abs(x[t0]).max(-1) / np.float32(127)).astype(np.float32)
+        sc = np.where(sc > 0, sc, np.float32(1))
+        scales[bi] = sc
+        codes[t0:t1] = np.clip(np.rint(x[t0:t1] / sc[None, :, None]), -127, 127).astype(np.int8)
+    return codes, scales
 
 
 def _mut_p_not_divided(p):
@@ -284,7 +354,8 @@ def _mut_first_block_only(s, values, quant_p=True, block=prefill_ref.KEY_BLOCK):
 
 @pytest.mark.parametrize("name,mutant", [
     ("quantize_rows_int8", _mut_int8_over_128), ("quantize_rows_int8", _mut_int8_truncate),
-    ("quantize_v_blocks", _mut_v_per_token), ("quantize_p", _mut_p_not_divided),
+    ("quantize_v_blocks", _mut_v_per_token), ("quantize_v_blocks", _mut_v_scale_not_pow2),
+    ("quantize_k_blocks", _mut_k_first_token_scale), ("quantize_p", _mut_p_not_divided),
     ("blocked_attend_row", _mut_no_acc_rescale), ("blocked_attend_row", _mut_lse_log2),
     ("blocked_attend_row", _mut_first_block_only)])
 def test_planted_prefill_mistakes_are_caught(monkeypatch, name, mutant):
