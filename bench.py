@@ -294,9 +294,10 @@ def prefill_counts(seqlens, H):
     """Work of one quantized causal prefill.
 
     Ops: every (query, visible key) pair of a head costs 2 * 192 (INT8 QK) +
-    2 * 128 (e4m3 PV).  Quantize bytes: bf16 Q, K, V read once; INT8 codes +
-    fp32 scales of Q and K, e4m3 V codes and per-block channel scales written.
-    Attention bytes: codes and scales read once, bf16 O and fp32 LSE written."""
+    2 * 128 (e4m3 PV).  Quantize bytes: bf16 Q, K, V read once; INT8 codes of
+    Q and K with Q's per-row and K's per-block fp32 scales, e4m3 V codes and
+    per-block channel scales written.  Attention bytes: codes and scales read
+    once, bf16 O and fp32 LSE written."""
     lens = [int(n) for n in seqlens]
     pairs = sum(n * (n + 1) // 2 for n in lens)
     T = sum(lens)
@@ -304,9 +305,10 @@ def prefill_counts(seqlens, H):
     return {
         "tokens": T, "blocks": nb, "pairs": pairs * H,
         "ops": pairs * H * 2 * (192 + 128),
-        "quant_bytes": T * H * (2 * 192 * 2 + 128 * 2) + T * H * 2 * (192 + 4)
+        "quant_bytes": T * H * (2 * 192 * 2 + 128 * 2) + T * H * (2 * 192 + 4) + nb * H * 4
         + nb * H * 128 * (128 + 4),
-        "attn_bytes": T * H * 2 * (192 + 4) + nb * H * 128 * (128 + 4) + T * H * (256 + 4),
+        "attn_bytes": T * H * (2 * 192 + 4) + nb * H * 4 + nb * H * 128 * (128 + 4)
+        + T * H * (256 + 4),
     }
 
 

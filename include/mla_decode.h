@@ -338,7 +338,7 @@ mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const v
  * cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (N_s of them), and token i of a
  * sequence sees keys 0..i of the same sequence.  For each (token, head):
  *
- *   s_j = (qc . kc_j) * q_scale * k_scale_j * softmax_scale     (INT32 exact)
+ *   s_j = (qc . kc_j) * q_scale * k_scale(block of j) * softmax_scale  (INT32 exact)
  *   keys taken in blocks of 128 from the sequence start; per block
  *     m' = max(m, max s_j),  a = e^(m - m'),  P_j = e^(s_j - m'),
  *     l = a l + sum_j P_j,   acc = a acc + sum_j e4m3(448 P_j) * vc_j * v_scale(block)
@@ -368,19 +368,23 @@ int32_t mla_prefill_num_blocks(const int32_t* seqlens, int32_t num_seqs);
  *   cu_seqlens  [S + 1] int32, device: 0 = cu[0] <= cu[1] <= ... <= cu[S] = T.
  *   q, k        [T, H, 192] bf16;  v  [T, H, 128] bf16.  Values must be finite.
  *   q_codes, k_codes  [T, H, 192] int8: code = RNE(x / s) clamped to +-127,
- *               with one scale per (token, head) row s = max|x| / 127 in fp32
- *               (1 for an all-zero row), written to q_scale / k_scale [T, H] fp32.
+ *               s = max|x| / 127 in fp32 (1 if the maximum is 0), taken over
+ *               each (token, head) row for Q (q_scale [T, H] fp32) and over
+ *               each (128-token block, head) for K (k_scale [num_blocks, H]).
  *   v_codes     [num_blocks, H, 128 channels, 128 keys] e4m3 bytes: for block
  *               b of a sequence and channel c, code = the e4m3 value nearest
- *               (ties to even) to v / s with s = max|v| / 448 over the block's
- *               tokens in channel c (1 if zero), written to
- *               v_scale [num_blocks, H, 128] fp32.  Within a (block, head,
+ *               (ties to even) to v / s, s the smallest power of two 2^e
+ *               (e >= -127) with max|v| / s <= 448 over the block's tokens in
+ *               channel c (2^0 if zero), written to v_scale [num_blocks, H, 128]
+ *               fp32 (powers of two: the fp8 matrix instruction applies them
+ *               as e8m0 scales).  Within a (block, head,
  *               channel) row of 128 bytes, key k = 16 a + 4 g + r
  *               (a < 8, g < 4, r < 4) sits at byte 32 g + 4 a + r: the order
  *               in which the PV matrix instruction takes them.  Keys past
  *               the sequence's end hold code 0.
  *
- * Quotients are correctly rounded fp32 divisions.  Errors: NULL_ARG,
+ * Q and K quotients are correctly rounded fp32 divisions; V's are exact.
+ * Errors: NULL_ARG,
  * BAD_SHAPE (negative sizes, d_qk != 192 or d_v != 128 is UNSUPPORTED),
  * MISALIGNED, HIP.  Blocks of a sequence whose cu_seqlens entries are out of
  * order or past T, or past num_blocks, are not written.  T = 0 is a no-op.

@@ -417,10 +417,10 @@ class PrefillQuant:
     """mla_prefill_quantize's outputs (torch device tensors)."""
     q_codes: object       # [T, H, 192] int8
     q_scale: object       # [T, H] fp32
-    k_codes: object
-    k_scale: object
+    k_codes: object       # [T, H, 192] int8
+    k_scale: object       # [blocks, H] fp32
     v_codes: object       # [blocks, H, 128, 128] uint8 (e4m3, PV operand key order)
-    v_scale: object       # [blocks, H, 128] fp32
+    v_scale: object       # [blocks, H, 128] fp32 powers of two
 
 
 def prefill_alloc_quant(shape: PrefillShape, device) -> PrefillQuant:
@@ -430,7 +430,7 @@ def prefill_alloc_quant(shape: PrefillShape, device) -> PrefillQuant:
         q_codes=torch.empty((T, H, PREFILL_D_QK), dtype=torch.int8, device=device),
         q_scale=torch.empty((T, H), dtype=torch.float32, device=device),
         k_codes=torch.empty((T, H, PREFILL_D_QK), dtype=torch.int8, device=device),
-        k_scale=torch.empty((T, H), dtype=torch.float32, device=device),
+        k_scale=torch.empty((nb, H), dtype=torch.float32, device=device),
         v_codes=torch.empty((nb, H, PREFILL_D_V, PREFILL_BLOCK), dtype=torch.uint8, device=device),
         v_scale=torch.empty((nb, H, PREFILL_D_V), dtype=torch.float32, device=device))
 

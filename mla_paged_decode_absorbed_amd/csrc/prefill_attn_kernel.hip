@@ -14,17 +14,18 @@
 //  * scores: S^T[16 keys x 16 queries] = K Q^T on v_mfma_i32_16x16x64_i8,
 //    3 steps over the 192 dims; Q's operands stay in registers.  In the
 //    output, lane l holds keys 4 (l / 16) + r of query l % 16;
-//  * s = S * q_scale * k_scale * softmax_scale (in log2 units), -inf for keys
-//    after the query or past the sequence; the row max takes two lane swaps
-//    (the 4 lanes of a query), the running max, sum and accumulator are
-//    rescaled by 2^(m_old - m_new);
+//  * s = S * q_scale * k_scale * softmax_scale (in log2 units; one key scale
+//    per block), -inf for keys after the query or past the sequence; the row
+//    max takes two lane swaps (the 4 lanes of a query), the running max, sum
+//    and accumulator are rescaled by 2^(m_old - m_new);
 //  * P = 2^(s - m) times 448 goes to e4m3 (hardware conversion, nearest
 //    even): the 8 score tiles of a lane are exactly the 32 keys
 //    16 a + 4 g + r the lane feeds to the PV instruction, so P never moves;
 //  * O^T[16 channels x 16 queries] += V^T P^T on
-//    v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), V^T read from LDS in
-//    the key order mla_prefill_quantize wrote, then times the channel scales
-//    of the block.
+//    v_mfma_scale_f32_16x16x128_f8f6f4, V^T read from LDS in the key order
+//    mla_prefill_quantize wrote; V's power-of-two channel scales ride along
+//    as the instruction's e8m0 scales of V^T's rows, so the product lands in
+//    the accumulators already dequantized.
 //
 // The workgroups of the last (most expensive) query blocks start first, and
 // consecutive workgroups are consecutive heads, so with H a multiple of 8
@@ -58,7 +59,7 @@ constexpr int kTilesPerWave = 1;              // 16-query tiles per wave
 // after some query (the diagonal block) or past the sequence's end.
 template <int kU, bool kMask>
 __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t* vtile,
-                                             const float* kscale, const float* vscale,
+                                             float kscale, const uint8_t* vexp,
                                              const i32x4 (&qop)[kU][3], const float (&qsc)[kU],
                                              const int (&qi)[kU], int key0, int n, int g, int col,
                                              float (&m)[kU], float (&lsum)[kU],
@@ -78,20 +79,19 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
         sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
     }
   }
-  // t = S * k_scale; with q_scale * softmax_scale * log2(e) = qsc > 0 the
-  // log2-domain score is t * qsc, so the row max is qsc * max t
+  // t = S; with the block's key scale times q_scale * softmax_scale * log2(e)
+  // = c > 0 the log2-domain score is t * c, so the row max is c * max t
   float t[kU][8][4];
   float mx[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) mx[u] = -INFINITY;
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
-    const f32x4 ksv = *reinterpret_cast<const f32x4*>(kscale + 16 * T + 4 * g);
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = float(sacc[u][T][r]) * ksv[r];
+        float v = float(sacc[u][T][r]);
         if (kMask) {
           const int key = key0 + 16 * T + 4 * g + r;
           if (!(key <= qi[u] && key < n)) v = -INFINITY;
@@ -104,9 +104,10 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
   i32x8 pop[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
+    const float c = qsc[u] * kscale;
     float mt = fmaxf(mx[u], __shfl_xor(mx[u], 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m[u], mt * qsc[u]);
+    const float mnew = fmaxf(m[u], mt * c);
     const bool none = mnew == -INFINITY;          // nothing visible yet (padding queries)
     alpha[u] = none ? 1.f : __builtin_amdgcn_exp2f(m[u] - mnew);
     // 448 P = 2^(t qsc - (m - log2 448)), straight into e4m3.  mnew rounds
@@ -120,7 +121,7 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(t[u][T][r], qsc[u], -mb));
+        p[r] = __builtin_amdgcn_exp2f(fmaf(t[u][T][r], c, -mb));
         if (kMask && t[u][T][r] == -INFINITY) p[r] = 0.f;
         ps += p[r];
       }
@@ -142,20 +143,21 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc[u][ct] *= alpha[u];
   }
-  // O^T += V^T P^T per 16-channel tile, times the block's channel scales
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // O^T += V^T P^T per 16-channel tile, straight into the accumulators: the
+  // lanes of channel row col hand the instruction that channel's e8m0 scale
+  // (its power-of-two exponent + 127), which it applies to the row of V^T
+  const uint32_t* vx = reinterpret_cast<const uint32_t*>(vexp + 8 * col);
+  const uint32_t ex[2] = {vx[0], vx[1]};
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
     const i32x4* vr = reinterpret_cast<const i32x4*>(vtile + (16 * ct + col) * kVStride + 32 * g);
     const i32x4 v0 = vr[0], v1 = vr[1];
     const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    const f32x4 vsc = *reinterpret_cast<const f32x4*>(vscale + 16 * ct + 4 * g);
+    const int sa = int((ex[ct >> 2] >> (8 * (ct & 3))) & 0xFFu);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          vop, pop[u], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
-      acc[u][ct] += c * vsc;
-    }
+    for (int u = 0; u < kU; ++u)
+      acc[u][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, pop[u], acc[u][ct], 0, 0,
+                                                                    0, sa, 0, kE8M0One);
   }
 }
 
@@ -168,7 +170,8 @@ struct BlockRegs {
   static constexpr int kV = kPfDV * 8 / kThreads;          // 16-byte V chunks per thread
   static_assert(kK * kThreads == kPfBlock * 12 && kV * kThreads == kPfDV * 8, "chunking");
   i32x4 k[kK], v[kV];
-  float sc;
+  float ks;        // the block's key scale
+  uint32_t vx;     // channel threadIdx.x's V scale as an e8m0 byte (first 128 threads)
 };
 
 template <int kThreads>
@@ -190,16 +193,16 @@ __device__ __forceinline__ void load_block(const PrefillAttnArgs& a, const PfBlo
       reinterpret_cast<const i32x4*>(a.vc + (int64_t(blk.b0 + kb) * H + h) * (kPfDV * kPfBlock));
 #pragma unroll
   for (int j = 0; j < BlockRegs<kThreads>::kV; ++j) r.v[j] = vsrc[int(threadIdx.x) + kThreads * j];
-  r.sc = 0.f;
-  if (threadIdx.x < kPfBlock)
-    r.sc = int(threadIdx.x) < nk ? a.ks[int64_t(blk.t0 + key0 + int(threadIdx.x)) * H + h] : 0.f;
-  else if (threadIdx.x < kPfBlock + kPfDV)
-    r.sc = a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x - kPfBlock];
+  r.ks = a.ks[int64_t(blk.b0 + kb) * H + h];
+  r.vx = 0u;
+  if (threadIdx.x < kPfDV)   // the e8m0 byte of a power of two 2^e is its fp32 exponent field
+    r.vx = (__float_as_uint(a.vs[(int64_t(blk.b0 + kb) * H + h) * kPfDV + threadIdx.x]) >> 23) &
+           0xFFu;
 }
 
 template <int kThreads>
 __device__ __forceinline__ void store_block(const BlockRegs<kThreads>& r, int8_t* ktile,
-                                            uint8_t* vtile, float* kscale, float* vscale) {
+                                            uint8_t* vtile, uint8_t* vexp) {
 #pragma unroll
   for (int j = 0; j < BlockRegs<kThreads>::kK; ++j) {
     const int c = int(threadIdx.x) + kThreads * j;
@@ -211,10 +214,8 @@ __device__ __forceinline__ void store_block(const BlockRegs<kThreads>& r, int8_t
     const int c = int(threadIdx.x) + kThreads * j;
     *reinterpret_cast<i32x4*>(vtile + (c >> 3) * kVStride + 16 * (c & 7)) = r.v[j];
   }
-  if (threadIdx.x < kPfBlock)
-    kscale[threadIdx.x] = r.sc;
-  else if (threadIdx.x < kPfBlock + kPfDV)
-    vscale[threadIdx.x - kPfBlock] = r.sc;
+  // channel c = 16 ct + col goes to byte 8 col + ct: a lane reads its 8 in one
+  if (threadIdx.x < kPfDV) vexp[8 * (threadIdx.x & 15) + (threadIdx.x >> 4)] = uint8_t(r.vx);
 }
 
 // kW waves of kU 16-query tiles each cover the 128 queries of a block.
@@ -224,8 +225,7 @@ __global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const Prefill
   constexpr int kThreads = kW * 64;
   __shared__ __attribute__((aligned(16))) int8_t ktile[kPfBlock * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kPfDV * kVStride];
-  __shared__ __attribute__((aligned(16))) float kscale[kPfBlock];
-  __shared__ __attribute__((aligned(16))) float vscale[kPfDV];
+  __shared__ __attribute__((aligned(16))) uint8_t vexp[kPfDV];
   const int H = a.num_heads;
   const int wi = int(blockIdx.x) / H;
   const int h = int(blockIdx.x) - wi * H;
@@ -270,15 +270,16 @@ __global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const Prefill
 
   for (int kb = 0; kb <= qb; ++kb) {
     __syncthreads();                              // the previous block's reads are done
-    store_block<kThreads>(regs, ktile, vtile, kscale, vscale);
+    store_block<kThreads>(regs, ktile, vtile, vexp);
+    const float kscale = regs.ks;
     __syncthreads();
     if (kb < qb) load_block<kThreads>(a, blk, kb + 1, h, regs);
     // blocks below the diagonal are whole and wholly visible
     if (kb < qb)
-      attend_block<kU, false>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n,
-                              g, col, m, lsum, acc);
+      attend_block<kU, false>(ktile, vtile, kscale, vexp, qop, qsc, qi, kb * kPfBlock, blk.n, g,
+                              col, m, lsum, acc);
     else
-      attend_block<kU, true>(ktile, vtile, kscale, vscale, qop, qsc, qi, kb * kPfBlock, blk.n, g,
+      attend_block<kU, true>(ktile, vtile, kscale, vexp, qop, qsc, qi, kb * kPfBlock, blk.n, g,
                              col, m, lsum, acc);
   }
 

@@ -1,23 +1,29 @@
 // Quantization for the SageAttention-style prefill (PaddlePaddle 3.0 inference
 // page, long-sequence inference): Q and K to INT8, V to FP8, on the fly.
 //
-// Q and K: one symmetric scale per (token, head) row of 192, s = max|x| / 127
-// (1 for an all-zero row), code = x / s rounded to nearest even, clamped to
+// Q: one symmetric scale per (token, head) row of 192, s = max|x| / 127 (1
+// for an all-zero row), code = x / s rounded to nearest even, clamped to
 // +-127.  Eight lanes take a row (24 values each: three 16-byte loads, three
 // 8-byte stores) and reduce its max with three lane swaps; a wave takes 8
-// rows.  Q rows come first in the row index, then K rows.
+// rows.
 //
-// V: one scale per (128-token block of a sequence, head, channel),
-// s = max|v| / 448 over the block's tokens (1 if zero), code = the e4m3 value
-// nearest to v / s (ties to even; the hardware conversion on the clamped
-// quotient, as in the cache append).  A workgroup takes one (block, head):
+// K: the same rule with one scale per (128-token block of a sequence, head),
+// the max over the block's 128 x 192 values: a workgroup takes one (block,
+// head), each thread 12 16-byte pieces, the max reduced over the wave and
+// through LDS.
+//
+// V: one power-of-two scale per (128-token block, head, channel), the
+// smallest 2^e (e >= -127) with max|v| / 2^e <= 448 (2^0 if zero), taken
+// exactly from the max's exponent and mantissa; code = the e4m3 value
+// nearest to v 2^-e (an exact product; the hardware conversion, nearest
+// even).  A workgroup takes one (block, head):
 // 16 threads cover a token's 256 bytes, 16 token groups reduce the channel
 // maxima through LDS, and the codes are laid out in LDS transposed, each
 // channel's 128 keys in the order the PV matrix instruction takes them (key
 // 16 a + 4 g + r at byte 32 g + 4 a + r), then copied out in 16-byte pieces.
 //
-// Quotients are correctly rounded fp32 divisions (the compiler's default for
-// '/').
+// Q and K quotients are correctly rounded fp32 divisions (the compiler's
+// default for '/').
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,9 +49,8 @@ __device__ __forceinline__ uint32_t int8_code(float x, float s) {
   return uint32_t(int32_t(c)) & 0xFFu;
 }
 
-__global__ __launch_bounds__(256) void mla_prefill_quant_qk_kernel(const PrefillQuantArgs a) {
-  const int64_t per_tensor = int64_t(a.num_tokens) * a.num_heads;
-  const int64_t rows = 2 * per_tensor;
+__global__ __launch_bounds__(256) void mla_prefill_quant_q_kernel(const PrefillQuantArgs a) {
+  const int64_t rows = int64_t(a.num_tokens) * a.num_heads;
   const int lane = threadIdx.x & 63, j = lane & 7;
   const int64_t stride = int64_t(gridDim.x) * kQkRowsPerBlock;
   // the loop bound is uniform over the wave, so every lane takes part in the
@@ -54,11 +59,9 @@ __global__ __launch_bounds__(256) void mla_prefill_quant_qk_kernel(const Prefill
        base += stride) {
     const int64_t r = base + (lane >> 3);
     const bool valid = r < rows;
-    const bool is_k = r >= per_tensor;
-    const int64_t rr = is_k ? r - per_tensor : r;
     u32x4 c[3] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
     if (valid) {
-      const u32x4* src = reinterpret_cast<const u32x4*>((is_k ? a.k : a.q) + rr * kPfDQK) + 3 * j;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.q + r * kPfDQK) + 3 * j;
       c[0] = src[0];
       c[1] = src[1];
       c[2] = src[2];
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void mla_prefill_quant_qk_kernel(const Prefill
     if (!valid) continue;
     float s = m / 127.f;
     if (!(s > 0.f)) s = 1.f;
-    u32x2* dst = reinterpret_cast<u32x2*>((is_k ? a.kc : a.qc) + rr * kPfDQK + 24 * j);
+    u32x2* dst = reinterpret_cast<u32x2*>(a.qc + r * kPfDQK + 24 * j);
 #pragma unroll
     for (int w = 0; w < 3; ++w) {
       u32x2 out;
@@ -86,21 +89,78 @@ __global__ __launch_bounds__(256) void mla_prefill_quant_qk_kernel(const Prefill
       }
       dst[w] = out;
     }
-    if (j == 0) (is_k ? a.ks : a.qs)[rr] = s;
+    if (j == 0) a.qs[r] = s;
   }
 }
 
-// e4m3 code of v / s: correctly rounded quotient, clamped to +-448 with the
-// sign kept, rounded by the hardware conversion (nearest, ties to even).
-__device__ __forceinline__ uint32_t e4m3_code(float x, float s) {
-  const float q = fminf(fabsf(x) / s, 448.f);
-  const float y = __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
+// K codes with one scale per (block, head): thread t takes pieces t + 256 p
+// (p < 12) of the block's 128 x 24 16-byte pieces (key = piece / 24).
+__global__ __launch_bounds__(256) void mla_prefill_quant_k_kernel(const PrefillQuantArgs a) {
+  __shared__ float wmax[4];
+  constexpr int kPieces = kPfBlock * (kPfDQK / 8) / 256;     // 12
+  const int H = a.num_heads;
+  const int i = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  PfBlock blk;
+  if (!pf_find_block(a.cu, a.num_seqs, a.num_tokens, a.num_blocks, i, &blk)) return;
+  const int key0 = blk.kb * kPfBlock;
+  const int nk = min(kPfBlock, blk.n - key0);
+  u32x4 x[kPieces];
+  float m = 0.f;
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) {
+    const int c = int(threadIdx.x) + 256 * p;
+    const int key = c / 24, part = c - key * 24;
+    x[p] = u32x4{0u, 0u, 0u, 0u};
+    if (key < nk)
+      x[p] = reinterpret_cast<const u32x4*>(a.k + (int64_t(blk.t0 + key0 + key) * H + h) *
+                                                      kPfDQK)[part];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[p][e])), fabsf(bf16_hi(x[p][e]))));
+  }
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float s = m / 127.f;
+  if (!(s > 0.f)) s = 1.f;
+  if (threadIdx.x == 0) a.ks[int64_t(i) * H + h] = s;
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) {
+    const int c = int(threadIdx.x) + 256 * p;
+    const int key = c / 24, part = c - key * 24;
+    if (key >= nk) continue;
+    u32x2 out;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t w0 = x[p][2 * w], w1 = x[p][2 * w + 1];
+      out[w] = int8_code(bf16_lo(w0), s) | (int8_code(bf16_hi(w0), s) << 8) |
+               (int8_code(bf16_lo(w1), s) << 16) | (int8_code(bf16_hi(w1), s) << 24);
+    }
+    reinterpret_cast<u32x2*>(a.kc + (int64_t(blk.t0 + key0 + key) * H + h) * kPfDQK)[part] = out;
+  }
+}
+
+// e4m3 code of v 2^-e (exact; within +-448 by the choice of e, clamped all
+// the same), rounded by the hardware conversion (nearest, ties to even).
+__device__ __forceinline__ uint32_t e4m3_code(float x, int e) {
+  const float y = fminf(fmaxf(ldexpf(x, -e), -448.f), 448.f);
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false)) & 0xFFu;
+}
+
+// Smallest e >= -127 with amax 2^-e <= 448, 0 for amax = 0: with
+// amax = f 2^E, f in [0.5, 1), 448 = 0.875 2^9 fits at E - 9 if f <= 0.875.
+__device__ __forceinline__ int pow2_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  const int e = f <= 0.875f ? E - 9 : E - 8;
+  return e < -127 ? -127 : e;
 }
 
 __global__ __launch_bounds__(256) void mla_prefill_quant_v_kernel(const PrefillQuantArgs a) {
   __shared__ float pmax[16][kPfDV];
-  __shared__ float scale[kPfDV];
+  __shared__ int expo[kPfDV];
   __shared__ __attribute__((aligned(16))) uint8_t codes[kPfDV * kPfBlock];
   const int H = a.num_heads;
   const int i = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
@@ -133,15 +193,14 @@ __global__ __launch_bounds__(256) void mla_prefill_quant_v_kernel(const PrefillQ
   if (threadIdx.x < kPfDV) {
     float m = 0.f;
     for (int r = 0; r < 16; ++r) m = fmaxf(m, pmax[r][threadIdx.x]);
-    float s = m / 448.f;
-    if (!(s > 0.f)) s = 1.f;
-    scale[threadIdx.x] = s;
-    a.vs[(int64_t(i) * H + h) * kPfDV + threadIdx.x] = s;
+    const int e = pow2_exponent(m);
+    expo[threadIdx.x] = e;
+    a.vs[(int64_t(i) * H + h) * kPfDV + threadIdx.x] = ldexpf(1.f, e);
   }
   __syncthreads();
-  float sc[8];
+  int sc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sc[e] = scale[8 * cc + e];
+  for (int e = 0; e < 8; ++e) sc[e] = expo[8 * cc + e];
   // key rg + 16 m = 16 m + 4 g + r with g = rg / 4, r = rg % 4: byte 32 g + 4 m + r
   const int pos0 = 32 * (rg >> 2) + (rg & 3);
 #pragma unroll
@@ -165,17 +224,21 @@ __global__ __launch_bounds__(256) void mla_prefill_quant_v_kernel(const PrefillQ
 }  // namespace
 
 hipError_t launch_prefill_quant(const PrefillQuantArgs& a, hipStream_t stream) {
-  const int64_t rows = 2 * int64_t(a.num_tokens) * a.num_heads;
+  const int64_t rows = int64_t(a.num_tokens) * a.num_heads;
   if (rows > 0) {
     const int blocks = int(std::min<int64_t>((rows + kQkRowsPerBlock - 1) / kQkRowsPerBlock,
                                              kMaxQkBlocks));
-    hipLaunchKernelGGL(mla_prefill_quant_qk_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(mla_prefill_quant_q_kernel, dim3(blocks), dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t vblocks = int64_t(a.num_blocks) * a.num_heads;
-  if (vblocks > 0) {
-    hipLaunchKernelGGL(mla_prefill_quant_v_kernel, dim3(unsigned(vblocks)), dim3(256), 0, stream,
+  const int64_t kvblocks = int64_t(a.num_blocks) * a.num_heads;
+  if (kvblocks > 0) {
+    hipLaunchKernelGGL(mla_prefill_quant_k_kernel, dim3(unsigned(kvblocks)), dim3(256), 0, stream,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_prefill_quant_v_kernel, dim3(unsigned(kvblocks)), dim3(256), 0, stream,
                        a);
     return hipGetLastError();
   }

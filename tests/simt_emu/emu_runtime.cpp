@@ -465,31 +465,32 @@ emu_i32x4 mfma_i8_16x16x64(emu_i32x4 a, emu_i32x4 b, emu_i32x4 c) {
   return out + c;
 }
 
-// 16x16x128 e4m3 x e4m3 (format code 0 for both operands), with block scales
-// 2^(scale - 127): lane l supplies row / column l % 16 and k-values
-// 32 (l / 16) .. + 31, byte j being k = 32 (l / 16) + j; output as above.
+// 16x16x128 e4m3 x e4m3 (format code 0 for both operands) with e8m0 block
+// scales: lane l supplies row / column l % 16 and k-values 32 (l / 16) .. + 31,
+// byte j being k = 32 (l / 16) + j; its scale byte (2^(byte - 127)) applies to
+// those 32 values of its row (A) or column (B).  Output as above.
 emu_f32x4 mfma_f8_16x16x128(emu_i32x8 a, emu_i32x8 b, emu_f32x4 c, int fmt_a, int fmt_b,
                             int scale_a, int scale_b) {
   if (fmt_a != 0 || fmt_b != 0) fail("mfma f8f6f4: only e4m3 operands are modelled");
-  struct In { emu_i32x8 a, b; };
-  const emu_f32x4 out = wave_op(In{a, b}, [](int l, auto get) {
+  struct In { emu_i32x8 a, b; int sa, sb; };
+  const emu_f32x4 out = wave_op(In{a, b, scale_a & 0xFF, scale_b & 0xFF}, [](int l, auto get) {
     emu_f32x4 d;
     const int j = l & 15;
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * (l >> 4) + r;
       double s = 0.0;
       for (int k = 0; k < 128; ++k) {
-        const emu_i32x8 av = get(i + 16 * (k >> 5)).a, bv = get(j + 16 * (k >> 5)).b;
-        const unsigned x = (uint32_t(av[(k & 31) >> 2]) >> (8 * (k & 3))) & 0xFFu;
-        const unsigned y = (uint32_t(bv[(k & 31) >> 2]) >> (8 * (k & 3))) & 0xFFu;
-        s += double(e4m3_to_f32(x)) * double(e4m3_to_f32(y));
+        const In ai = get(i + 16 * (k >> 5)), bj = get(j + 16 * (k >> 5));
+        const unsigned x = (uint32_t(ai.a[(k & 31) >> 2]) >> (8 * (k & 3))) & 0xFFu;
+        const unsigned y = (uint32_t(bj.b[(k & 31) >> 2]) >> (8 * (k & 3))) & 0xFFu;
+        s += std::ldexp(double(e4m3_to_f32(x)) * double(e4m3_to_f32(y)),
+                        (ai.sa - 127) + (bj.sb - 127));
       }
       d[r] = float(s);
     }
     return d;
   });
-  const float sc = std::ldexp(1.f, scale_a - 127) * std::ldexp(1.f, scale_b - 127);
-  return out * sc + c;
+  return out + c;
 }
 
 emu_f32x2 cvt_pk_f32_fp8(int v, bool hi) {

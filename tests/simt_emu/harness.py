@@ -149,7 +149,7 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def run_prefill(case, num_blocks: int, timeout: float = 900.0):
     """A packed prefill case (``workloads.prefill.PrefillCase``) through
     mla_prefill_quantize + mla_prefill_attn.  Returns a dict of the outputs:
-    qc, qs, kc, ks [T, H, ...], vc [blocks, H, 128, 128], vs [blocks, H, 128],
+    qc, qs, kc [T, H, ...], ks [blocks, H], vc [blocks, H, 128, 128], vs [blocks, H, 128],
     o (bf16 bits [T, H, 128]), lse [T, H]."""
     S, T, H = case.num_seqs, case.num_tokens, case.num_heads
     hdr = np.array([PREFILL_MAGIC, S, T, H, num_blocks, 0, 0, 0, 0, 0, 0, 0], dtype=np.int32)
@@ -178,7 +178,7 @@ def run_prefill(case, num_blocks: int, timeout: float = 900.0):
     take("qc", T * H * 192, np.int8, (T, H, 192))
     take("qs", T * H * 4, np.float32, (T, H))
     take("kc", T * H * 192, np.int8, (T, H, 192))
-    take("ks", T * H * 4, np.float32, (T, H))
+    take("ks", num_blocks * H * 4, np.float32, (num_blocks, H))
     take("vc", num_blocks * H * 128 * 128, np.uint8, (num_blocks, H, 128, 128))
     take("vs", num_blocks * H * 128 * 4, np.float32, (num_blocks, H, 128))
     take("o", T * H * 128 * 2, np.uint16, (T, H, 128))

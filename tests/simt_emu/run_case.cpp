@@ -37,7 +37,8 @@
 //   in.bin : int32 header[12] = {magic, S, T, H, num_blocks, 0, ...}, float
 //            softmax scale, cu_seqlens (S+1 int32), q, k (T*H*192 bf16),
 //            v (T*H*128 bf16)
-//   out.bin: q codes, q scales, k codes, k scales, v codes, v scales, O
+//   out.bin: q codes, q scales (T*H), k codes, k scales (blocks*H), v codes,
+//            v scales, O
 //            (T*H*128 bf16), LSE (T*H fp32), each at its exact size
 #include <cstdint>
 #include <cstdio>
@@ -138,7 +139,7 @@ int run_prefill(FILE* f, const int32_t* hd, const char* out_path) {
   int8_t* qc = static_cast<int8_t*>(exact_alloc(TH * 192));
   int8_t* kc = static_cast<int8_t*>(exact_alloc(TH * 192));
   float* qs = static_cast<float*>(exact_alloc(TH * 4, 4));
-  float* ks = static_cast<float*>(exact_alloc(TH * 4, 4));
+  float* ks = static_cast<float*>(exact_alloc(BH * 4, 4));
   uint8_t* vc = static_cast<uint8_t*>(exact_alloc(BH * 128 * 128));
   float* vs = static_cast<float*>(exact_alloc(BH * 128 * 4));
   void* o = exact_alloc(TH * 128 * 2);
@@ -162,7 +163,7 @@ int run_prefill(FILE* f, const int32_t* hd, const char* out_path) {
   std::fwrite(qc, 1, TH * 192, g);
   std::fwrite(qs, 1, TH * 4, g);
   std::fwrite(kc, 1, TH * 192, g);
-  std::fwrite(ks, 1, TH * 4, g);
+  std::fwrite(ks, 1, BH * 4, g);
   std::fwrite(vc, 1, BH * 128 * 128, g);
   std::fwrite(vs, 1, BH * 128 * 4, g);
   std::fwrite(o, 1, TH * 128 * 2, g);

@@ -206,7 +206,8 @@ def test_append_kernel_machine_code(append_isa):
 
 @pytest.mark.parametrize("src,kernel", [("plan_kernel.hip", "mla_plan_kernel"),
                                         ("tree_kernel.hip", "mla_tree_kernel"),
-                                        ("prefill_quant_kernel.hip", "mla_prefill_quant_qk_kernel"),
+                                        ("prefill_quant_kernel.hip", "mla_prefill_quant_q_kernel"),
+                                        ("prefill_quant_kernel.hip", "mla_prefill_quant_k_kernel"),
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_v_kernel"),
                                         ("prefill_attn_kernel.hip", "mla_prefill_attn_kernel")])
 def test_small_kernels_machine_code(tmp_path, src, kernel):
