@@ -4,12 +4,12 @@
 // and multiplied with the e4m3 V on the fp8 matrix cores, V's per-channel
 // scale taken off each block's product.
 //
-// A workgroup takes one 128-token query block of one head; each of its 8
-// waves one 16-query tile (a smaller register set per wave than two tiles,
-// so more waves share a SIMD and the compiler can hoist the LDS operand
-// reads).  Key blocks of 128 (the same blocks that carry V's scales) are
-// staged in LDS in turn, up to the diagonal, the next block's codes already
-// loading into registers while one is computed:
+// A workgroup takes 64 queries (half a 128-token query block) of one head;
+// each of its 4 waves one 16-query tile.  Two workgroups share a CU, so
+// their barrier-separated phases (staging, INT8 products, softmax, fp8
+// products) overlap.  Key blocks of 128 (the same blocks that carry the
+// scales of K and V) are staged in LDS in turn, up to the diagonal, the next
+// block's codes already loading into registers while one is computed:
 //
 //  * scores: S^T[16 keys x 16 queries] = K Q^T on v_mfma_i32_16x16x64_i8,
 //    3 steps over the 192 dims; Q's operands stay in registers.  In the
@@ -52,7 +52,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2PScale = 8.807354922057604f;   // log2(448)
 constexpr float kLnPScale = 6.104793232414985f;     // ln(448)
 constexpr int kE8M0One = 127;                 // unit block scale of the fp8 instruction
-constexpr int kWaves = 8;                     // waves per workgroup
+constexpr int kWaves = 4;                     // waves per workgroup
 constexpr int kTilesPerWave = 1;              // 16-query tiles per wave
 
 // One key block: scores, online softmax, P V.  kMask: the block holds keys
@@ -218,17 +218,23 @@ __device__ __forceinline__ void store_block(const BlockRegs<kThreads>& r, int8_t
   if (threadIdx.x < kPfDV) vexp[8 * (threadIdx.x & 15) + (threadIdx.x >> 4)] = uint8_t(r.vx);
 }
 
-// kW waves of kU 16-query tiles each cover the 128 queries of a block.
+// kW waves of kU 16-query tiles each: a workgroup covers kQ = 16 kW kU
+// queries, kSplit workgroups one 128-query block.
+// At most 256 VGPRs: two waves per SIMD, so two workgroups share a CU and
+// their load / MFMA / softmax phases overlap instead of running in lockstep.
 template <int kW, int kU>
-__global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
-  static_assert(kW * kU * 16 == kPfBlock, "a workgroup covers one query block");
+__global__ __launch_bounds__(kW * 64, 2) void mla_prefill_attn_kernel(const PrefillAttnArgs a) {
+  constexpr int kQ = 16 * kW * kU;
+  constexpr int kSplit = kPfBlock / kQ;
+  static_assert(kSplit * kQ == kPfBlock, "workgroups tile a query block");
   constexpr int kThreads = kW * 64;
   __shared__ __attribute__((aligned(16))) int8_t ktile[kPfBlock * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kPfDV * kVStride];
   __shared__ __attribute__((aligned(16))) uint8_t vexp[kPfDV];
   const int H = a.num_heads;
-  const int wi = int(blockIdx.x) / H;
-  const int h = int(blockIdx.x) - wi * H;
+  const int rest = int(blockIdx.x) / H;
+  const int h = int(blockIdx.x) - rest * H;
+  const int wi = rest / kSplit, part = rest - wi * kSplit;
   const int i = a.num_blocks - 1 - wi;          // the last blocks carry the most keys
   PfBlock blk;
   if (!pf_find_block(a.cu, a.num_seqs, a.num_tokens, a.num_blocks, i, &blk)) return;
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const Prefill
   i32x4 qop[kU][3];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    qi[u] = qb * kPfBlock + wave * 16 * kU + u * 16 + col;
+    qi[u] = qb * kPfBlock + part * kQ + wave * 16 * kU + u * 16 + col;
     qsc[u] = 0.f;
 #pragma unroll
     for (int sg = 0; sg < 3; ++sg) qop[u][sg] = i32x4{0, 0, 0, 0};
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kW * 64) void mla_prefill_attn_kernel(const Prefill
 }  // namespace
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
-  const int64_t wgs = int64_t(a.num_blocks) * a.num_heads;
+  const int64_t wgs = int64_t(a.num_blocks) * a.num_heads * (kPfBlock / (16 * kWaves * kTilesPerWave));
   if (wgs <= 0) return hipSuccess;
   if (wgs > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((mla_prefill_attn_kernel<kWaves, kTilesPerWave>), dim3(unsigned(wgs)),
