@@ -45,7 +45,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKStride = 208;                 // LDS bytes per key row (192 + 16)
+constexpr int kKStride = 224;                 // LDS bytes per key row (192 + 32: fewer bank conflicts than + 16)
 constexpr int kVStride = 144;                 // LDS bytes per channel row (128 + 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
