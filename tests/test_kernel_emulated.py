@@ -155,15 +155,10 @@ def test_emulated_restart_on_late_dominant_key():
             _check(case, out, lse)
 
 
-# ---------------------------------------------------------------- candidate kernel
-CANDIDATE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "simt_emu", "candidates",
-                         "decode_kernel_pairs.hip")
-
-
-@pytest.fixture(scope="module")
-def candidate_binary():
-    from tests.simt_emu import build as _b
-    return _b.build(decode_source=CANDIDATE, tag="pairs")
+# ---------------------------------------------------------------- 32-key kernel
+# The default plan (bf16 cache, one workgroup per 128-row block) runs
+# mla_decode_kernel_pairs; these cases stress its pair stepping: odd tile
+# counts, tails inside the second stage of a pair, drafts up to 8 tokens.
 
 
 @pytest.mark.parametrize("kv_lens,q_lens,nwg,kv_dtype,H,P", [
@@ -173,22 +168,9 @@ def candidate_binary():
     ([77, 300], [4, 1], 6, "bf16", 16, 16),
     ([77, 300], [8, 1], 6, "bf16", 16, 16),                         # longest draft
 ])
-def test_candidate_pairs_kernel_matches_oracle(candidate_binary, kv_lens, q_lens, nwg, kv_dtype,
-                                               H, P):
+def test_pair_stepping_matches_oracle(kv_lens, q_lens, nwg, kv_dtype, H, P):
     case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, kv_dtype=kv_dtype, num_heads=H,
                      page_size=P, sm_scale=1 / math.sqrt(192))
     for mode in ("wait-lockstep", "issue-drift"):
-        out, lse, meta = harness.run(case, nwg, 1, binary=candidate_binary, env_extra=MODES[mode])
+        out, lse, meta = harness.run(case, nwg, 1, env_extra=MODES[mode])
         _check(case, out, lse)
-
-
-def test_candidate_restart_and_phased_plans(candidate_binary):
-    # the restart pass of the 32-key kernel, and the library kernel it keeps
-    # for plans with several phases
-    case = _late_dominant_key_case()
-    for phases, nwg in ((1, 1), (4, 4)):
-        for mode in ("wait-lockstep", "issue-drift"):
-            out, lse, meta = harness.run(case, nwg, phases, binary=candidate_binary,
-                                         env_extra=MODES[mode])
-            assert meta["phases"] == phases
-            _check(case, out, lse)

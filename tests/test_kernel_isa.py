@@ -12,9 +12,8 @@ cross-compiles; nothing runs on a GPU).
 * The key loop of the default (bf16, one phase) kernel issues the expected
   MFMAs and LDS reads per 16-key tile.
 
-The same checks run on the candidate kernel kept with the CPU emulator
-(tests/simt_emu/candidates), whose default instantiation steps 32 keys at a
-time.
+The default plan runs mla_decode_kernel_pairs (32 keys per step); the
+checks cover it and every instantiation of the 16-key kernel.
 """
 import os
 import re
@@ -32,7 +31,6 @@ pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 
 SOURCES = {
     "library": os.path.join(CSRC, "decode_kernel.hip"),
-    "candidate": os.path.join(ROOT, "tests", "simt_emu", "candidates", "decode_kernel_pairs.hip"),
 }
 
 
@@ -138,16 +136,10 @@ def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
 def test_default_kernel_tile_work(isa):
     which, text = isa
     ks = _kernels(text)
-    if which == "library":
-        name = next(n for n in ks if "ILi0ELi1E" in n)
-        # per 16-key tile: 36 QK + 16 PV MFMAs, 18 K-fragment and 32
-        # transposing V reads
-        step_mfma, step_k, step_v = 52, 18, 32
-    else:
-        name = next(n for n in ks if "mla_decode_kernel_pairsILi0E" in n)
-        # per 32 keys: 36 QK (32x32x16) + 32 PV MFMAs, 36 K-fragment and 64
-        # transposing V reads
-        step_mfma, step_k, step_v = 68, 36, 64
+    name = next(n for n in ks if "mla_decode_kernel_pairsILi0E" in n)
+    # per 32 keys: 36 QK (32x32x16) + 32 PV MFMAs, 36 K-fragment and 64
+    # transposing V reads
+    step_mfma, step_k, step_v = 68, 36, 64
     loop = _key_loop_blocks(ks[name])
     mfma = sum(sum("v_mfma" in i for i in ins) for _, ins in loop)
     k_reads = sum(sum(i.startswith("ds_read_b128") for i in ins) for _, ins in loop)
