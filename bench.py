@@ -41,6 +41,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ("decode_kernel.hip", "gfx950_asm.h", "kernels.h", "plan_layout.h")
 DECODE_KERNEL = "mla_decode_kernel"
+# the kernel a plan launches: a bf16 cache with one workgroup per 128-row block
+# runs the 32-key kernel, every other plan the 16-key one
+PAIRS_KERNEL = "mla_decode_kernel_pairs"
+
+
+def decode_kernel_name(kv_dtype: str, phases: int) -> str:
+    return PAIRS_KERNEL if kv_dtype == "bf16" and phases == 1 else DECODE_KERNEL
 
 
 def log(msg: str) -> None:
@@ -642,7 +649,8 @@ def main() -> int:
     else:
         achieved, peak, unit, bound = cnt["flops"] / t_fwd / 1e12, MFMA_BF16_PEAK_TFLOPS, \
             "TFLOP/s", "mfma"
-    traffic = read_traffic(args.workload)
+    kernel_name = decode_kernel_name(case.kv_dtype, pl.phases)
+    traffic = read_traffic(args.workload, kernel_name)
 
     res = {
         "metric": METRIC,
@@ -676,7 +684,7 @@ def main() -> int:
             "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": None if traffic is None else round(traffic),
-            "kernel": DECODE_KERNEL,
+            "kernel": kernel_name,
             "alg_bytes_per_launch": cnt["alg_bytes"], "flops_per_launch": cnt["flops"],
         },
         "plan": {"host_us": round(plan_us, 1),
