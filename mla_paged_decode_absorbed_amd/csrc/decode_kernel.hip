@@ -668,12 +668,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-#ifndef MLA_KW5
-#define MLA_KW5 4
-#endif
-#ifndef MLA_VW5
-#define MLA_VW5 4
-#endif
 
 // One workgroup = four waves, each owning 32 query rows of a 128-row block;
 // all four read every key tile.  Keys are processed in pairs of 16-key ring
@@ -681,7 +675,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 // a whole score row in the lane pair {l, l^32} (16 keys each), so the row
 // max is one lane swap and the probabilities are the B operand of the PV
 // step with no permute (the PV contraction takes the keys in the order the
-// score layout holds them; V^T is read in the same order).
+// score layout holds them; V^T is read in the same order).  bf16 caches only:
+// with e4m3 widening in the loop this schedule no longer fits the registers.
 template <int KVD>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_pairs(
     const DecodeArgs a, const int32_t* __restrict__ plan, const uint8_t* __restrict__ qg,
@@ -689,10 +684,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_pairs(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_lens,
     const int32_t* __restrict__ q_lens, uint8_t* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
+  static_assert(KVD == 0, "the 32-key kernel takes bf16 caches");
   using C = Cfg<KVD>;
   constexpr int NR = kRounds<KVD>;
-  constexpr int KW = MLA_KW5;
-  constexpr int VW = MLA_VW5;
+  constexpr int KW = 4;   // K fragments in flight in the QK step
+  constexpr int VW = 4;   // V fragments in flight in the PV step
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const uint32_t smem_base = lds_address(smem);
 
@@ -721,23 +717,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_pairs(
   // stage s), column block cb: column 32cb + l32 and, for hl = 0, keys
   // 0..3 and 8..11 of the stage, for hl = 1 keys 4..7 and 12..15.
   int kb_e, kb_o, vb1, vb2;
-  if constexpr (KVD == 0) {
+  {
     const int rl = l32 & 15, rh = rl >> 3, r8 = rl & 7, sp = l32 >> 4;
     kb_e = sp * C::TILE + rh * 1024 + (8 * (hl ^ rh) + r8) * 16;
     kb_o = sp * C::TILE + rh * 1024 + (8 * (hl ^ rh) + (r8 ^ 4)) * 16;
     const int i = l16, G = g4 & 1, u = (i >> 1) & 1, rr = 4 * hl + (i >> 2);
     vb1 = (16 * G + 8 * u + (rr ^ (4 * G))) * 16 + 8 * (i & 1);
     vb2 = 1024 + (16 * G + 8 * (u ^ 1) + (rr ^ (4 * G))) * 16 + 8 * (i & 1);
-  } else {
-    const int rl = l32 & 15, sp = l32 >> 4;
-    kb_e = sp * C::TILE + rl * 16 + 8 * hl;
-    kb_o = sp * C::TILE + (rl ^ 8) * 16 + 8 * hl;
-    const int i = l16, G = g4 & 1, k = i >> 1;
-    const int key = (k & 3) + 4 * hl + 8 * (k >> 2);
-    vb1 = (16 * G + (key ^ (8 * G))) * 16 + 8 * (i & 1);
-    vb2 = 0;
   }
-  constexpr int KSTEP = KVD == 0 ? 2048 : 1024;   // 4 QK steps (64 dims) of a key row
+  constexpr int KSTEP = 2048;   // 4 QK steps (64 dims) of a key row
   volatile LDS_PTR(int) restart_flag = (volatile LDS_PTR(int))(smem + kFlagOff);
 
   for (int it = it_begin; it < it_end; ++it) {
@@ -818,40 +806,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_pairs(
           // ---- S^T = K . Q^T over 36 steps of 16 dims
           f32x16 S = f32x16{};
           {
-            typedef typename std::conditional<KVD == 0, bf16x8, i32x2>::type KFrag;
-            auto kload = [&](int c) -> KFrag {
+            auto kload = [&](int c) -> bf16x8 {
               const int o = ((c & 1) ? kb_o : kb_e) + (c >> 2) * KSTEP + (c & 3) * 256;
-              return *(const LDS_PTR(KFrag))(st + o);
+              return *(const LDS_PTR(bf16x8))(st + o);
             };
-            KFrag kb[KW];
+            bf16x8 kb[KW];
 #pragma unroll
             for (int c = 0; c < KW - 1; ++c) kb[c] = kload(c);
 #pragma unroll
             for (int c = 0; c < 36; ++c) {
               if (c + KW - 1 < 36) kb[(c + KW - 1) % KW] = kload(c + KW - 1);
-              if constexpr (KVD == 0)
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[c % KW], qf[c], S, 0, 0, 0);
-              else
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(kb[c % KW]), qf[c],
-                                                            S, 0, 0, 0);
+              S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[c % KW], qf[c], S, 0, 0, 0);
             }
           }
 
           // ---- online softmax over keys kp + 8(r/4) + 4hl + r%4 (r = 0..15)
           float s[16];
-          if constexpr (KVD == 1) {
-            const char* sp = smem + kScaleOff + wave * (kRounds<1> * kScaleSlotBytes) +
-                             (j % NR) * kScaleSlotBytes + (32 * pp + 4 * hl) * 4;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 ks = *(const LDS_PTR(f32x4))(sp + 32 * q);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) s[4 * q + e] = S[4 * q + e] * (a.scale_log2 * ks[e]);
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = S[r] * a.scale_log2;
-          }
+          for (int r = 0; r < 16; ++r) s[r] = S[r] * a.scale_log2;
           if (kp + 2 * kTileTok > lim_all) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -877,50 +849,31 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_pairs(
             p[r] = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m);
             l += p[r];
           }
-          if constexpr (KVD == 1) {
-            const char* sp = smem + kScaleOff + wave * (kRounds<1> * kScaleSlotBytes) +
-                             (j % NR) * kScaleSlotBytes + (32 * pp + 4 * hl) * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 ks = *(const LDS_PTR(f32x4))(sp + 32 * q);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) p[4 * q + e] *= ks[e];
-            }
-          }
           bf16x8 pf[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)p[r];
 
           // ---- O^T[512 x 32] += V^T . P^T: 2 key steps x 16 column blocks
           {
-            typedef typename std::conditional<KVD == 0, bf16x8, i32x2>::type VFrag;
-            auto vload = [&](int n) -> VFrag {   // n = 16 * step + cb
+            auto vload = [&](int n) -> bf16x8 {   // n = 16 * step + cb
               const int sidx = n >> 4, cb = n & 15;
               const char* sb = st + sidx * C::TILE;
-              if constexpr (KVD == 0) {
-                const int o = 2048 * (cb >> 1) + 512 * (cb & 1);
-                const bf16x4 lo =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(sb + vb1 + o));
-                const bf16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(sb + vb2 + o));
-                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-              } else {
-                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2))(sb + vb1 + 512 * cb));
-              }
+              const int o = 2048 * (cb >> 1) + 512 * (cb & 1);
+              const bf16x4 lo =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(sb + vb1 + o));
+              const bf16x4 hi =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(sb + vb2 + o));
+              return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             };
-            VFrag vf[VW];
+            bf16x8 vf[VW];
 #pragma unroll
             for (int n = 0; n < VW - 1; ++n) vf[n] = vload(n);
 #pragma unroll
             for (int n = 0; n < 32; ++n) {
               if (n + VW - 1 < 32) vf[(n + VW - 1) % VW] = vload(n + VW - 1);
               const int cb = n & 15;
-              if constexpr (KVD == 0)
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n % VW], pf[n >> 4], acc[cb],
-                                                                  0, 0, 0);
-              else
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(vf[n % VW]),
-                                                                  pf[n >> 4], acc[cb], 0, 0, 0);
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n % VW], pf[n >> 4], acc[cb],
+                                                                0, 0, 0);
             }
           }
         }
