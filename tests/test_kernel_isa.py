@@ -8,7 +8,8 @@ cross-compiles; nothing runs on a GPU).
 * Every HBM->LDS copy (global_load_lds) reads its scalar base no sooner than
   five wait states after a VALU instruction wrote it (the CDNA rule for a
   VALU-written SGPR read by a vector-memory instruction; the compiler cannot
-  enforce it across the kernel's inline assembly).
+  enforce it across the kernel's inline assembly), on every control-flow
+  path into the copy.
 * The key loop of the default (bf16, one phase) kernel issues the expected
   MFMAs and LDS reads per 16-key tile.
 
@@ -112,25 +113,83 @@ def _sgprs(tok):
     return {int(m.group(1))} if m else set()
 
 
+def _predecessors(blocks):
+    """Control-flow predecessors of every block: the block before it (unless
+    that one ends in an unconditional branch) and every block branching to it."""
+    index = {lab: k for k, (lab, _) in enumerate(blocks)}
+    preds = {k: [] for k in range(len(blocks))}
+    for k, (_, ins) in enumerate(blocks):
+        for i in ins:
+            m = re.match(r"s_(?:c)?branch\S*\s+(\.LBB\S+)", i)
+            if m and m.group(1) in index:
+                preds[index[m.group(1)]].append(k)
+        last = ins[-1] if ins else ""
+        if k + 1 < len(blocks) and not last.startswith("s_branch"):
+            preds[k + 1].append(k)
+    return preds
+
+
+def _wait_states(i):
+    op = i.split()[0]
+    return int(i.split()[1]) + 1 if op == "s_nop" else 1
+
+
 def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
+    """Walks back from every copy over all control-flow paths (through
+    branches and fall-throughs), not only inside the copy's own block."""
     for name, blocks in _kernels(isa[1]).items():
-        for lab, ins in blocks:
-            for k, i in enumerate(ins):
+        preds = _predecessors(blocks)
+
+        def walk(k, end, used, ws, depth):
+            lab, ins = blocks[k]
+            for j in range(end - 1, -1, -1):
+                if ws >= 5:
+                    return
+                p = ins[j]
+                if p.split()[0].startswith("v_") and " " in p:
+                    dst = p.split(None, 1)[1].split(",")[0].strip()
+                    assert not (_sgprs(dst) & used), f"{name} {lab}: {p} reaches a copy"
+                ws += _wait_states(p)
+            if ws < 5 and depth < 8:
+                for q in preds[k]:
+                    walk(q, len(blocks[q][1]), used, ws, depth + 1)
+
+        copies = 0
+        for k, (lab, ins) in enumerate(blocks):
+            for j, i in enumerate(ins):
                 if not i.startswith("global_load_lds"):
                     continue
+                copies += 1
                 used = set()
                 for tok in i.split(None, 1)[1].split(","):
                     used |= _sgprs(tok.strip().split()[0])
-                ws = 0
-                for j in range(k - 1, max(-1, k - 12), -1):
-                    if ws >= 5:
-                        break
-                    p = ins[j]
-                    op = p.split()[0]
-                    if op.startswith("v_") and " " in p:
-                        dst = p.split(None, 1)[1].split(",")[0].strip()
-                        assert not (_sgprs(dst) & used), f"{name} {lab}: {p} -> {i}"
-                    ws += int(p.split()[1]) + 1 if op == "s_nop" else 1
+                walk(k, j, used, 0, 0)
+        assert copies > 0, name
+
+
+def test_hazard_walk_follows_branches():
+    """The walk above sees a VALU write to a copy's base in another block."""
+    blocks = [("entry", ["v_readfirstlane_b32 s4, v1", "s_cbranch_scc1 .LBB0_2"]),
+              (".LBB0_1", ["s_nop 7"]),
+              (".LBB0_2", ["s_mov_b32 m0, s6", "global_load_lds_dwordx4 v2, s[4:5] offset:0"])]
+    preds = _predecessors(blocks)
+    assert sorted(preds[2]) == [0, 1]
+    found = []
+
+    def walk(k, end, ws):
+        for j in range(end - 1, -1, -1):
+            if ws >= 5:
+                return
+            p = blocks[k][1][j]
+            if p.startswith("v_readfirstlane_b32 s4"):
+                found.append(k)
+            ws += _wait_states(p)
+        if ws < 5:
+            for q in preds[k]:
+                walk(q, len(blocks[q][1]), ws)
+
+    walk(2, 1, 0)
+    assert found == [0]   # through the branch, not through the s_nop 7 path
 
 
 def test_default_kernel_tile_work(isa):
