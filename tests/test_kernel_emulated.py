@@ -67,6 +67,10 @@ CASES = [
     ([700, 130], [2, 2], 8, 2, "bf16"),                             # pairs of workgroups, splits
     ([900, 70], [1, 2], 16, 4, "fp8_e4m3"),                         # e4m3 cache with scales
     ([0, 200, 64], [0, 2, 1], 5, 1, "bf16"),                        # empty sequence without query
+    # one workgroup running one-round items back to back (direct output, then
+    # a longer sequence), for both kernels of the default plan
+    ([64, 64, 130, 18], [1, 1, 1, 1], 1, 1, "fp8_e4m3"),
+    ([64, 64, 130, 18], [1, 1, 1, 1], 1, 1, "bf16"),
 ]
 
 
