@@ -445,6 +445,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time mla_decode_fwd + mla_combine replayed from HIP graphs "
                          "captured with a fixed-shape plan (us_per_call_graph)")
+    ap.add_argument("--num-workgroups", type=int, default=0,
+                    help="plan the decode for this many workgroups instead of one per CU "
+                         "(per-CU throughput against the number of CUs at work)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")
@@ -500,11 +503,13 @@ def main() -> int:
     shape = mla.Shape.make(batch=case.batch, num_heads=case.num_heads, max_q_len=case.max_q_len,
                            page_size=case.page_size, num_pages=case.num_pages,
                            max_pages_per_seq=case.max_pages, kv_dtype=kvd, causal=case.causal)
+    nwg = args.num_workgroups if args.num_workgroups > 0 else None
     t0 = time.perf_counter()
     for _ in range(20):
-        pl = mla.plan(shape, case.kv_lens, case.q_lens, device=dev, upload=False)
+        pl = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=nwg, device=dev,
+                      upload=False)
     plan_us = (time.perf_counter() - t0) / 20 * 1e6
-    pl = mla.plan(shape, case.kv_lens, case.q_lens, device=dev)
+    pl = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=nwg, device=dev)
 
     # input sets: enough copies that consecutive steps miss the Infinity Cache
     kv_np = case.kv.view(np.int16) if case.kv_dtype == "bf16" else case.kv
