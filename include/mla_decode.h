@@ -250,6 +250,65 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info,
                        void* o, float* lse, mla_stream_t stream);
 
 /*
+ * Debug validation of the device-resident inputs mla_decode_fwd and
+ * mla_combine take on trust (a checked mode for callers that assemble block
+ * tables, lengths and plans on the device, or replay a captured launch with a
+ * plan image of their own).  Nothing here is needed on the fast path; the
+ * Python binding runs it before every decode when MLA_DEBUG_CHECK=1.
+ *
+ * The decode kernels read pages through the block table (the page layout of
+ * the FlashAttention-3 in DeepSeek-R1 page, section 4.1) and key ranges from
+ * the split-K plan (same page, chapter 2) without checking them: a plan built
+ * for other lengths (a stale image after the lengths changed) or a page id
+ * outside the pool makes them read outside the cache.  This call checks, on
+ * the device and in one workgroup, with every read bounded by sizes it has
+ * already checked:
+ *
+ *   MLA_CHECK_PLAN         the image's header matches *info (magic, version,
+ *                          workgroups, phases, partials within the workspace
+ *                          layout) and its tables fit info->plan_bytes; the
+ *                          workgroup item ranges are ordered and cover the items;
+ *   MLA_CHECK_LENGTHS      every kv_lens[b], q_lens[b] passes the planner's
+ *                          checks (0 <= q_b <= max_q_len, 0 <= L_b <=
+ *                          max_pages_per_seq * page_size, causal: L_b >= q_b
+ *                          when q_b > 0);
+ *   MLA_CHECK_BLOCK_TABLE  block_table[b][j] is in [0, num_pages) for every
+ *                          page j < ceil(L_b / page_size) a sequence uses;
+ *   MLA_CHECK_ITEM         every work item names a sequence of the batch, keys
+ *                          0 <= k0 <= k1 <= L_b with k0 on a 64-key boundary,
+ *                          a first row below q_b * H and a partial slot the
+ *                          plan has; and the items together cover every
+ *                          (key, query row) pair of the lengths exactly as
+ *                          often as a plan for them does (index = the item
+ *                          count).  A stale plan fails here;
+ *   MLA_CHECK_COMBINE      every combine entry names rows that exist and
+ *                          partial slots the plan has.
+ *
+ *   err   int32[2] device (4-byte aligned): receives the lowest failing check
+ *         code (MLA_CHECK_OK = 0 if all pass) and the index it concerns (the
+ *         sequence for LENGTHS and BLOCK_TABLE, the item or combine entry, the
+ *         workgroup for a broken item range; saturated at 2^24 - 1).  Written
+ *         stream-ordered; the caller reads it after the stream passes it.
+ *
+ * Other arguments as for mla_decode_fwd (plan_dev holds info->plan_bytes
+ * bytes).  Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, BAD_PLAN (the
+ * info itself is inconsistent with the shape), HIP.
+ */
+typedef enum mla_check_code {
+  MLA_CHECK_OK = 0,
+  MLA_CHECK_PLAN = 1,
+  MLA_CHECK_LENGTHS = 2,
+  MLA_CHECK_BLOCK_TABLE = 3,
+  MLA_CHECK_ITEM = 4,
+  MLA_CHECK_COMBINE = 5
+} mla_check_code;
+
+mla_status mla_decode_check(const mla_shape* shape, const mla_plan_info* info,
+                            const void* plan_dev, const int32_t* block_table,
+                            const int32_t* kv_lens, const int32_t* q_lens, int32_t* err,
+                            mla_stream_t stream);
+
+/*
  * Tree-shaped drafts: the draft tokens' part of the attention, merged into
  * the result of a decode over the cached prefix.
  *

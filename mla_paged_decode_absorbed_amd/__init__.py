@@ -23,8 +23,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "Shape", "PlanInfo", "Plan", "MLAError", "load_library", "plan", "plan_device", "decode_fwd",
-    "combine", "tree_attend", "decode_tree",
+    "Shape", "PlanInfo", "Plan", "MLAError", "MLAInputError", "load_library", "plan",
+    "plan_device", "decode_fwd", "combine", "check", "tree_attend", "decode_tree",
     "decode", "kv_append", "status_string", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH",
 ]
 
@@ -40,8 +40,11 @@ EXPORTED_SYMBOLS = (
     "mla_workspace_bytes_bound", "mla_device_num_cus", "mla_decode_plan",
     "mla_decode_fwd", "mla_combine", "mla_kv_append", "mla_decode_plan_fixed",
     "mla_decode_plan_device", "mla_tree_attend", "mla_prefill_num_blocks",
-    "mla_prefill_quantize", "mla_prefill_attn",
+    "mla_prefill_quantize", "mla_prefill_attn", "mla_decode_check",
 )
+# codes of mla_decode_check (mla_check_code)
+CHECK_NAMES = {0: "ok", 1: "plan image", 2: "device lengths", 3: "block-table entry",
+               4: "work item", 5: "combine entry"}
 PREFILL_D_QK = 192
 PREFILL_D_V = 128
 PREFILL_BLOCK = 128
@@ -51,6 +54,14 @@ class MLAError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class MLAInputError(ValueError):
+    """A device-resident input failed mla_decode_check (MLA_DEBUG_CHECK=1)."""
+
+    def __init__(self, code: int, index: int):
+        self.code, self.index = code, index
+        super().__init__(f"mla_decode_check: bad {CHECK_NAMES.get(code, code)} (index {index})")
 
 
 class Shape(ctypes.Structure):
@@ -132,6 +143,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_fwd.argtypes = [sp, ip, P, P, P, P, P, P, P, F32, P, P, P, U64, P]
     lib.mla_combine.restype = I32
     lib.mla_combine.argtypes = [sp, ip, P, P, U64, P, P, P, P]
+    lib.mla_decode_check.restype = I32
+    lib.mla_decode_check.argtypes = [sp, ip, P, P, P, P, P, P]
     lib.mla_kv_append.restype = I32
     lib.mla_kv_append.argtypes = [sp, I32, P, P, P, P, P, P, P, P]
     pp = ctypes.POINTER(PrefillShape)
@@ -290,6 +303,35 @@ def combine(shape: Shape, pl: Plan, workspace, q_lens, out, lse, stream=None):
     _check(st, "mla_combine")
 
 
+def check(shape: Shape, pl: Plan, block_table, kv_lens, q_lens=None, err=None, stream=None,
+          wait: bool = True):
+    """Validate the device-resident inputs of a decode (``mla_decode_check``):
+    the plan image against the device lengths, the lengths, and the
+    block-table entries in use.  Returns (code, index), code 0 when all pass
+    (names in CHECK_NAMES).  ``err`` (two int32 on the device) is reused when
+    given; with ``wait=False`` nothing is synchronised and the codes stay in
+    ``err``."""
+    import torch
+    lib = load_library()
+    dev = kv_lens.device
+    if err is None:
+        err = torch.empty(2, dtype=torch.int32, device=dev)
+    if err.dtype != torch.int32 or err.numel() < 2 or not err.is_contiguous():
+        raise ValueError("err must be a contiguous int32 tensor of two elements")
+    st = lib.mla_decode_check(ctypes.byref(shape), ctypes.byref(pl.info), _ptr(pl.device),
+                              _ptr(block_table), _ptr(kv_lens), _ptr(q_lens), _ptr(err),
+                              _stream(stream))
+    _check(st, "mla_decode_check")
+    if not wait:
+        return None
+    got = err.cpu().tolist()   # waits for the stream
+    return int(got[0]), int(got[1])
+
+
+def debug_check_enabled() -> bool:
+    return os.environ.get("MLA_DEBUG_CHECK", "0") not in ("", "0")
+
+
 def alloc_workspace(pl: Plan, device="cuda"):
     import torch
     n = max(1, (pl.workspace_bytes + 255) // 256 * 256)
@@ -302,7 +344,9 @@ def decode(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm
 
     q [B, q_max, H, 576] bf16; kv_cache [pages, P, 576] bf16 (or uint8 e4m3 with
     kv_scale [pages, P] fp32); block_table [B, max_pages] int32; kv_lens / q_lens
-    [B] int32 on the device.  Returns (out [B, q_max, H, 512] bf16, lse fp32)."""
+    [B] int32 on the device.  Returns (out [B, q_max, H, 512] bf16, lse fp32).
+    With MLA_DEBUG_CHECK=1 the device inputs first pass ``check`` (one small
+    kernel and a wait); a failure raises MLAInputError before any decode work."""
     import torch
     B, qmax, H = shape.batch, shape.max_q_len, shape.num_heads
     dev = q.device
@@ -319,6 +363,12 @@ def decode(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm
         lse = torch.empty((B, qmax, H), dtype=torch.float32, device=dev)
     if workspace is None and pl.info.num_partials > 0:
         workspace = alloc_workspace(pl, dev)
+    if debug_check_enabled():
+        # checked mode: the device inputs are validated first, and a bad one
+        # raises here instead of reaching the kernels
+        code, index = check(shape, pl, block_table, kv_lens, q_lens, stream=stream)
+        if code:
+            raise MLAInputError(code, index)
     decode_fwd(shape, pl, q, kv_cache, block_table, kv_lens, q_lens, sm_scale, out, lse,
                workspace, kv_scale=kv_scale, stream=stream)
     combine(shape, pl, workspace, q_lens, out, lse, stream=stream)

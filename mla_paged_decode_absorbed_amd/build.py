@@ -21,7 +21,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "plan.cpp", "decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
            "plan_kernel.hip", "tree_kernel.hip", "prefill_quant_kernel.hip",
-           "prefill_attn_kernel.hip"]
+           "prefill_attn_kernel.hip", "check_kernel.hip"]
 ARCH = "gfx950"
 
 

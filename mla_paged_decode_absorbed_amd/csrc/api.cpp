@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "append.h"
+#include "check.h"
 #include "kernels.h"
 #include "mla_decode.h"
 #include "plan_device.h"
@@ -186,6 +187,42 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   return launch_decode(a, shape->kv_dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_check(const mla_shape* shape, const mla_plan_info* info,
+                            const void* plan_dev, const int32_t* block_table,
+                            const int32_t* kv_lens, const int32_t* q_lens, int32_t* err,
+                            mla_stream_t stream) {
+  mla_status st = validate_shape(shape);
+  if (st != MLA_OK) return st;
+  st = check_info(shape, info);
+  if (st != MLA_OK) return st;
+  if (!plan_dev || !err || (shape->batch > 0 && (!block_table || !kv_lens)))
+    return MLA_ERR_NULL_ARG;
+  if (!aligned16(plan_dev) || (reinterpret_cast<uintptr_t>(err) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3u) || (reinterpret_cast<uintptr_t>(q_lens) & 3u))
+    return MLA_ERR_MISALIGNED;
+  if (info->plan_bytes < uint64_t(kHeaderWords) * sizeof(int32_t)) return MLA_ERR_BAD_PLAN;
+  CheckArgs a{};
+  a.plan = static_cast<const int32_t*>(plan_dev);
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.q_lens = q_lens;
+  a.err = err;
+  a.plan_words = int64_t(info->plan_bytes / sizeof(int32_t));
+  a.batch = shape->batch;
+  a.num_heads = shape->num_heads;
+  a.max_q_len = shape->max_q_len;
+  a.causal = shape->causal;
+  a.page_size = shape->page_size;
+  a.num_pages = shape->num_pages;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_wg = info->num_workgroups;
+  a.phases = info->phases;
+  a.num_partials = info->num_partials;
+  return launch_check(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
+                                                                                : MLA_ERR_HIP;
 }
 
 mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info, const void* plan_dev,

@@ -21,7 +21,8 @@ BIN = os.path.join(OUT, "run_case")
 KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
                 "plan_kernel.hip", "tree_kernel.hip", "api.cpp", "plan.cpp", "kernels.h",
                 "append.h", "plan_core.h", "plan_device.h", "tree.h", "plan_layout.h",
-                "validate.h", "prefill.h", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip"]
+                "validate.h", "prefill.h", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip",
+                "check.h", "check_kernel.hip"]
 
 
 def compiler() -> str:
@@ -31,9 +32,12 @@ def compiler() -> str:
     raise RuntimeError("clang++ not found")
 
 
-def build(sanitize: bool = True, decode_source: str | None = None, tag: str = "") -> str:
+def build(sanitize: bool = True, decode_source: str | None = None, tag: str = "",
+          patches: dict | None = None) -> str:
     """Build the emulator binary.  ``decode_source`` replaces the library's
-    decode_kernel.hip (a candidate kernel); ``tag`` names that binary."""
+    decode_kernel.hip (a candidate kernel); ``patches`` maps a copied source
+    file to (old, new) text replacements, each of which must apply (a variant
+    of the library, built on the CPU only); ``tag`` names that binary."""
     out = os.path.join(OUT, tag) if tag else OUT
     src = os.path.join(out, "src")
     os.makedirs(src, exist_ok=True)
@@ -41,6 +45,15 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
         shutil.copyfile(os.path.join(CSRC, f), os.path.join(src, f))
     if decode_source:
         shutil.copyfile(decode_source, os.path.join(src, "decode_kernel.hip"))
+    for fname, reps in (patches or {}).items():
+        path = os.path.join(src, fname)
+        text = open(path).read()
+        for old, new in reps:
+            if text.count(old) != 1:
+                raise RuntimeError(f"patch for {fname} does not apply once: {old!r}")
+            text = text.replace(old, new)
+        with open(path, "w") as fh:
+            fh.write(text)
     shutil.copyfile(os.path.join(HERE, "gfx950_asm.h"), os.path.join(src, "gfx950_asm.h"))
     flags = ["-std=c++20", "-O1", "-g", "-pthread", "-fno-omit-frame-pointer",
              f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument", "-Wno-psabi"]
@@ -49,7 +62,8 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
     units = [os.path.join(src, f) for f in ("decode_kernel.hip", "combine_kernel.hip",
                                              "append_kernel.hip", "plan_kernel.hip",
                                              "tree_kernel.hip", "prefill_quant_kernel.hip",
-                                             "prefill_attn_kernel.hip", "api.cpp", "plan.cpp")]
+                                             "prefill_attn_kernel.hip", "check_kernel.hip",
+                                             "api.cpp", "plan.cpp")]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     objs = []
     for u in units:

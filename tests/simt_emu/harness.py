@@ -34,10 +34,11 @@ def _stale() -> bool:
 
 def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
         env_extra: dict | None = None, binary: str | None = None, fixed: bool = False,
-        tree_mask=None):
+        tree_mask=None, want_plan: bool = False):
     """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta).
     ``fixed`` plans with mla_decode_plan_fixed (launch bounds, padded plan);
-    ``tree_mask`` [B, qmax] runs the tree-draft path (prefix decode + merge)."""
+    ``tree_mask`` [B, qmax] runs the tree-draft path (prefix decode + merge);
+    ``want_plan`` adds the plan image the kernels ran (int32 words) to meta."""
     B, H, qmax = case.batch, case.num_heads, case.max_q_len
     kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
     magic = MAGIC if tree_mask is None else TREE_MAGIC
@@ -63,6 +64,9 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
             env["MLA_PHASES"] = str(phases)
         if env_extra:
             env.update(env_extra)
+        fplan = os.path.join(d, "plan.bin")
+        if want_plan:
+            env["EMU_PLAN_OUT"] = fplan
         res = subprocess.run([binary or ensure_built(), fin, fout], capture_output=True, text=True,
                              timeout=timeout, env=env)
         if os.environ.get("EMU_SHOW"):
@@ -70,12 +74,16 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
         if res.returncode != 0:
             raise RuntimeError(f"emulated run failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
         raw = np.fromfile(fout, dtype=np.uint8)
+        plan = np.fromfile(fplan, dtype=np.int32) if want_plan else None
     meta = raw[:16].view(np.int32).copy()
     n_o = B * qmax * H * 512 * 2
     out = raw[16:16 + n_o].view(np.uint16).reshape(B, qmax, H, 512)
     lse = raw[16 + n_o:].view(np.float32).reshape(B, qmax, H)
-    return out, lse, {"num_items": int(meta[0]), "num_partials": int(meta[1]),
-                      "num_combine": int(meta[2]), "phases": int(meta[3])}
+    info = {"num_items": int(meta[0]), "num_partials": int(meta[1]),
+            "num_combine": int(meta[2]), "phases": int(meta[3])}
+    if want_plan:
+        info["plan"] = plan
+    return out, lse, info
 
 
 def run_append(kv, kv_scale, block_table, kv_lens, new_lens, new_rows_bits, page_size: int,
@@ -115,6 +123,52 @@ def run_append(kv, kv_scale, block_table, kv_lens, new_lens, new_rows_bits, page
 
 
 PLAN_MAGIC = 0x4D4C4150
+CHECK_MAGIC = 0x4D4C4143
+
+
+def run_check(case, num_workgroups: int, plan_kv_lens=None, plan_q_lens=None, kv_lens=None,
+              q_lens=None, block_table=None, pokes=(), phases: int | None = None,
+              timeout: float = 600.0, want_plan: bool = False):
+    """mla_decode_plan from (plan_kv_lens, plan_q_lens) (default: the case's),
+    then mla_decode_check against the device lengths and block table (default:
+    the case's), with (word, value) pokes applied to the plan image.  Returns
+    (call status, check code, index), and the plan image before the pokes
+    (int32 words) as a fourth element with ``want_plan``."""
+    B = case.batch
+    has_ql = case.q_lens is not None
+    kvd = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
+    hdr = np.array([CHECK_MAGIC, B, case.num_heads, case.max_q_len, case.page_size,
+                    case.num_pages, case.max_pages, kvd, int(case.causal), num_workgroups,
+                    int(has_ql), len(pokes)], dtype=np.int32)
+    pick = lambda x, d: np.ascontiguousarray(d if x is None else x, dtype=np.int32)  # noqa: E731
+    with tempfile.TemporaryDirectory() as d:
+        fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
+        with open(fin, "wb") as f:
+            f.write(hdr.tobytes())
+            f.write(pick(plan_kv_lens, case.kv_lens).tobytes())
+            if has_ql:
+                f.write(pick(plan_q_lens, case.q_lens).tobytes())
+            f.write(pick(kv_lens, case.kv_lens).tobytes())
+            if has_ql:
+                f.write(pick(q_lens, case.q_lens).tobytes())
+            f.write(pick(block_table, case.block_table).tobytes())
+            f.write(np.asarray(pokes, dtype=np.int32).reshape(-1).tobytes())
+        env = dict(os.environ)
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+        if phases is not None:
+            env["MLA_PHASES"] = str(phases)
+        fplan = os.path.join(d, "plan.bin")
+        if want_plan:
+            env["EMU_PLAN_OUT"] = fplan
+        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+                             timeout=timeout, env=env)
+        if res.returncode != 0:
+            raise RuntimeError(f"emulated check failed (rc {res.returncode}):\n{res.stderr[-6000:]}")
+        raw = np.fromfile(fout, dtype=np.int32)
+        res3 = (int(raw[0]), int(raw[1]), int(raw[2]))
+        if want_plan:
+            return res3 + (np.fromfile(fplan, dtype=np.int32),)
+    return res3
 
 
 def run_plan_device(batch, num_heads, max_q_len, page_size, num_pages, max_pages, causal,

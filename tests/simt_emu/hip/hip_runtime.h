@@ -128,5 +128,15 @@ inline hipError_t hipMemcpyToSymbol(const void* sym, const void* src, size_t n) 
 inline unsigned __float_as_uint(float x) { return __builtin_bit_cast(unsigned, x); }
 inline float __uint_as_float(unsigned x) { return __builtin_bit_cast(float, x); }
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_RELAXED); }
+inline unsigned long long atomicAdd(unsigned long long* p, unsigned long long v) {
+  const unsigned long long old = *p;
+  *p = old + v;
+  return old;
+}
+inline int atomicMin(int* p, int v) {
+  int old = *p;
+  if (v < old) *p = v;
+  return old;
+}
 inline int min(int a, int b) { return a < b ? a : b; }
 inline int max(int a, int b) { return a > b ? a : b; }

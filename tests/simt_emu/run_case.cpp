@@ -32,6 +32,16 @@
 //   out.bin: int32 skipped count (-1 without a counter), then the kv cache
 //            and, for e4m3, the kv scales
 //
+// A debug-check case (mla_decode_plan, then mla_decode_check) has its own
+// magic; the plan is built from its own lengths, so a stale plan can be
+// checked against new device lengths, and words of the image can be poked:
+//   in.bin : int32 header[12] = {magic, B, H, qmax, page_size, num_pages,
+//            max_pages, kv_dtype, causal, num_workgroups, has_q_lens,
+//            n_pokes}, then the planner's kv_lens and q_lens (if any), the
+//            device kv_lens and q_lens (if any), the block table, and n_pokes
+//            (word index, value) pairs applied to the plan image
+//   out.bin: int32 {call status, err[0], err[1]}
+//
 // A quantized-prefill case (mla_prefill_quantize + mla_prefill_attn) has its
 // own magic:
 //   in.bin : int32 header[12] = {magic, S, T, H, num_blocks, 0, ...}, float
@@ -219,6 +229,69 @@ int run_plan(FILE* f, const int32_t* hd, const char* out_path) {
   return 0;
 }
 
+int run_check(FILE* f, const int32_t* hd, const char* out_path) {
+  mla_shape s{};
+  s.batch = hd[1];
+  s.num_heads = hd[2];
+  s.max_q_len = hd[3];
+  s.d_latent = 512;
+  s.d_rope = 64;
+  s.page_size = hd[4];
+  s.num_pages = hd[5];
+  s.max_pages_per_seq = hd[6];
+  s.kv_dtype = hd[7];
+  s.causal = hd[8];
+  const int nwg = hd[9];
+  const bool has_ql = hd[10] != 0;
+  const int n_pokes = hd[11];
+  const size_t B4 = size_t(s.batch) * 4;
+  std::vector<int32_t> plan_kvl(s.batch), plan_ql(has_ql ? s.batch : 0);
+  read_into(f, plan_kvl.data(), B4);
+  if (has_ql) read_into(f, plan_ql.data(), B4);
+  int32_t* kvl = static_cast<int32_t*>(exact_alloc(B4, 4));
+  int32_t* ql = has_ql ? static_cast<int32_t*>(exact_alloc(B4, 4)) : nullptr;
+  int32_t* bt = static_cast<int32_t*>(exact_alloc(size_t(s.batch) * s.max_pages_per_seq * 4, 4));
+  read_into(f, kvl, B4);
+  if (ql) read_into(f, ql, B4);
+  read_into(f, bt, size_t(s.batch) * s.max_pages_per_seq * 4);
+  std::vector<int32_t> pokes(size_t(2) * n_pokes);
+  read_into(f, pokes.data(), pokes.size() * 4);
+  std::fclose(f);
+  const uint64_t bound = mla_plan_bytes_bound(&s, nwg);
+  if (bound == 0) die("shape rejected by mla_plan_bytes_bound");
+  std::vector<int32_t> host_plan(bound / 4 + 1);
+  mla_plan_info info{};
+  if (mla_decode_plan(&s, plan_kvl.data(), has_ql ? plan_ql.data() : nullptr, nwg,
+                      host_plan.data(), host_plan.size() * 4, &info) != MLA_OK)
+    die("mla_decode_plan failed");
+  int32_t* plan = static_cast<int32_t*>(exact_alloc(info.plan_bytes));
+  std::memcpy(plan, host_plan.data(), info.plan_bytes);
+  if (const char* dump = std::getenv("EMU_PLAN_OUT")) {   // the image before the pokes
+    FILE* pf = std::fopen(dump, "wb");
+    if (!pf) die("cannot open the plan dump file");
+    std::fwrite(plan, 1, info.plan_bytes, pf);
+    std::fclose(pf);
+  }
+  for (int k = 0; k < n_pokes; ++k) {
+    if (pokes[2 * k] < 0 || uint64_t(pokes[2 * k]) >= info.plan_bytes / 4) die("poke out of range");
+    plan[pokes[2 * k]] = pokes[2 * k + 1];
+  }
+  int32_t* err = static_cast<int32_t*>(exact_alloc(8, 8));
+  err[0] = err[1] = -7;
+  const mla_status st = mla_decode_check(&s, &info, plan, bt, kvl, ql, err, nullptr);
+  FILE* g = std::fopen(out_path, "wb");
+  if (!g) die("cannot open output");
+  const int32_t out[3] = {int32_t(st), err[0], err[1]};
+  std::fwrite(out, 1, sizeof out, g);
+  std::fclose(g);
+  std::free(kvl);
+  std::free(ql);
+  std::free(bt);
+  std::free(plan);
+  std::free(err);
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -231,6 +304,7 @@ int main(int argc, char** argv) {
   if (hd[0] == 0x4d4c4141) return run_append(f, hd, argv[2]);
   if (hd[0] == 0x4d4c4150) return run_plan(f, hd, argv[2]);
   if (hd[0] == 0x4d4c5046) return run_prefill(f, hd, argv[2]);
+  if (hd[0] == 0x4d4c4143) return run_check(f, hd, argv[2]);
   read_into(f, &scale, sizeof scale);
   const bool tree = hd[0] == 0x4d4c4154;
   if (hd[0] != 0x4d4c4145 && !tree) die("bad magic");
@@ -291,6 +365,12 @@ int main(int argc, char** argv) {
   // the "device" plan image: exactly plan_bytes long
   void* plan = exact_alloc(info.plan_bytes);
   std::memcpy(plan, host_plan.data(), info.plan_bytes);
+  if (const char* dump = std::getenv("EMU_PLAN_OUT")) {   // the image, for the caller to inspect
+    FILE* pf = std::fopen(dump, "wb");
+    if (!pf) die("cannot open the plan dump file");
+    std::fwrite(plan, 1, info.plan_bytes, pf);
+    std::fclose(pf);
+  }
   void* ws = info.workspace_bytes ? exact_alloc(info.workspace_bytes, 256) : nullptr;
 
   void* o = exact_alloc(rows * 512 * 2);

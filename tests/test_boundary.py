@@ -224,6 +224,27 @@ def test_fwd_and_combine_validate_before_any_launch(lib):
                                None) == 5
 
 
+def test_check_validates_before_any_launch(lib):
+    shape = _shape(B=2)
+    pl = mla.plan(shape, np.array([100, 3000], np.int32), num_workgroups=64, upload=False)
+    A = 0x10000   # aligned fake device addresses; never dereferenced on these paths
+
+    def chk(info=pl.info, plan=A, bt=A, kvl=A, ql=None, err=A, sh=shape):
+        return lib.mla_decode_check(ctypes.byref(sh), ctypes.byref(info), plan, bt, kvl, ql, err,
+                                    None)
+
+    assert chk(plan=None) == 1 and chk(err=None) == 1 and chk(bt=None) == 1
+    assert chk(kvl=None) == 1
+    assert chk(plan=A + 4) == 4 and chk(err=A + 2) == 4 and chk(ql=A + 1) == 4
+    bad = mla.PlanInfo.from_buffer_copy(pl.info)
+    bad.phases = 3
+    assert chk(info=bad) == 7
+    bad = mla.PlanInfo.from_buffer_copy(pl.info)
+    bad.plan_bytes = 32
+    assert chk(info=bad) == 7
+    assert chk(sh=_shape(B=2, P=48)) == 3
+
+
 def test_empty_batch_is_a_noop(lib):
     shape = _shape(B=0)
     pl = mla.plan(shape, np.zeros(0, np.int32), num_workgroups=8, upload=False)

@@ -178,3 +178,60 @@ def test_pair_stepping_matches_oracle(kv_lens, q_lens, nwg, kv_dtype, H, P):
     for mode in ("wait-lockstep", "issue-drift"):
         out, lse, meta = harness.run(case, nwg, 1, env_extra=MODES[mode])
         _check(case, out, lse)
+
+
+# ---------------------------------------------------------------- the case of the fifth GPU fault
+# The last faulting GPU run used a planner that charged one round per piece
+# and cut units at any round (item cost 1, shortest piece 1 round), and
+# faulted in the e4m3 page-relayout case below with 16 workgroups.  That
+# planner is the library's with MLA_ITEM_COST_ROUNDS=1 and kMinPieceRounds = 1;
+# it is built here for the emulator only.  Its plan gives one workgroup two
+# one-round items back to back (sequence 1, 64 keys, written directly; then
+# the first 64 keys of sequence 2, a partial).  The library's planner keeps
+# one item per workgroup for this case.
+
+
+def _relayout(case, seed):
+    from workloads import MLACase
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(case.num_pages).astype(np.int32)
+    kv = np.empty_like(case.kv)
+    kv[perm] = case.kv
+    sc = None
+    if case.kv_scale is not None:
+        sc = np.empty_like(case.kv_scale)
+        sc[perm] = case.kv_scale
+    bt = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    return MLACase(**{**case.__dict__, "kv": kv, "kv_scale": sc, "block_table": bt})
+
+
+def _plan_items(words):
+    G, N, off_wg, off_items = int(words[2]), int(words[3]), int(words[8]), int(words[9])
+    wg = words[off_wg:off_wg + G + 1]
+    items = words[off_items:off_items + 8 * N].reshape(N, 8)
+    return [[tuple(int(x) for x in items[i][:5]) for i in range(wg[g], wg[g + 1])]
+            for g in range(G)]
+
+
+def test_fifth_fault_case_replays_in_bounds_with_its_plan():
+    from tests.simt_emu import build as _b
+    binary = _b.build(tag="min_piece_1", patches={"plan_core.h": [
+        ("constexpr int kMinPieceRounds = 2;", "constexpr int kMinPieceRounds = 1;")]})
+    case = make_case(kv_lens=[700, 64, 1234], q_lens=[2, 1, 1], kv_dtype="fp8_e4m3", seed=22,
+                     sm_scale=1 / math.sqrt(192))
+    relaid = _relayout(case, 5)
+    env5 = {"MLA_ITEM_COST_ROUNDS": "1"}
+    # the library's plan: one item per workgroup
+    _, _, meta = harness.run(case, 16, 1, want_plan=True)
+    assert all(len(w) == 1 for w in _plan_items(meta["plan"]))
+    for mode in ("wait-lockstep", "issue-drift"):
+        outs = []
+        for c in (case, relaid):
+            out, lse, meta = harness.run(c, 16, 1, binary=binary, env_extra={**env5, **MODES[mode]},
+                                         want_plan=True)
+            per_wg = _plan_items(meta["plan"])
+            two = [w for w in per_wg if len(w) == 2]
+            assert two == [[(1, 0, 0, 64, -1), (2, 0, 0, 64, two[0][1][4])]], per_wg
+            _check(c, out, lse)
+            outs.append((out.copy(), lse.copy()))
+        assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])

@@ -260,10 +260,12 @@ def test_append_kernel_machine_code(append_isa):
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_q_kernel"),
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_k_kernel"),
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_v_kernel"),
-                                        ("prefill_attn_kernel.hip", "mla_prefill_attn_kernel")])
+                                        ("prefill_attn_kernel.hip", "mla_prefill_attn_kernel"),
+                                        ("check_kernel.hip", "mla_check_kernel")])
 def test_small_kernels_machine_code(tmp_path, src, kernel):
-    # the device planner, the tree-draft merge and the prefill kernels: no
-    # scratch, no scalar stores, LDS within the 160 KB a workgroup may use
+    # the device planner, the tree-draft merge, the prefill kernels and the
+    # debug check: no scratch, no scalar stores, LDS within the 160 KB a
+    # workgroup may use
     out = tmp_path / "k.s"
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
@@ -297,3 +299,219 @@ def test_prefill_attention_uses_the_int8_and_fp8_matrix_cores(tmp_path):
     f8 = sum(re.match(r"v_mfma(_scale)?_f32_16x16x128_f8f6f4", i) is not None for i in ins)
     assert i8 > 0 and i8 % (2 * 24) == 0 and f8 * 3 == i8
     assert not [i for i in ins if i.startswith("v_mfma") and "bf16" in i]
+
+
+# ---------------------------------------------------------------- the copy asm and its neighbours
+#
+# The HBM -> LDS copies are inline assembly, which the compiler's hazard
+# recognizer and wait-count pass do not look into.  The checks below cover,
+# in the compiled code, what the compiler therefore cannot: M0 (the copy's
+# LDS address) is written and read only inside the copy blocks; the register
+# a copy block saves M0 in is never read afterwards before it is rewritten
+# (the compiler may pick VCC for it); every copy follows its M0 write by at
+# least one wait state; and the vmcnt literals of the e4m3 kernels count
+# whole rounds of copies, each round issued as one branch-free run.
+
+
+def _kernels_asm(text):
+    """{kernel: [(label, [(instruction, asm block id or None)])]}"""
+    out, cur, asm_id, n_asm = {}, None, None, 0
+    for line in text.splitlines():
+        m = re.match(r"^(_ZN3mla\S*mla_decode_kernel\S*):", line)
+        if m:
+            cur = [("entry", [])]
+            out[m.group(1)] = cur
+            continue
+        if cur is None:
+            continue
+        if ";;#ASMSTART" in line:
+            n_asm += 1
+            asm_id = n_asm
+            continue
+        if ";;#ASMEND" in line:
+            asm_id = None
+            continue
+        s = line.split(";")[0].strip()
+        if s.startswith("s_endpgm"):
+            cur[-1][1].append((s, None))
+            cur = None
+            continue
+        lab = re.match(r"^(\.LBB\S+):", line)
+        if lab:
+            cur.append((lab.group(1), []))
+        elif s and not s.startswith("."):
+            cur[-1][1].append((s, asm_id))
+    return out
+
+
+def _regs(tok):
+    """Scalar registers a token names: 'sN', 'vcc_lo', 'vcc_hi', 'm0', 'exec_*'."""
+    tok = tok.strip()
+    if tok == "vcc":
+        return {"vcc_lo", "vcc_hi"}
+    if tok == "exec":
+        return {"exec_lo", "exec_hi"}
+    if tok in ("vcc_lo", "vcc_hi", "m0", "exec_lo", "exec_hi"):
+        return {tok}
+    return {f"s{i}" for i in _sgprs(tok)}
+
+
+_NO_DST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier",
+           "s_setprio", "s_endpgm", "s_sleep", "s_setreg", "s_sendmsg", "s_trap")
+
+
+def _reads_writes(ins):
+    """(read, written) scalar registers of one instruction (conservative: an
+    operand not known to be a destination counts as read)."""
+    parts = ins.split(None, 1)
+    op = parts[0]
+    ops = [o.strip().split()[0] for o in parts[1].split(",")] if len(parts) > 1 else []
+    reads, writes = set(), set()
+    dst_pos = set()
+    if op.startswith("s_") and not op.startswith(_NO_DST):
+        dst_pos = {0}
+    elif op.startswith(("v_readfirstlane", "v_readlane")) or (op.startswith("v_cmp") and not op.startswith("v_cmpx")):
+        dst_pos = {0}
+    elif op.startswith(("v_add_co", "v_sub_co", "v_subrev_co", "v_addc_co", "v_subb_co",
+                        "v_subbrev_co", "v_div_scale", "v_mad_u64", "v_mad_i64")):
+        dst_pos = {0, 1}
+    for k, o in enumerate(ops):
+        (writes if k in dst_pos else reads).update(_regs(o))
+    if op.startswith(("v_addc_co", "v_subb_co", "v_subbrev_co")) and op.endswith("_e32"):
+        reads |= {"vcc_lo", "vcc_hi"}
+    if op.startswith(("s_cbranch_vccz", "s_cbranch_vccnz", "v_div_fmas")):
+        reads |= {"vcc_lo", "vcc_hi"}
+    if op.startswith("v_cmp") and op.endswith("_e32"):
+        writes |= {"vcc_lo", "vcc_hi"}
+    return reads, writes
+
+
+def _successors(blocks):
+    index = {lab: k for k, (lab, _) in enumerate(blocks)}
+    succ = {k: [] for k in range(len(blocks))}
+    for k, (_, ins) in enumerate(blocks):
+        for i, _a in ins:
+            m = re.match(r"s_(?:c)?branch\S*\s+(\.LBB\S+)", i)
+            if m and m.group(1) in index:
+                succ[k].append(index[m.group(1)])
+        last = ins[-1][0] if ins else ""
+        if k + 1 < len(blocks) and not last.startswith(("s_branch", "s_endpgm")):
+            succ[k].append(k + 1)
+    return succ
+
+
+def _first_access_after(blocks, succ, k, j, regs):
+    """Walks every control-flow path forward from instruction j of block k;
+    returns the instructions that read any of `regs` before a write to all
+    of them on that path."""
+    bad, seen = [], set()
+    stack = [(k, j + 1, frozenset(regs))]
+    while stack:
+        b, i, live = stack.pop()
+        if (b, i, live) in seen:
+            continue
+        seen.add((b, i, live))
+        ins = blocks[b][1]
+        while i < len(ins):
+            r, w = _reads_writes(ins[i][0])
+            if r & live:
+                bad.append((blocks[b][0], ins[i][0]))
+                break
+            live = live - w
+            if not live:
+                break
+            i += 1
+        else:
+            for s in succ[b]:
+                stack.append((s, 0, live))
+    return bad
+
+
+def _copy_blocks(blocks):
+    """[(block index, index of the block's last instruction, [instructions])]
+    for every inline-asm block that issues a copy."""
+    out = {}
+    for k, (_, ins) in enumerate(blocks):
+        for j, (i, a) in enumerate(ins):
+            if a is not None:
+                out.setdefault(a, (k, j, []))
+                out[a] = (k, j, out[a][2] + [i])
+    return [v for v in out.values() if any(i.startswith("global_load_lds") for i in v[2])]
+
+
+def test_m0_is_written_and_read_only_inside_the_copy_blocks(isa):
+    for name, blocks in _kernels_asm(isa[1]).items():
+        for lab, ins in blocks:
+            for i, a in ins:
+                if a is None:
+                    assert not re.search(r"\bm0\b", i), f"{name} {lab}: {i}"
+
+
+def test_copy_block_shape_and_m0_wait_state(isa):
+    for name, blocks in _kernels_asm(isa[1]).items():
+        cbs = _copy_blocks(blocks)
+        assert cbs, name
+        for _k, _j, ins in cbs:
+            assert len(ins) == 5, ins
+            save = re.match(r"s_mov_b32 (\S+), m0$", ins[0])
+            setm0 = re.match(r"s_mov_b32 m0, (\S+)$", ins[1])
+            assert save and setm0 and ins[2] == "s_nop 0", ins
+            assert ins[3].startswith("global_load_lds_dword"), ins
+            assert ins[4] == f"s_mov_b32 m0, {save.group(1)}", ins
+            # the saved register is neither the new M0 nor an operand of the copy
+            tmp = _regs(save.group(1))
+            assert not (tmp & _regs(setm0.group(1))), ins
+            copy_regs = set()
+            for tok in ins[3].split(None, 1)[1].split(","):
+                copy_regs |= _regs(tok.strip().split()[0])
+            assert not (tmp & copy_regs), ins
+            # SALU write of M0 -> LDS-DMA read of M0: one wait state (s_nop 0)
+            assert _wait_states(ins[2]) >= 1
+
+
+def test_register_holding_saved_m0_is_not_read_after_the_copy(isa):
+    for name, blocks in _kernels_asm(isa[1]).items():
+        succ = _successors(blocks)
+        for k, j, ins in _copy_blocks(blocks):
+            tmp = _regs(re.match(r"s_mov_b32 (\S+), m0$", ins[0]).group(1))
+            bad = _first_access_after(blocks, succ, k, j, tmp)
+            assert not bad, f"{name}: {sorted(tmp)} read after a copy block: {bad[:3]}"
+
+
+def test_saved_register_walk_catches_a_planted_read():
+    blocks = [("entry", [("s_mov_b32 vcc_lo, m0", 1), ("s_mov_b32 m0, vcc_lo", 1),
+                         ("s_cbranch_scc1 .LBB0_2", None)]),
+              (".LBB0_1", [("v_cmp_gt_f32_e32 vcc, v1, v2", None)]),
+              (".LBB0_2", [("s_cbranch_vccnz .LBB0_1", None)])]
+    succ = _successors(blocks)
+    bad = _first_access_after(blocks, succ, 0, 1, {"vcc_lo"})
+    assert bad == [(".LBB0_2", "s_cbranch_vccnz .LBB0_1")]
+    # a write on the path first makes it safe
+    blocks[0][1].insert(2, ("s_mov_b32 vcc_lo, 0", None))
+    assert not _first_access_after(blocks, _successors(blocks), 0, 1, {"vcc_lo"})
+
+
+def test_literal_vmcnt_waits_count_whole_rounds(isa):
+    """bf16 kernels wait for every copy (vmcnt(0)); the e4m3 kernels wait with
+    vmcnt(10 * rounds issued after the awaited one), which is sound because
+    each round is one branch-free run of exactly 10 copies (9 of 16 bytes per
+    lane for the keys, 1 of 4 bytes for the scales) and vector-memory
+    operations complete in issue order: any other vector-memory operation only
+    adds to the count."""
+    for name, blocks in _kernels_asm(isa[1]).items():
+        e4m3 = "ILi1E" in name
+        literals = {int(m.group(1)) for _, ins in blocks for i, a in ins if a is not None
+                    for m in [re.match(r"s_waitcnt vmcnt\((\d+)\)$", i)] if m}
+        assert literals <= ({0, 10, 20} if e4m3 else {0}), (name, literals)
+        for lab, ins in blocks:
+            idx = [j for j, (i, _a) in enumerate(ins) if i.startswith("global_load_lds")]
+            if not idx:
+                continue
+            run = [i for i, _a in ins[idx[0]: idx[-1] + 1]]
+            x4 = sum(i.startswith("global_load_lds_dwordx4") for i in run)
+            x1 = sum(i.startswith("global_load_lds_dword ") for i in run)
+            assert (x4, x1) == ((9, 1) if e4m3 else (18, 0)), (name, lab, x4, x1)
+            # no branch and no other vector-memory operation inside the run
+            assert not [i for i in run if i.startswith(("s_cbranch", "s_branch", "global_load_d",
+                                                         "global_store", "buffer_", "scratch_",
+                                                         "flat_"))], (name, lab)
