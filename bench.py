@@ -11,7 +11,8 @@ Infinity Cache, so every step streams its cache from HBM.
 
 Prints ONE JSON line:
   value       KV GB/s: cached latent bytes of the visible keys / device time per step
-  us_per_call device time per step (fwd + combine), from HIP events
+  us_per_call device time per step (fwd + combine), from HIP events (mean;
+              us_per_call_pct and us_fwd_kernel_pct give p10 / median / p90)
   roofline    dominant kernel (mla_decode_kernel): algorithmic bytes (or FLOPs)
               per launch / its average launch time, against MI355X peak
   cpu_baseline the float64 oracle on a bounded sample of the same workload
@@ -99,9 +100,38 @@ def workload_counts(case):
                 kv_tokens=kv_tokens, rows=rows)
 
 
+def code_object_hash(source: str):
+    """Hash of the gfx950 code object the built library holds for one kernel
+    source (.text, .rodata, .note; written by the build), or None."""
+    path = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "_build", "code_objects.json")
+    try:
+        with open(path) as f:
+            return json.load(f).get(source)
+    except (OSError, ValueError):
+        return None
+
+
+def percentiles(ms):
+    """p10 / median / p90 of per-launch times in ms, returned in microseconds."""
+    xs = sorted(ms)
+    n = len(xs)
+
+    def q(p):   # linear interpolation between order statistics
+        x = p * (n - 1)
+        i = int(math.floor(x))
+        j = min(i + 1, n - 1)
+        return xs[i] + (xs[j] - xs[i]) * (x - i)
+
+    return {"p10": round(q(0.1) * 1e3, 2), "median": round(q(0.5) * 1e3, 2),
+            "p90": round(q(0.9) * 1e3, 2)}
+
+
 def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOURCES):
     """HBM bytes per launch of a kernel from the committed counter summary, or
-    None if there is none or the kernel source changed since."""
+    None if there is none or the kernel changed since.  A summary keyed by
+    code_object_sha256 holds while the machine code of sources[0] is the one
+    it was counted on; an older one keyed by kernel_source_sha256 holds while
+    the source text is unchanged."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -111,7 +141,10 @@ def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOUR
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
+    if "code_object_sha256" in kv:
+        if kv["code_object_sha256"] != code_object_hash(sources[0]):
+            return None
+    elif kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -263,7 +296,8 @@ def main_append(args) -> int:
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    avg_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(K)) / K
+    call_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    avg_ms = sum(call_ms) / K
     t = avg_ms * 1e-3
     achieved = cnt["alg_bytes"] / t / 1e9
     log(f"timed {K} appends: avg {avg_ms * 1e3:.2f} us, {achieved:.1f} GB/s")
@@ -277,12 +311,14 @@ def main_append(args) -> int:
         "config": {"workload": args.workload, "batch": B, "new_tokens_per_seq": n,
                    "kv_len": L, "page_size": P, "kv_dtype": kv_dtype},
         "us_per_call": round(avg_ms * 1e3, 2),
+        "us_per_call_pct": percentiles(call_ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "kernel": APPEND_KERNEL, "alg_bytes_per_launch": cnt["alg_bytes"]},
         "wall_s_timed": round(wall, 4), "input_sets": nsets,
-        "kernel_source_sha256": kernel_source_hash(APPEND_SOURCES), "cpu_baseline": None,
+        "kernel_source_sha256": kernel_source_hash(APPEND_SOURCES),
+        "code_object_sha256": code_object_hash(APPEND_SOURCES[0]), "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle append for about {args.cpu_seconds:.0f} s")
@@ -399,8 +435,9 @@ def main_prefill(args) -> int:
             log(f"step {i + 1}/{K}")
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    a_list = [e[1].elapsed_time(e[2]) for e in ev]
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    a_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    a_ms = sum(a_list) / K
     call_ms = q_ms + a_ms
     tops = cnt["ops"] / (a_ms * 1e-3) / 1e12
     quant_gbs = cnt["quant_bytes"] / (q_ms * 1e-3) / 1e9
@@ -417,6 +454,7 @@ def main_prefill(args) -> int:
                    "num_heads": H, "d_qk": 192, "d_v": 128, "causal": True,
                    "description": PREFILL_WORKLOADS[args.workload][1]},
         "ms_quantize": round(q_ms, 4), "ms_attention": round(a_ms, 4),
+        "us_attention_pct": percentiles(a_list),
         "quantize_GBps": round(quant_gbs, 1), "attention_tops": round(tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(tops, 2),
                      "peak": MFMA_INT8_FP8_PEAK_TOPS, "unit": "TOPS",
@@ -425,7 +463,8 @@ def main_prefill(args) -> int:
                      "kernel": PREFILL_KERNEL, "ops_per_launch": cnt["ops"],
                      "alg_bytes_per_launch": cnt["attn_bytes"]},
         "wall_s_timed": round(wall, 4),
-        "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES), "cpu_baseline": None,
+        "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES),
+        "code_object_sha256": code_object_hash(PREFILL_SOURCES[0]), "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on one head for about {args.cpu_seconds:.0f} s")
@@ -601,7 +640,8 @@ def main() -> int:
     if args.graph and tree is None:
         # one graph per input set, each capturing fwd + combine with the
         # fixed-shape plan of the same lengths (same split, all workgroups)
-        plf = mla.plan(shape, case.kv_lens, case.q_lens, device=dev, fixed=True)
+        plf = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=nwg, device=dev,
+                       fixed=True)
         wsf = torch.empty(plf.info.workspace_bytes, dtype=torch.uint8, device=dev)
         graphs = []
         for k in range(nsets):
@@ -630,14 +670,14 @@ def main() -> int:
         log(f"graph replays: avg {graph_avg * 1e3:.2f} us per fwd + combine")
         # the device-side planner on the same lengths (one workgroup)
         kvl0, ql0 = sets[0][4], sets[0][5]
-        dp = mla.plan_device(shape, kvl0, ql0)
+        dp = mla.plan_device(shape, kvl0, ql0, num_workgroups=nwg)
         for _ in range(3):
-            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device)
+            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device, num_workgroups=nwg)
         torch.cuda.synchronize()
         pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
         for k in range(20):
             pev[k][0].record(stream)
-            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device)
+            mla.plan_device(shape, kvl0, ql0, plan_buf=dp.device, num_workgroups=nwg)
             pev[k][1].record(stream)
         torch.cuda.synchronize()
         plan_dev_us = sum(pev[k][0].elapsed_time(pev[k][1]) for k in range(20)) / 20 * 1e3
@@ -680,6 +720,8 @@ def main() -> int:
         },
         "us_per_call": round(step_avg * 1e3, 2),
         "us_fwd_kernel": round(fwd_avg * 1e3, 2),
+        "us_per_call_pct": percentiles(step_ms),
+        "us_fwd_kernel_pct": percentiles(fwd_ms),
         "us_per_call_warm": round(warm_avg * 1e3, 2),
         "us_per_call_graph": None if graph_avg is None else round(graph_avg * 1e3, 2),
         "us_tree_merge": None if tree_avg is None else round(tree_avg * 1e3, 2),
@@ -700,6 +742,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "input_sets": nsets,
         "kernel_source_sha256": kernel_source_hash(),
+        "code_object_sha256": code_object_hash("decode_kernel.hip"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

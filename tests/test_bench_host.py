@@ -51,3 +51,42 @@ def test_traffic_summary_keyed_by_source_hash(tmp_path, monkeypatch):
     (csrc / bench.KERNEL_SOURCES[0]).write_text("changed")
     assert bench.read_traffic("wl", "mla_decode_kernel_pairs") is None
     assert bench.read_traffic("other", "mla_decode_kernel_pairs") is None
+
+
+def test_traffic_summary_keyed_by_code_object(tmp_path, monkeypatch):
+    # a summary keyed by the machine code stays valid across source edits that
+    # leave the code object alone, and goes stale when the code object changes
+    import json
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    build = tmp_path / "mla_paged_decode_absorbed_amd" / "_build"
+    build.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    manifest = build / "code_objects.json"
+    manifest.write_text(json.dumps({"decode_kernel.hip": "00112233aabbccdd"}))
+    f = prof / "mla_decode_kernel_pairs_wl_traffic.txt"
+    f.write_text("code_object_sha256: 00112233aabbccdd\nhbm_bytes_per_launch: 777\n")
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") == 777.0
+    manifest.write_text(json.dumps({"decode_kernel.hip": "ffffffffffffffff"}))
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") is None
+    manifest.unlink()
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") is None
+
+
+def test_percentiles_by_hand():
+    p = bench.percentiles([0.001 * k for k in range(1, 12)])   # 1 .. 11 us
+    assert p == {"p10": 2.0, "median": 6.0, "p90": 10.0}
+    assert bench.percentiles([0.005]) == {"p10": 5.0, "median": 5.0, "p90": 5.0}
+
+
+def test_build_manifest_matches_the_library_objects():
+    # the manifest the build writes names every kernel source's code object
+    import json
+    from mla_paged_decode_absorbed_amd import build
+    if not os.path.exists(build.CODE_OBJECTS):
+        import pytest
+        pytest.skip("library not built")
+    with open(build.CODE_OBJECTS) as f:
+        m = json.load(f)
+    assert set(m) == {s for s in build.SOURCES if s.endswith(".hip")}
+    assert bench.code_object_hash("decode_kernel.hip") == m["decode_kernel.hip"]
