@@ -26,6 +26,12 @@
  *
  *   1. mla_decode_plan   host only: split-KV schedule from host-side lengths.
  *   2. copy the plan image (plan_host, info.plan_bytes) to device memory.
+ *      The caller copies: the planner makes no HIP call (it runs, and is
+ *      tested, without a GPU), and one plan serves every layer of a decode
+ *      step, so the caller decides when and on which stream it travels
+ *      (from pinned memory with hipMemcpyAsync, keeping the host buffer alive
+ *      until the stream passes the copy, or synchronously).  Plans built on
+ *      the GPU need no copy: mla_decode_plan_device.
  *   3. mla_decode_fwd    main kernel: writes O/LSE for unsplit row blocks and
  *                        partial (O, LSE) into the workspace for split ones.
  *   4. mla_combine       merges the partials of split row blocks into O/LSE.
@@ -111,8 +117,10 @@ int32_t mla_abi_version(void);
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status status);
 
-/* Upper bounds, for allocating before the lengths are known.  num_workgroups
- * as passed to mla_decode_plan (0 is not accepted here: pass the CU count). */
+/* Upper bounds, for allocating before the lengths are known (the exact sizes
+ * of a plan are info->plan_bytes and info->workspace_bytes, known once it is
+ * built; hence "_bound").  num_workgroups as passed to mla_decode_plan (0 is
+ * not accepted here: pass the CU count). */
 uint64_t mla_plan_bytes_bound(const mla_shape* shape, int32_t num_workgroups);
 uint64_t mla_workspace_bytes_bound(const mla_shape* shape, int32_t num_workgroups);
 
@@ -205,7 +213,16 @@ mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups
                                   mla_stream_t stream);
 
 /*
- * Main decode kernel launch.
+ * Main decode kernel launch: the attention of the formula at the top of this
+ * file for every valid query row, over the keys of its work items.  The
+ * operation is the decode-time weight-absorbed MLA of the KsanaLLM 0.6.0 page
+ * (prefill/decode disaggregation section: the query arrives absorbed, O
+ * leaves in latent space); q_len > 1 is the draft verification of the
+ * PaddlePaddle 3.0 inference page (speculative decoding section), token t
+ * seeing keys j <= L_b - q_b + t; the natural-log LSE output is the
+ * softmax_lse of the FlashAttention-3 in DeepSeek-R1 page (chapter 2), whose
+ * split-K partition this kernel applies to row blocks the plan cut; fp8
+ * caches carry that page's per-token scale (section 3.1).
  *
  *   plan_dev     device copy of the plan image described by *info.
  *   q            [B, max_q_len, H, d_latent + d_rope] bf16, row-major.  Rows
@@ -237,7 +254,9 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info,
                           void* workspace, uint64_t workspace_bytes, mla_stream_t stream);
 
 /*
- * Merge of split row blocks: for each combine entry of the plan,
+ * Merge of split row blocks (the log-sum-exp combination that makes the
+ * split-K key partition of the FlashAttention-3 in DeepSeek-R1 page, chapter
+ * 2, exact up to rounding): for each combine entry of the plan,
  *   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) * O_s  -> bf16,
  * reading the workspace partials laid out as described for mla_decode_fwd.
  * A row whose partials are all empty (LSE_s = -inf) gets O = 0, LSE = -inf.
@@ -310,7 +329,12 @@ mla_status mla_decode_check(const mla_shape* shape, const mla_plan_info* info,
 
 /*
  * Tree-shaped drafts: the draft tokens' part of the attention, merged into
- * the result of a decode over the cached prefix.
+ * the result of a decode over the cached prefix.  Sources: all drafts of a
+ * sequence verified in one decode pass (PaddlePaddle 3.0 inference page,
+ * speculative decoding section); EAGLE-style top-k drafting, whose drafts
+ * form a tree (Dewu DeepSeek deployment slides, MTP); the merge is the
+ * log-sum-exp combination of split-K (FlashAttention-3 in DeepSeek-R1 page,
+ * chapter 2).
  *
  * With EAGLE-style speculative decoding (top-k candidates per step) the
  * q_b draft tokens of sequence b form a tree and are verified in one pass:
@@ -459,8 +483,9 @@ mla_status mla_prefill_quantize(const mla_prefill_shape* shape, const int32_t* c
  *   o    [T, H, 128] bf16 (device, 16-byte aligned); lse [T, H] fp32 (device).
  *   softmax_scale  finite and > 0 (BAD_SHAPE otherwise).
  *
- * One workgroup per (128-token block, head); the P V product runs on e4m3
- * matrix instructions and the Q K product on INT8 ones.  Errors as for
+ * Two workgroups per (128-token query block, head), 64 queries each; the P V
+ * product runs on e4m3 matrix instructions and the Q K product on INT8 ones.
+ * Errors as for
  * mla_prefill_quantize; rows of sequences with inconsistent cu_seqlens are
  * not written.
  */

@@ -20,7 +20,7 @@ The plain definition:
    The scale and the quotient are computed in fp32 because they decide
    integer codes: this is the precision the kernel takes them in.
 
-Pins (``tests/test_oracle_pins.py``): the encoder maps every finite code's
+Pins (``tests/test_oracle_append_pins.py``): the encoder maps every finite code's
 value back to that code, sends every midpoint between neighbouring codes to
 the even one, and agrees with the library cast ``torch.float8_e4m3fn`` on
 random fp32 values over the whole range; the largest element of each row gets

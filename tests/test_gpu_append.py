@@ -171,10 +171,14 @@ def test_append_then_decode_bf16():
     O, L = oracle.mla_decode_ref(case)
     o = out.float().cpu().numpy().astype(np.float64)
     lse_np = lse.cpu().numpy()
+    num = den = 0.0
     for b in range(case.batch):
         n = int(case.q_lens[b])
         assert np.abs(o[b, :n] - O[b, :n]).max() <= 2e-2
         assert np.abs(lse_np[b, :n] - L[b, :n]).max() <= 1e-3
+        num += float(((o[b, :n] - O[b, :n]) ** 2).sum())
+        den += float((O[b, :n] ** 2).sum())
+    assert math.sqrt(num / den) <= 5e-3
 
 
 def test_append_then_decode_e4m3():

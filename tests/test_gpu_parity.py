@@ -322,29 +322,27 @@ def test_combine_kernel_matches_combine_ref():
                 assert np.isneginf(l[b, t, h]) and np.all(o[b, t, h] == 0)
                 continue
             assert abs(l[b, t, h] - Lc[r]) <= 1e-4 * max(1.0, abs(Lc[r]))
+            # fp32 merge, then one bf16 rounding: at most 2^-9 of the row's
+            # largest value, so 4e-3 of it leaves a factor of two
             err = np.abs(o[b, t, h] - Oc[r]).max()
-            assert err <= 1e-2 * max(1.0, np.abs(Oc[r]).max())
+            assert err <= 4e-3 * np.abs(Oc[r]).max()
 
 
 # ---------------------------------------------------------------- full-size workloads
+# The four workloads at their full sizes, in the launch configuration bench.py
+# times (one workgroup per CU): every sequence against the float64 oracle,
+# max-abs and rel-L2 over the whole output tensor (about 1 s to 15 s of
+# oracle time each on 16 host threads).
 
-FULL = [
-    ("v3_decode_bf16", [0, 17, 40, 63]),
-    ("mtp_verify_bf16", [0, 5, 77, 127]),
-    ("long_ctx_fp8", [0, 9, 15]),
-    ("ragged_serving_bf16", [1, 2, 100, 200, 255]),
-]
+FULL = ["v3_decode_bf16", "mtp_verify_bf16", "long_ctx_fp8", "ragged_serving_bf16"]
 
 
-@pytest.mark.parametrize("name,seqs", FULL)
-def test_full_size_workloads_sampled(name, seqs):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads(name):
     case = workload(name)
     (out, lse), pl = run_gpu(case)
     print(f"{name}: workgroups {pl.info.num_workgroups} items {pl.info.num_items} "
           f"partials {pl.info.num_partials}", flush=True)
-    worst, rel = check(case, out, lse, seqs=seqs)
-    print(f"{name}: sampled max-abs {worst:.3g} rel-L2 {rel:.3g}", flush=True)
-    # every valid row of the whole call is finite
-    o = out.float()
-    for b in range(case.batch):
-        assert torch.isfinite(o[b, :int(case.q_lens[b])]).all()
+    worst, rel = check(case, out, lse)
+    print(f"{name}: all {case.batch} sequences: max-abs {worst:.3g} rel-L2 {rel:.3g}",
+          flush=True)

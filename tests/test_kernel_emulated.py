@@ -235,3 +235,45 @@ def test_fifth_fault_case_replays_in_bounds_with_its_plan():
             _check(c, out, lse)
             outs.append((out.copy(), lse.copy()))
         assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------- restart storms
+# The kernels fix each row's reference max at its first visible key step and
+# restart the item when a later score exceeds it by more than 32 (log2
+# units).  The reference only rises, by more than 32 for some row at each
+# restart, so an item restarts at most ceil((s_max - s_ref) * log2(e) / 32)
+# times per row, where s_ref is the row's first reference: finite, but with
+# steadily rising scores every key step can restart and the item's work grows
+# with the square of its length.  These cases build exactly that (cached rows
+# whose every entry is c_j, c_j rising by about 0.6 every 32 keys, against an
+# all-ones query: the score rises by about 36 log2 units every 32 keys) and
+# check the result through all the restarts.
+
+
+def _rising_scores_case(kv_dtype, L=300, H=16):
+    import torch
+    case = make_case(kv_lens=[L], q_lens=[1], num_heads=H, seed=41, kv_dtype=kv_dtype,
+                     sm_scale=1 / math.sqrt(192))
+    ones = torch.ones(576, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
+    case.q[0, 0, :] = ones.view(np.uint16)
+    c = (np.arange(L, dtype=np.float32) * np.float32(0.6 / 32)).astype(np.float32)
+    for j in range(L):
+        page, slot = case.block_table[0, j // case.page_size], j % case.page_size
+        if kv_dtype == "bf16":
+            v = torch.full((576,), float(c[j])).to(torch.bfloat16).view(torch.int16).numpy()
+            case.kv[page, slot] = v.view(np.uint16)
+        else:
+            # every code 448 (0x7E) with scale c_j / 448: the row decodes to c_j
+            case.kv[page, slot] = 0x7E
+            case.kv_scale[page, slot] = np.float32(max(c[j], 1e-3) / 448.0)
+    return case
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_emulated_restart_storm_with_rising_scores(kv_dtype):
+    case = _rising_scores_case(kv_dtype)
+    # the first and the last 32-key step differ by far more than 32 log2 units
+    O, L = oracle.mla_decode_ref(case)
+    assert L[0, 0, 0] * math.log2(math.e) > 9 * 32
+    out, lse, _ = harness.run(case, 1, 1, env_extra=MODES["wait-lockstep"])
+    _check(case, out, lse)
