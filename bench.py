@@ -100,15 +100,22 @@ def workload_counts(case):
                 kv_tokens=kv_tokens, rows=rows)
 
 
-def code_object_hash(source: str):
-    """Hash of the gfx950 code object the built library holds for one kernel
-    source (.text, .rodata, .note; written by the build), or None."""
+def code_object_hash(source: str, kernel: str):
+    """Fingerprint of one kernel in the built library (its machine code,
+    kernel descriptor and metadata, as the build records them), or None."""
     path = os.path.join(ROOT, "mla_paged_decode_absorbed_amd", "_build", "code_objects.json")
     try:
         with open(path) as f:
-            return json.load(f).get(source)
-    except (OSError, ValueError):
+            return (json.load(f).get(source) or {}).get(kernel)
+    except (OSError, ValueError, AttributeError):
         return None
+
+
+def decode_kernel_symbol(kv_dtype: str, phases: int) -> str:
+    """The instantiation a plan launches, as the build's fingerprints name it."""
+    if kv_dtype == "bf16" and phases == 1:
+        return "mla_decode_kernel_pairs<0>"
+    return f"mla_decode_kernel<{0 if kv_dtype == 'bf16' else 1}, {phases}>"
 
 
 def percentiles(ms):
@@ -126,12 +133,13 @@ def percentiles(ms):
             "p90": round(q(0.9) * 1e3, 2)}
 
 
-def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOURCES):
+def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOURCES,
+                 symbol: str | None = None):
     """HBM bytes per launch of a kernel from the committed counter summary, or
     None if there is none or the kernel changed since.  A summary keyed by
-    code_object_sha256 holds while the machine code of sources[0] is the one
-    it was counted on; an older one keyed by kernel_source_sha256 holds while
-    the source text is unchanged."""
+    code_object_sha256 holds while the fingerprint of `symbol` (the launched
+    instantiation, in sources[0]) is the one it was counted on; an older one
+    keyed by kernel_source_sha256 holds while the source text is unchanged."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -142,7 +150,7 @@ def read_traffic(workload: str, kernel: str = DECODE_KERNEL, sources=KERNEL_SOUR
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     if "code_object_sha256" in kv:
-        if kv["code_object_sha256"] != code_object_hash(sources[0]):
+        if symbol is None or kv["code_object_sha256"] != code_object_hash(sources[0], symbol):
             return None
     elif kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
@@ -301,7 +309,8 @@ def main_append(args) -> int:
     t = avg_ms * 1e-3
     achieved = cnt["alg_bytes"] / t / 1e9
     log(f"timed {K} appends: avg {avg_ms * 1e3:.2f} us, {achieved:.1f} GB/s")
-    traffic = read_traffic(args.workload, APPEND_KERNEL, APPEND_SOURCES)
+    append_sym = f"{APPEND_KERNEL}<{0 if kv_dtype == 'bf16' else 1}>"
+    traffic = read_traffic(args.workload, APPEND_KERNEL, APPEND_SOURCES, append_sym)
     res = {
         "metric": "MLA cache append µs/call and HBM GB/s",
         "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -318,7 +327,8 @@ def main_append(args) -> int:
                      "kernel": APPEND_KERNEL, "alg_bytes_per_launch": cnt["alg_bytes"]},
         "wall_s_timed": round(wall, 4), "input_sets": nsets,
         "kernel_source_sha256": kernel_source_hash(APPEND_SOURCES),
-        "code_object_sha256": code_object_hash(APPEND_SOURCES[0]), "cpu_baseline": None,
+        "code_object_sha256": code_object_hash(APPEND_SOURCES[0], append_sym),
+        "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle append for about {args.cpu_seconds:.0f} s")
@@ -443,7 +453,8 @@ def main_prefill(args) -> int:
     quant_gbs = cnt["quant_bytes"] / (q_ms * 1e-3) / 1e9
     log(f"timed {K} calls: quantize {q_ms:.3f} ms ({quant_gbs:.0f} GB/s), "
         f"attention {a_ms:.3f} ms ({tops:.1f} TOPS)")
-    traffic = read_traffic(args.workload, PREFILL_KERNEL, PREFILL_SOURCES)
+    prefill_sym = f"{PREFILL_KERNEL}<4, 1>"
+    traffic = read_traffic(args.workload, PREFILL_KERNEL, PREFILL_SOURCES, prefill_sym)
     res = {
         "metric": "quantized causal prefill tokens/s (INT8 QK, e4m3 PV, head dim 192/128)",
         "value": round(cnt["tokens"] / (call_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -464,7 +475,8 @@ def main_prefill(args) -> int:
                      "alg_bytes_per_launch": cnt["attn_bytes"]},
         "wall_s_timed": round(wall, 4),
         "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES),
-        "code_object_sha256": code_object_hash(PREFILL_SOURCES[0]), "cpu_baseline": None,
+        "code_object_sha256": code_object_hash(PREFILL_SOURCES[0], prefill_sym),
+        "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on one head for about {args.cpu_seconds:.0f} s")
@@ -695,7 +707,8 @@ def main() -> int:
         achieved, peak, unit, bound = cnt["flops"] / t_fwd / 1e12, MFMA_BF16_PEAK_TFLOPS, \
             "TFLOP/s", "mfma"
     kernel_name = decode_kernel_name(case.kv_dtype, pl.phases)
-    traffic = read_traffic(args.workload, kernel_name)
+    kernel_sym = decode_kernel_symbol(case.kv_dtype, pl.phases)
+    traffic = read_traffic(args.workload, kernel_name, symbol=kernel_sym)
 
     res = {
         "metric": METRIC,
@@ -742,7 +755,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "input_sets": nsets,
         "kernel_source_sha256": kernel_source_hash(),
-        "code_object_sha256": code_object_hash("decode_kernel.hip"),
+        "code_object_sha256": code_object_hash("decode_kernel.hip", kernel_sym),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

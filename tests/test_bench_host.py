@@ -63,14 +63,21 @@ def test_traffic_summary_keyed_by_code_object(tmp_path, monkeypatch):
     build.mkdir(parents=True)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     manifest = build / "code_objects.json"
-    manifest.write_text(json.dumps({"decode_kernel.hip": "00112233aabbccdd"}))
+    sym = bench.decode_kernel_symbol("bf16", 1)
+    assert sym == "mla_decode_kernel_pairs<0>"
+    manifest.write_text(json.dumps({"decode_kernel.hip": {sym: "00112233aabbccdd",
+                                                          "other<1>": "1"}}))
     f = prof / "mla_decode_kernel_pairs_wl_traffic.txt"
     f.write_text("code_object_sha256: 00112233aabbccdd\nhbm_bytes_per_launch: 777\n")
-    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") == 777.0
-    manifest.write_text(json.dumps({"decode_kernel.hip": "ffffffffffffffff"}))
-    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") is None
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs", symbol=sym) == 777.0
+    # another kernel of the same file changing does not matter
+    manifest.write_text(json.dumps({"decode_kernel.hip": {sym: "00112233aabbccdd",
+                                                          "other<1>": "2"}}))
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs", symbol=sym) == 777.0
+    manifest.write_text(json.dumps({"decode_kernel.hip": {sym: "ffffffffffffffff"}}))
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs", symbol=sym) is None
     manifest.unlink()
-    assert bench.read_traffic("wl", "mla_decode_kernel_pairs") is None
+    assert bench.read_traffic("wl", "mla_decode_kernel_pairs", symbol=sym) is None
 
 
 def test_percentiles_by_hand():
@@ -89,4 +96,7 @@ def test_build_manifest_matches_the_library_objects():
     with open(build.CODE_OBJECTS) as f:
         m = json.load(f)
     assert set(m) == {s for s in build.SOURCES if s.endswith(".hip")}
-    assert bench.code_object_hash("decode_kernel.hip") == m["decode_kernel.hip"]
+    for kvd in ("bf16", "fp8_e4m3"):
+        for ph in (1, 2, 4):
+            sym = bench.decode_kernel_symbol(kvd, ph)
+            assert bench.code_object_hash("decode_kernel.hip", sym) == m["decode_kernel.hip"][sym]

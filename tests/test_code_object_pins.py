@@ -1,21 +1,23 @@
-"""The gfx950 machine code of the library's GPU kernels, pinned (CPU only:
-hipcc cross-compiles, nothing runs on a GPU).
+"""The gfx950 machine code of the library's GPU kernels, pinned kernel by
+kernel (CPU only: hipcc cross-compiles, nothing runs on a GPU).
 
-Each kernel source is compiled device-only with the library's own flags, and
-the code object's machine code (.text), kernel descriptors (.rodata: register
-counts, LDS size, launch properties) and metadata (.note) are hashed.  The
-pinned hashes are those of the build whose library passed the GPU parity,
-graph-replay, tree-draft and cache-append suites (and, for the prefill
-kernels, the quantized-prefill suite) on MI355X.  A source edit that leaves
-the machine code alone keeps the pin; any change of the code that runs on
-the GPU fails here, so it cannot enter the library unnoticed.
+Each kernel source is compiled device-only with the library's own flags; for
+every kernel in its code object the test hashes the kernel's machine code
+(its bytes of .text), its kernel descriptor (64 bytes of .rodata: register
+counts, LDS and scratch sizes, launch properties; the field that locates the
+code is masked, since adding another kernel to the file may move it) and its
+entry of the code object metadata (argument layout, sizes).  The pinned
+hashes are those of the build whose library passed the GPU parity, graph,
+tree-draft and cache-append suites (and, for the prefill kernels, the
+quantized-prefill suite) on MI355X.  A source edit that leaves the machine
+code alone keeps the pins, and kernels may be added beside the pinned ones;
+any change of a pinned kernel fails here, so no kernel that has not passed
+the GPU suites replaces a validated one unnoticed.
 
 The hashes hold for one compiler build only; under another one the test is
 skipped (it says which).
 """
-import hashlib
 import os
-import re
 import shutil
 import subprocess
 import sys
@@ -27,28 +29,51 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 from mla_paged_decode_absorbed_amd import build as libbuild  # noqa: E402
 
-LLVM = "/opt/rocm/llvm/bin"
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 # The compiler the pins were taken with.
 PINNED_COMPILER = "AMD clang version 22.0.0git (https://github.com/RadeonOpenCompute/llvm-project " \
                   "roc-7.2.0 26014 7b800a19466229b8479a78de19143dc33c3ab9b5)"
 
-# sha256 (first 16 hex digits) of .text + .rodata + .note of each source's
-# gfx950 code object.
+# source -> {kernel (demangled name, template arguments kept): sha256 (16 hex
+# digits) of its code, masked descriptor and metadata}
 PINS = {
-    "decode_kernel.hip": "2f71c036ab578aff",
-    "combine_kernel.hip": "95b0acb3adf772a6",
-    "append_kernel.hip": "845cbeead2be0fec",
-    "plan_kernel.hip": "7b64942843243e1d",
-    "tree_kernel.hip": "1342ea6d494bdfca",
-    "prefill_quant_kernel.hip": "f3ac478ecf16a5f1",
-    "prefill_attn_kernel.hip": "181cb571a4592cb5",
+    "append_kernel.hip": {
+        "mla_kv_append_kernel<0>": "af40742b52a854ed",
+        "mla_kv_append_kernel<1>": "99a6f632625ccac8",
+    },
+    "combine_kernel.hip": {
+        "mla_combine_kernel": "3b55ab76a3e9e923",
+    },
+    "decode_kernel.hip": {
+        "mla_decode_kernel<0, 2>": "f68f1fafb811c729",
+        "mla_decode_kernel<0, 4>": "f80e603336080f50",
+        "mla_decode_kernel<1, 1>": "4561acbbca3d28d9",
+        "mla_decode_kernel<1, 2>": "12030241895c4f29",
+        "mla_decode_kernel<1, 4>": "1385b15ad6d2f593",
+        "mla_decode_kernel_pairs<0>": "01606bf0968b13e5",
+    },
+    "plan_kernel.hip": {
+        "mla_plan_kernel": "37c084122812ee11",
+    },
+    "prefill_attn_kernel.hip": {
+        "mla_prefill_attn_kernel<4, 1>": "6134ed22eb397dcc",
+    },
+    "prefill_quant_kernel.hip": {
+        "mla_prefill_quant_k_kernel": "e9418dd04c1a1462",
+        "mla_prefill_quant_q_kernel": "d7c6220d5a7f9bef",
+        "mla_prefill_quant_v_kernel": "0c5fed5eae148b9b",
+    },
+    "tree_kernel.hip": {
+        "mla_tree_kernel": "925d7d16b9f574d5",
+    },
 }
 
-pytestmark = pytest.mark.skipif(
-    HIPCC is None or not os.path.exists(os.path.join(LLVM, "llvm-objcopy")),
-    reason="ROCm toolchain not available")
+# Kernel sources added after the last GPU run of this library; none of them is
+# on the default decode path.
+NOT_YET_RUN_ON_GPU = ("check_kernel.hip",)   # mla_decode_check, opt-in debug mode
+
+pytestmark = pytest.mark.skipif(HIPCC is None, reason="ROCm toolchain not available")
 
 
 def _compiler_id() -> str:
@@ -59,51 +84,77 @@ def _compiler_id() -> str:
     return ""
 
 
-def code_object_hash(src: str, workdir: str) -> str:
-    """Hash of the gfx950 code object that the library build embeds for one
-    source file (same flags; device-only, unbundled)."""
+# The fingerprint (code bytes, masked descriptor, metadata entry) is
+# libbuild.kernel_fingerprints; the planted-change test below checks that it
+# sees a one-byte change of one kernel and nothing of its neighbour.
+kernel_fingerprints = libbuild.kernel_fingerprints
+
+
+def compile_code_object(src: str, workdir: str) -> str:
     co = os.path.join(workdir, src + ".co")
     cmd = [HIPCC, *libbuild.common_flags(), "--cuda-device-only", "--no-gpu-bundle-output",
            "-c", os.path.join(libbuild.CSRC, src), "-o", co]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
-    h = hashlib.sha256()
-    for sec in (".text", ".rodata", ".note"):
-        out = os.path.join(workdir, f"{src}{sec}.bin")
-        res = subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "-O", "binary",
-                              f"--only-section={sec}", co, out], capture_output=True, text=True)
-        assert res.returncode == 0, res.stderr
-        with open(out, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return co
 
 
 @pytest.fixture(scope="module")
-def hashes(tmp_path_factory):
+def fingerprints(tmp_path_factory):
     if _compiler_id() != PINNED_COMPILER:
         pytest.skip(f"pins were taken with {PINNED_COMPILER!r}, this is {_compiler_id()!r}")
+    pytest.importorskip("msgpack")
     d = str(tmp_path_factory.mktemp("co"))
     with ThreadPoolExecutor(max_workers=4) as ex:
-        vals = list(ex.map(lambda s: code_object_hash(s, d), sorted(PINS)))
-    return dict(zip(sorted(PINS), vals))
+        cos = list(ex.map(lambda s: compile_code_object(s, d), sorted(PINS)))
+    return {src: kernel_fingerprints(co) for src, co in zip(sorted(PINS), cos)}
 
 
 @pytest.mark.parametrize("src", sorted(PINS))
-def test_kernel_machine_code_is_the_validated_one(hashes, src):
-    assert hashes[src] == PINS[src], (
-        f"{src}: the gfx950 code object changed ({hashes[src]} != pinned {PINS[src]}); "
-        "code that has not passed the GPU suites must not replace the validated kernels")
+def test_validated_kernels_are_unchanged(fingerprints, src):
+    got = fingerprints[src]
+    for kernel, pin in PINS[src].items():
+        assert kernel in got, f"{src}: validated kernel {kernel} is gone ({sorted(got)})"
+        assert got[kernel] == pin, (
+            f"{src}: {kernel} changed ({got[kernel]} != pinned {pin}); code that has not "
+            "passed the GPU suites must not replace a validated kernel")
 
 
 def test_every_library_kernel_source_is_pinned_or_new():
     """Every HIP source of the library is either pinned here or listed as a
-    kernel added since, whose GPU status the design notes state."""
+    kernel source added since, whose GPU status the design notes state."""
     srcs = {s for s in libbuild.SOURCES if s.endswith(".hip")}
     unpinned = srcs - set(PINS)
     assert unpinned <= set(NOT_YET_RUN_ON_GPU), sorted(unpinned - set(NOT_YET_RUN_ON_GPU))
-    assert not re.search(r"\s", "".join(srcs))
 
 
-# Kernel sources added after the last GPU run of this library; none of them is
-# on the default decode path.
-NOT_YET_RUN_ON_GPU = ("check_kernel.hip",)   # mla_decode_check, opt-in debug mode
+def test_fingerprint_sees_a_one_byte_change(tmp_path):
+    """A planted change of one instruction byte of one kernel changes that
+    kernel's fingerprint and not its neighbour's."""
+    if _compiler_id() != PINNED_COMPILER:
+        pytest.skip("other compiler")
+    pytest.importorskip("msgpack")
+    co = compile_code_object("append_kernel.hip", str(tmp_path))
+    before = kernel_fingerprints(co)
+    with open(co, "rb") as f:
+        blob = bytearray(f.read())
+    secs, cstr = libbuild._elf_sections(bytes(blob))
+    syms = libbuild._elf_symbols(bytes(blob), secs, cstr)
+    kd = next(md[".symbol"] for md in libbuild._amdgpu_kernels_metadata(bytes(blob), secs)
+              if libbuild.kernel_short_name(md[".name"]) == "mla_kv_append_kernel<1>")
+    value, size, shndx = syms[kd[:-3]]
+    pos = secs[shndx]["off"] + value - secs[shndx]["addr"] + size // 2
+    blob[pos] ^= 0x01
+    planted = tmp_path / "planted.co"
+    planted.write_bytes(bytes(blob))
+    after = kernel_fingerprints(str(planted))
+    assert after["mla_kv_append_kernel<1>"] != before["mla_kv_append_kernel<1>"]
+    assert after["mla_kv_append_kernel<0>"] == before["mla_kv_append_kernel<0>"]
+
+
+def test_short_names():
+    assert libbuild.kernel_short_name(
+        "_ZN3mla12_GLOBAL__N_117mla_decode_kernelILi1ELi4EEEvNS_10DecodeArgsE") == \
+        "mla_decode_kernel<1, 4>"
+    assert libbuild.kernel_short_name(
+        "_ZN3mla12_GLOBAL__N_118mla_combine_kernelENS_11CombineArgsE") == "mla_combine_kernel"
