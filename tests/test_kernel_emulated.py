@@ -277,3 +277,20 @@ def test_emulated_restart_storm_with_rising_scores(kv_dtype):
     assert L[0, 0, 0] * math.log2(math.e) > 9 * 32
     out, lse, _ = harness.run(case, 1, 1, env_extra=MODES["wait-lockstep"])
     _check(case, out, lse)
+
+
+# ---------------------------------------------------------------- full-length sequences
+# The longest sequences of the workloads at their full length, through the
+# emulated kernels under AddressSanitizer: 32768 keys with an e4m3 cache (the
+# long-context and ragged-serving workloads' maximum), and 8192 keys with two
+# draft tokens (the MTP-verification maximum), split over 16 workgroups as a
+# full-size plan splits them.
+
+
+@pytest.mark.parametrize("L,q,kv_dtype", [(32768, 1, "fp8_e4m3"), (8192, 2, "bf16")])
+def test_emulated_full_length_sequence(L, q, kv_dtype):
+    case = make_case(kv_lens=[L], q_lens=[q], num_heads=128, seed=51, kv_dtype=kv_dtype,
+                     sm_scale=1 / math.sqrt(192))
+    out, lse, meta = harness.run(case, 16, 1, env_extra=MODES["wait-lockstep"], timeout=1200)
+    assert meta["num_partials"] >= 8
+    _check(case, out, lse)
