@@ -153,3 +153,31 @@ def test_lowest_code_wins():
     kvl = case.kv_lens.copy()
     kvl[2] = -1
     assert harness.run_check(case, 16, kv_lens=kvl, block_table=bt)[1:] == (LENGTHS, 2)
+
+
+def test_every_plan_of_random_shapes_passes_and_a_damaged_one_fails():
+    """Seeded random shapes, lengths (zero-length and idle sequences included),
+    workgroup counts and phases: the planner's image always passes the check,
+    and one damaged word in an item (its key end past the sequence) always
+    fails it."""
+    rng = np.random.default_rng(2024)
+    for trial in range(24):
+        B = int(rng.integers(1, 10))
+        H = int(rng.choice([16, 32, 128]))
+        qmax = int(rng.integers(1, 5))
+        kvd = str(rng.choice(["bf16", "fp8_e4m3"]))
+        P = int(rng.choice([64, 256] if kvd == "fp8_e4m3" else [16, 64, 256]))
+        ql = rng.integers(0, qmax + 1, size=B)
+        kvl = np.where(ql > 0, rng.integers(0, 3000, size=B) + ql, rng.integers(0, 50, size=B))
+        phases = int(rng.choice([1, 2, 4]))
+        nwg = phases * int(rng.integers(1, 24))
+        case = make_case(kv_lens=kvl.tolist(), q_lens=ql.tolist(), num_heads=H, page_size=P,
+                         kv_dtype=kvd, max_q_len=qmax, seed=trial, sm_scale=1 / math.sqrt(192))
+        st, code, idx, w = harness.run_check(case, nwg, phases=phases, want_plan=True)
+        assert (st, code, idx) == (0, OK, 0), (trial, code, idx)
+        items = w[w[9]: w[9] + 8 * w[3]].reshape(-1, 8)
+        if len(items):
+            n = int(rng.integers(0, len(items)))
+            b = int(items[n, 0])
+            poke = [(int(w[9]) + 8 * n + 3, int(case.kv_lens[b]) + 1)]
+            assert harness.run_check(case, nwg, phases=phases, pokes=poke)[1] == ITEM, trial
