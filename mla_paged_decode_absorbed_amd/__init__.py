@@ -167,6 +167,37 @@ def _check(status: int, where: str):
         raise MLAError(status, where)
 
 
+def _sized(dev, named):
+    """Every (name, tensor, bytes, element size) given a tensor must be
+    contiguous, on `dev` and exactly that many bytes of that element size: the
+    C ABI takes bare device pointers, so a tensor of another size would make
+    the kernels read or write outside it."""
+    for name, t, nbytes, esize in named:
+        if t is None:
+            continue
+        if not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be contiguous and on {dev}")
+        if t.element_size() != esize or t.numel() * t.element_size() != nbytes:
+            raise ValueError(f"{name} must hold {nbytes // esize} elements of {esize} bytes, "
+                             f"not {t.numel()} of {t.element_size()}")
+
+
+def _decode_sizes(shape, q, kv_cache, kv_scale, block_table, kv_lens, q_lens, out=None, lse=None):
+    B, qmax, H = shape.batch, shape.max_q_len, shape.num_heads
+    NP, P = shape.num_pages, shape.page_size
+    fp8 = shape.kv_dtype == KV_FP8_E4M3
+    if fp8 and kv_scale is None:
+        raise ValueError("an e4m3 cache needs kv_scale")
+    rows = B * qmax * H
+    _sized(q.device, [
+        ("q", q, rows * (D_LATENT + D_ROPE) * 2, 2),
+        ("kv_cache", kv_cache, NP * P * (D_LATENT + D_ROPE) * (1 if fp8 else 2), 1 if fp8 else 2),
+        ("kv_scale", kv_scale if fp8 else None, NP * P * 4, 4),
+        ("block_table", block_table, B * shape.max_pages_per_seq * 4, 4),
+        ("kv_lens", kv_lens, B * 4, 4), ("q_lens", q_lens, B * 4, 4),
+        ("out", out, rows * D_LATENT * 2, 2), ("lse", lse, rows * 4, 4)])
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -312,12 +343,15 @@ def check(shape: Shape, pl: Plan, block_table, kv_lens, q_lens=None, err=None, s
     given; with ``wait=False`` nothing is synchronised and the codes stay in
     ``err``."""
     import torch
-    lib = load_library()
     dev = kv_lens.device
     if err is None:
         err = torch.empty(2, dtype=torch.int32, device=dev)
     if err.dtype != torch.int32 or err.numel() < 2 or not err.is_contiguous():
         raise ValueError("err must be a contiguous int32 tensor of two elements")
+    B = shape.batch
+    _sized(dev, [("block_table", block_table, B * shape.max_pages_per_seq * 4, 4),
+                 ("kv_lens", kv_lens, B * 4, 4), ("q_lens", q_lens, B * 4, 4)])
+    lib = load_library()
     st = lib.mla_decode_check(ctypes.byref(shape), ctypes.byref(pl.info), _ptr(pl.device),
                               _ptr(block_table), _ptr(kv_lens), _ptr(q_lens), _ptr(err),
                               _stream(stream))
@@ -354,9 +388,7 @@ def decode(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm
         raise ValueError("q must be a contiguous bfloat16 tensor")
     if tuple(q.shape) != (B, qmax, H, D_LATENT + D_ROPE):
         raise ValueError(f"q shape {tuple(q.shape)} does not match the shape struct")
-    for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("kv_lens", kv_lens)):
-        if not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name} must be contiguous and on {dev}")
+    _decode_sizes(shape, q, kv_cache, kv_scale, block_table, kv_lens, q_lens, out, lse)
     if out is None:
         out = torch.empty((B, qmax, H, D_LATENT), dtype=torch.bfloat16, device=dev)
     if lse is None:
@@ -421,16 +453,15 @@ def tree_attend(shape: Shape, q, kv_cache, block_table, kv_lens, q_lens, tree_ma
     place (``mla_tree_attend``).  tree_mask [B, max_q_len] int32/uint32 on the
     device: bit k of word t lets draft token t see draft k."""
     import torch
-    lib = load_library()
     B, qmax = shape.batch, shape.max_q_len
     if tuple(tree_mask.shape) != (B, qmax) or tree_mask.element_size() != 4:
         raise ValueError("tree_mask must be a [batch, max_q_len] tensor of 32-bit words")
     if lse is None or lse.dtype != torch.float32:
         raise ValueError("lse (the prefix decode's) is required")
-    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
-                    ("kv_lens", kv_lens), ("tree_mask", tree_mask), ("out", out), ("lse", lse)):
-        if not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be contiguous and on {q.device}")
+    if not tree_mask.is_contiguous() or tree_mask.device != q.device:
+        raise ValueError(f"tree_mask must be contiguous and on {q.device}")
+    _decode_sizes(shape, q, kv_cache, kv_scale, block_table, kv_lens, q_lens, out, lse)
+    lib = load_library()
     st = lib.mla_tree_attend(ctypes.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(kv_scale),
                              _ptr(block_table), _ptr(kv_lens), _ptr(q_lens), _ptr(tree_mask),
                              float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
@@ -485,21 +516,27 @@ def prefill_alloc_quant(shape: PrefillShape, device) -> PrefillQuant:
         v_scale=torch.empty((nb, H, PREFILL_D_V), dtype=torch.float32, device=device))
 
 
-def _prefill_tensors_ok(dev, named):
-    for name, t in named:
-        if t is None or not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+def _prefill_quant_sizes(shape: PrefillShape, dev, quant: PrefillQuant):
+    T, H, nb = shape.num_tokens, shape.num_heads, shape.num_blocks
+    _sized(dev, [("q_codes", quant.q_codes, T * H * PREFILL_D_QK, 1),
+                 ("q_scale", quant.q_scale, T * H * 4, 4),
+                 ("k_codes", quant.k_codes, T * H * PREFILL_D_QK, 1),
+                 ("k_scale", quant.k_scale, nb * H * 4, 4),
+                 ("v_codes", quant.v_codes, nb * H * PREFILL_D_V * PREFILL_BLOCK, 1),
+                 ("v_scale", quant.v_scale, nb * H * PREFILL_D_V * 4, 4)])
 
 
 def prefill_quantize(shape: PrefillShape, cu_seqlens, q, k, v, quant: PrefillQuant = None,
                      stream=None) -> PrefillQuant:
     """``mla_prefill_quantize``: packed bf16 q, k [T, H, 192] and v [T, H, 128]
     to INT8 / e4m3 codes and scales; cu_seqlens [S + 1] int32 on the device."""
-    lib = load_library()
     quant = prefill_alloc_quant(shape, q.device) if quant is None else quant
-    _prefill_tensors_ok(q.device, [("cu_seqlens", cu_seqlens), ("q", q), ("k", k), ("v", v),
-                                   ("q_codes", quant.q_codes), ("k_codes", quant.k_codes),
-                                   ("v_codes", quant.v_codes)])
+    T, H = shape.num_tokens, shape.num_heads
+    _sized(q.device, [("cu_seqlens", cu_seqlens, (shape.num_seqs + 1) * 4, 4),
+                      ("q", q, T * H * PREFILL_D_QK * 2, 2), ("k", k, T * H * PREFILL_D_QK * 2, 2),
+                      ("v", v, T * H * PREFILL_D_V * 2, 2)])
+    _prefill_quant_sizes(shape, q.device, quant)
+    lib = load_library()
     st = lib.mla_prefill_quantize(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(quant.q_codes), _ptr(quant.q_scale), _ptr(quant.k_codes),
                                   _ptr(quant.k_scale), _ptr(quant.v_codes), _ptr(quant.v_scale),
@@ -513,14 +550,16 @@ def prefill_attn(shape: PrefillShape, cu_seqlens, quant: PrefillQuant, sm_scale:
     """``mla_prefill_attn``: causal attention from the quantized inputs.
     Returns (O [T, H, 128] bf16, LSE [T, H] fp32)."""
     import torch
-    lib = load_library()
     dev = quant.q_codes.device
     T, H = shape.num_tokens, shape.num_heads
     if out is None:
         out = torch.empty((T, H, PREFILL_D_V), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    _prefill_tensors_ok(dev, [("cu_seqlens", cu_seqlens), ("out", out), ("lse", lse)])
+    _sized(dev, [("cu_seqlens", cu_seqlens, (shape.num_seqs + 1) * 4, 4),
+                 ("out", out, T * H * PREFILL_D_V * 2, 2), ("lse", lse, T * H * 4, 4)])
+    _prefill_quant_sizes(shape, dev, quant)
+    lib = load_library()
     st = lib.mla_prefill_attn(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(quant.q_codes),
                               _ptr(quant.q_scale), _ptr(quant.k_codes), _ptr(quant.k_scale),
                               _ptr(quant.v_codes), _ptr(quant.v_scale), float(sm_scale), _ptr(out),
