@@ -47,7 +47,16 @@ DECODE_KERNEL = "mla_decode_kernel"
 PAIRS_KERNEL = "mla_decode_kernel_pairs"
 
 
+W8_KERNEL = "mla_decode_kernel_w8"
+
+
+def _w8_selected(kv_dtype: str, phases: int) -> bool:
+    return os.environ.get("MLA_DECODE_KERNEL") == "w8" and kv_dtype == "bf16" and phases == 1
+
+
 def decode_kernel_name(kv_dtype: str, phases: int) -> str:
+    if _w8_selected(kv_dtype, phases):
+        return W8_KERNEL
     return PAIRS_KERNEL if kv_dtype == "bf16" and phases == 1 else DECODE_KERNEL
 
 
@@ -113,6 +122,8 @@ def code_object_hash(source: str, kernel: str):
 
 def decode_kernel_symbol(kv_dtype: str, phases: int) -> str:
     """The instantiation a plan launches, as the build's fingerprints name it."""
+    if _w8_selected(kv_dtype, phases):
+        return "mla_decode_kernel_w8<0>"
     if kv_dtype == "bf16" and phases == 1:
         return "mla_decode_kernel_pairs<0>"
     return f"mla_decode_kernel<{0 if kv_dtype == 'bf16' else 1}, {phases}>"
@@ -499,6 +510,9 @@ def main() -> int:
     ap.add_argument("--num-workgroups", type=int, default=0,
                     help="plan the decode for this many workgroups instead of one per CU "
                          "(per-CU throughput against the number of CUs at work)")
+    ap.add_argument("--decode-kernel", choices=("default", "w8"), default="default",
+                    help="w8: time the two-waves-per-SIMD candidate (bf16 cache, one-phase "
+                         "plans; not yet run on a GPU) instead of the library's default kernel")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")
@@ -516,6 +530,8 @@ def main() -> int:
     import mla_paged_decode_absorbed_amd as mla
     from workloads import workload
 
+    if args.decode_kernel == "w8":
+        os.environ["MLA_DECODE_KERNEL"] = "w8"
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -708,7 +724,8 @@ def main() -> int:
             "TFLOP/s", "mfma"
     kernel_name = decode_kernel_name(case.kv_dtype, pl.phases)
     kernel_sym = decode_kernel_symbol(case.kv_dtype, pl.phases)
-    traffic = read_traffic(args.workload, kernel_name, symbol=kernel_sym)
+    kernel_src = "decode_w8_kernel.hip" if kernel_name == W8_KERNEL else "decode_kernel.hip"
+    traffic = read_traffic(args.workload, kernel_name, (kernel_src,), symbol=kernel_sym)
 
     res = {
         "metric": METRIC,
@@ -755,7 +772,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "input_sets": nsets,
         "kernel_source_sha256": kernel_source_hash(),
-        "code_object_sha256": code_object_hash("decode_kernel.hip", kernel_sym),
+        "code_object_sha256": code_object_hash(kernel_src, kernel_sym),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

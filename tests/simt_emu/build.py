@@ -22,7 +22,7 @@ KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
                 "plan_kernel.hip", "tree_kernel.hip", "api.cpp", "plan.cpp", "kernels.h",
                 "append.h", "plan_core.h", "plan_device.h", "tree.h", "plan_layout.h",
                 "validate.h", "prefill.h", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip",
-                "check.h", "check_kernel.hip"]
+                "check.h", "check_kernel.hip", "decode_w8_kernel.hip"]
 
 
 def compiler() -> str:
@@ -63,7 +63,7 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
                                              "append_kernel.hip", "plan_kernel.hip",
                                              "tree_kernel.hip", "prefill_quant_kernel.hip",
                                              "prefill_attn_kernel.hip", "check_kernel.hip",
-                                             "api.cpp", "plan.cpp")]
+                                             "decode_w8_kernel.hip", "api.cpp", "plan.cpp")]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     objs = []
     for u in units:

@@ -100,3 +100,14 @@ def test_build_manifest_matches_the_library_objects():
         for ph in (1, 2, 4):
             sym = bench.decode_kernel_symbol(kvd, ph)
             assert bench.code_object_hash("decode_kernel.hip", sym) == m["decode_kernel.hip"][sym]
+
+
+def test_candidate_kernel_naming(monkeypatch):
+    monkeypatch.setenv("MLA_DECODE_KERNEL", "w8")
+    assert bench.decode_kernel_name("bf16", 1) == "mla_decode_kernel_w8"
+    assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_w8<0>"
+    # plans the candidate does not cover keep the library kernels
+    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel<1, 1>"
+    assert bench.decode_kernel_name("bf16", 4) == "mla_decode_kernel"
+    monkeypatch.delenv("MLA_DECODE_KERNEL")
+    assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"

@@ -269,6 +269,20 @@ def _rising_scores_case(kv_dtype, L=300, H=16):
     return case
 
 
+@pytest.mark.xfail(strict=True, raises=RuntimeError, reason=(
+    "known race in the library kernels' restart flag: a wave that reads the single flag after "
+    "a faster wave set it in the same round leaves the round loop one barrier early; the "
+    "drift schedule reaches it and reports the barrier deadlock.  On the GPU the flag is read "
+    "right after the barrier and set no sooner than one QK step and softmax later (one wave per "
+    "SIMD); the fix (per-wave flags by round parity) is in decode_w8_kernel.hip and would "
+    "change the validated machine code"))
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_library_restart_flag_under_drift(kv_dtype):
+    case = _rising_scores_case(kv_dtype)
+    out, lse, _ = harness.run(case, 1, 1, env_extra=MODES["wait-drift"])
+    _check(case, out, lse)
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
 def test_emulated_restart_storm_with_rising_scores(kv_dtype):
     case = _rising_scores_case(kv_dtype)
@@ -294,3 +308,67 @@ def test_emulated_full_length_sequence(L, q, kv_dtype):
     out, lse, meta = harness.run(case, 16, 1, env_extra=MODES["wait-lockstep"], timeout=1200)
     assert meta["num_partials"] >= 8
     _check(case, out, lse)
+
+
+# ---------------------------------------------------------------- two waves per SIMD
+# The candidate decode kernel (decode_w8_kernel.hip, chosen by
+# MLA_DECODE_KERNEL=w8 for bf16 one-phase plans): eight waves of 16 rows, two
+# per SIMD.  The same cases as the default kernel's, in both copy-landing
+# modes: several items per workgroup, ragged tails inside a pair's second
+# stage, empty sequences, up to 8 draft tokens over several row blocks,
+# small and large pages, the restart paths and a full-length sequence.
+
+W8 = {"MLA_DECODE_KERNEL": "w8"}
+
+
+@pytest.mark.parametrize("mode", ["wait-lockstep", "issue-drift"])
+@pytest.mark.parametrize("kv_lens,q_lens,nwg,H,P", [
+    ([3000, 700, 65, 1800], [1, 2, 1, 2], 1, 128, 64),    # six items on one workgroup
+    ([1, 15, 16, 17, 129, 31, 33], [1, 1, 2, 1, 2, 1, 2], 12, 128, 64),
+    ([0, 200, 64], [0, 2, 1], 5, 128, 64),                 # empty sequence without query
+    ([64, 64, 130, 18], [1, 1, 1, 1], 1, 128, 64),         # one-round items back to back
+    ([77, 300], [4, 1], 6, 16, 16),
+    ([77, 300], [8, 1], 6, 16, 16),                        # longest draft
+    ([700, 130], [2, 2], 64, 128, 256),                    # many splits, large pages
+])
+def test_w8_kernel_matches_oracle(kv_lens, q_lens, nwg, H, P, mode):
+    case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, num_heads=H, page_size=P,
+                     sm_scale=1 / math.sqrt(192), max_q_len=max(2, max(q_lens)))
+    out, lse, meta = harness.run(case, nwg, 1, env_extra={**MODES[mode], **W8})
+    _check(case, out, lse)
+
+
+def test_w8_kernel_restarts():
+    # the drift schedules let one wave overshoot (and publish it) a whole
+    # round ahead of the others: the round-parity flags keep them at one barrier
+    for case in (_late_dominant_key_case(), _rising_scores_case("bf16")):
+        for mode in ("wait-lockstep", "wait-drift", "issue-drift"):
+            out, lse, _ = harness.run(case, 1, 1, env_extra={**MODES[mode], **W8})
+            _check(case, out, lse)
+
+
+def test_w8_kernel_fixed_shape_plan_and_full_length():
+    case = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
+                     sm_scale=1 / math.sqrt(192))
+    out, lse, _ = harness.run(case, 8, 1, fixed=True, env_extra={**MODES["issue-drift"], **W8})
+    _check(case, out, lse)
+    case = make_case(kv_lens=[8192], q_lens=[2], num_heads=128, seed=51,
+                     sm_scale=1 / math.sqrt(192))
+    out, lse, _ = harness.run(case, 16, 1, env_extra={**MODES["wait-lockstep"], **W8},
+                              timeout=1200)
+    _check(case, out, lse)
+
+
+def test_w8_emulation_catches_a_missing_barrier(tmp_path):
+    # the candidate with its per-round barrier taken out (planted on the CPU):
+    # a wave refills ring stages other waves still read
+    from tests.simt_emu import build as _b
+    src = open(os.path.join(_b.CSRC, "decode_w8_kernel.hip")).read()
+    marker = "barrier();   // tiles of round j come from all waves"
+    assert src.count(marker) == 1
+    binary = _b.build(tag="w8_planted_race", patches={"decode_w8_kernel.hip": [
+        (marker, "/* barrier removed */")]})
+    case = make_case(kv_lens=[700, 300], q_lens=[2, 1], seed=5, sm_scale=1 / math.sqrt(192))
+    out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={**MODES["issue-drift"], **W8})
+    with pytest.raises(AssertionError):
+        _check(case, out, lse)

@@ -32,7 +32,12 @@ pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 
 SOURCES = {
     "library": os.path.join(CSRC, "decode_kernel.hip"),
+    # the two-waves-per-SIMD candidate (opt-in, MLA_DECODE_KERNEL=w8)
+    "w8": os.path.join(CSRC, "decode_w8_kernel.hip"),
 }
+# kernels per source, and copies per wave and round (a branch-free run)
+EXPECTED_KERNELS = {"library": 6, "w8": 1}
+COPIES_PER_ROUND = {"library": {"bf16": (18, 0), "e4m3": (9, 1)}, "w8": {"bf16": (9, 0)}}
 
 
 @pytest.fixture(scope="module", params=sorted(SOURCES))
@@ -79,7 +84,7 @@ def _key_loop_blocks(blocks):
 
 def test_all_instantiations_present(isa):
     ks = _kernels(isa[1])
-    assert len(ks) == 6, sorted(ks)
+    assert len(ks) == EXPECTED_KERNELS[isa[0]], sorted(ks)
 
 
 # The e4m3 kernel with four phases (opt-in through MLA_PHASES=4, never chosen
@@ -194,6 +199,8 @@ def test_hazard_walk_follows_branches():
 
 def test_default_kernel_tile_work(isa):
     which, text = isa
+    if which != "library":
+        pytest.skip("the library's default kernel")
     ks = _kernels(text)
     name = next(n for n in ks if "mla_decode_kernel_pairsILi0E" in n)
     # per 32 keys: 36 QK (32x32x16) + 32 PV MFMAs, 36 K-fragment and 64
@@ -503,6 +510,7 @@ def test_literal_vmcnt_waits_count_whole_rounds(isa):
         literals = {int(m.group(1)) for _, ins in blocks for i, a in ins if a is not None
                     for m in [re.match(r"s_waitcnt vmcnt\((\d+)\)$", i)] if m}
         assert literals <= ({0, 10, 20} if e4m3 else {0}), (name, literals)
+        want = COPIES_PER_ROUND[isa[0]]["e4m3" if e4m3 else "bf16"]
         for lab, ins in blocks:
             idx = [j for j, (i, _a) in enumerate(ins) if i.startswith("global_load_lds")]
             if not idx:
@@ -510,8 +518,31 @@ def test_literal_vmcnt_waits_count_whole_rounds(isa):
             run = [i for i, _a in ins[idx[0]: idx[-1] + 1]]
             x4 = sum(i.startswith("global_load_lds_dwordx4") for i in run)
             x1 = sum(i.startswith("global_load_lds_dword ") for i in run)
-            assert (x4, x1) == ((9, 1) if e4m3 else (18, 0)), (name, lab, x4, x1)
+            assert (x4, x1) == want, (name, lab, x4, x1)
             # no branch and no other vector-memory operation inside the run
             assert not [i for i in run if i.startswith(("s_cbranch", "s_branch", "global_load_d",
                                                          "global_store", "buffer_", "scratch_",
                                                          "flat_"))], (name, lab)
+
+
+def test_two_waves_per_simd_register_budget(isa):
+    """The candidate runs eight waves per CU, two per SIMD: each wave must fit
+    256 registers (VGPRs and AGPRs together) with nothing spilled, and its key
+    loop keeps 2 x 18 QK and 32 PV steps of v_mfma_f32_16x16x32_bf16 per 32 keys."""
+    which, text = isa
+    if which != "w8":
+        pytest.skip("the two-waves-per-SIMD candidate")
+    v = int(re.search(r"\.vgpr_count:\s+(\d+)", text).group(1))
+    a = int(re.search(r"\.agpr_count:\s+(\d+)", text).group(1))
+    assert v + a <= 256, (v, a)
+    assert int(re.search(r"\.vgpr_spill_count:\s+(\d+)", text).group(1)) == 0
+    assert int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", text).group(1)) == 0
+    assert "amdhsa_next_free_vgpr" in text
+    (name, blocks), = _kernels(text).items()
+    loop = _key_loop_blocks(blocks)
+    mfma = sum(sum(i.startswith("v_mfma_f32_16x16x32_bf16") for i in ins) for _, ins in loop)
+    tr = sum(sum(i.startswith("ds_read_b64_tr_b16") for i in ins) for _, ins in loop)
+    k = sum(sum(i.startswith("ds_read_b128") for i in ins) for _, ins in loop)
+    assert mfma % 68 == 0 and mfma >= 68, mfma
+    steps = mfma // 68
+    assert (tr, k) == (64 * steps, 36 * steps), (tr, k, steps)
