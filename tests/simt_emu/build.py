@@ -10,6 +10,7 @@ from __future__ import annotations
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
@@ -65,14 +66,16 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
                                              "prefill_attn_kernel.hip", "check_kernel.hip",
                                              "decode_w8_kernel.hip", "api.cpp", "plan.cpp")]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
-    objs = []
-    for u in units:
+    def compile_unit(u):
         obj = os.path.join(out, os.path.basename(u) + ".o")
         cmd = [compiler(), *flags, "-x", "c++", "-c", u, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"emulator build failed on {u}:\n{res.stderr[-4000:]}")
-        objs.append(obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_unit, units))
     binary = os.path.join(out, "run_case")
     cmd = [compiler(), *flags, *objs, "-o", binary]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -86,6 +86,17 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
     return out, lse, info
 
 
+def run_many(jobs, workers: int = 6):
+    """run(case, num_workgroups, phases, **kw) for each (case, num_workgroups,
+    phases, kw) of `jobs`, several emulator processes at a time; the results
+    in order (each process is independent: its own files and buffers)."""
+    from concurrent.futures import ThreadPoolExecutor
+    ensure_built()
+    with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        futs = [ex.submit(run, c, n, p, **kw) for c, n, p, kw in jobs]
+        return [f.result() for f in futs]
+
+
 def run_append(kv, kv_scale, block_table, kv_lens, new_lens, new_rows_bits, page_size: int,
                kv_dtype: str, with_counter: bool = True, timeout: float = 600.0):
     """mla_kv_append on the emulator.  Returns (kv', kv_scale' or None, skipped

@@ -175,8 +175,8 @@ def test_emulated_restart_on_late_dominant_key():
 def test_pair_stepping_matches_oracle(kv_lens, q_lens, nwg, kv_dtype, H, P):
     case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, kv_dtype=kv_dtype, num_heads=H,
                      page_size=P, sm_scale=1 / math.sqrt(192))
-    for mode in ("wait-lockstep", "issue-drift"):
-        out, lse, meta = harness.run(case, nwg, 1, env_extra=MODES[mode])
+    jobs = [(case, nwg, 1, dict(env_extra=MODES[mode])) for mode in ("wait-lockstep", "issue-drift")]
+    for out, lse, _meta in harness.run_many(jobs):
         _check(case, out, lse)
 
 
@@ -220,21 +220,21 @@ def test_fifth_fault_case_replays_in_bounds_with_its_plan():
     case = make_case(kv_lens=[700, 64, 1234], q_lens=[2, 1, 1], kv_dtype="fp8_e4m3", seed=22,
                      sm_scale=1 / math.sqrt(192))
     relaid = _relayout(case, 5)
-    env5 = {"MLA_ITEM_COST_ROUNDS": "1"}
+    env5 = {"MLA_ITEM_COST_ROUNDS": "1", **MODES["issue-drift"]}
+    jobs = [(case, 16, 1, dict(want_plan=True)),   # the library's plan
+            (case, 16, 1, dict(binary=binary, env_extra=env5, want_plan=True)),
+            (relaid, 16, 1, dict(binary=binary, env_extra=env5, want_plan=True))]
+    lib, *run5 = harness.run_many(jobs)
     # the library's plan: one item per workgroup
-    _, _, meta = harness.run(case, 16, 1, want_plan=True)
-    assert all(len(w) == 1 for w in _plan_items(meta["plan"]))
-    for mode in ("wait-lockstep", "issue-drift"):
-        outs = []
-        for c in (case, relaid):
-            out, lse, meta = harness.run(c, 16, 1, binary=binary, env_extra={**env5, **MODES[mode]},
-                                         want_plan=True)
-            per_wg = _plan_items(meta["plan"])
-            two = [w for w in per_wg if len(w) == 2]
-            assert two == [[(1, 0, 0, 64, -1), (2, 0, 0, 64, two[0][1][4])]], per_wg
-            _check(c, out, lse)
-            outs.append((out.copy(), lse.copy()))
-        assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert all(len(w) == 1 for w in _plan_items(lib[2]["plan"]))
+    outs = []
+    for c, (out, lse, meta) in zip((case, relaid), run5):
+        per_wg = _plan_items(meta["plan"])
+        two = [w for w in per_wg if len(w) == 2]
+        assert two == [[(1, 0, 0, 64, -1), (2, 0, 0, 64, two[0][1][4])]], per_wg
+        _check(c, out, lse)
+        outs.append((out, lse))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
 # ---------------------------------------------------------------- restart storms
@@ -278,7 +278,7 @@ def _rising_scores_case(kv_dtype, L=300, H=16):
     "change the validated machine code"))
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
 def test_library_restart_flag_under_drift(kv_dtype):
-    case = _rising_scores_case(kv_dtype)
+    case = _rising_scores_case(kv_dtype, L=160)
     out, lse, _ = harness.run(case, 1, 1, env_extra=MODES["wait-drift"])
     _check(case, out, lse)
 
@@ -294,20 +294,21 @@ def test_emulated_restart_storm_with_rising_scores(kv_dtype):
 
 
 # ---------------------------------------------------------------- full-length sequences
-# The longest sequences of the workloads at their full length, through the
-# emulated kernels under AddressSanitizer: 32768 keys with an e4m3 cache (the
-# long-context and ragged-serving workloads' maximum), and 8192 keys with two
-# draft tokens (the MTP-verification maximum), split over 16 workgroups as a
-# full-size plan splits them.
+# Full-length sequences through the emulated kernels under AddressSanitizer:
+# 32768 keys with an e4m3 cache (the long-context and ragged-serving
+# workloads' maximum) and 4096 keys with two draft tokens (the DeepSeek-V3
+# decode maximum), split over 16 workgroups as a full-size plan splits them.
 
 
-@pytest.mark.parametrize("L,q,kv_dtype", [(32768, 1, "fp8_e4m3"), (8192, 2, "bf16")])
-def test_emulated_full_length_sequence(L, q, kv_dtype):
-    case = make_case(kv_lens=[L], q_lens=[q], num_heads=128, seed=51, kv_dtype=kv_dtype,
-                     sm_scale=1 / math.sqrt(192))
-    out, lse, meta = harness.run(case, 16, 1, env_extra=MODES["wait-lockstep"], timeout=1200)
-    assert meta["num_partials"] >= 8
-    _check(case, out, lse)
+def test_emulated_full_length_sequences():
+    cases = [make_case(kv_lens=[L], q_lens=[q], num_heads=128, seed=51, kv_dtype=kvd,
+                       sm_scale=1 / math.sqrt(192))
+             for L, q, kvd in ((32768, 1, "fp8_e4m3"), (4096, 2, "bf16"))]
+    res = harness.run_many([(c, 16, 1, dict(env_extra=MODES["wait-lockstep"], timeout=1200))
+                            for c in cases])
+    for c, (out, lse, meta) in zip(cases, res):
+        assert meta["num_partials"] >= 8
+        _check(c, out, lse)
 
 
 # ---------------------------------------------------------------- two waves per SIMD
@@ -321,42 +322,47 @@ def test_emulated_full_length_sequence(L, q, kv_dtype):
 W8 = {"MLA_DECODE_KERNEL": "w8"}
 
 
-@pytest.mark.parametrize("mode", ["wait-lockstep", "issue-drift"])
-@pytest.mark.parametrize("kv_lens,q_lens,nwg,H,P", [
-    ([3000, 700, 65, 1800], [1, 2, 1, 2], 1, 128, 64),    # six items on one workgroup
+W8_CASES = [
+    # (kv_lens, q_lens, num_workgroups, H, page size)
+    ([1500, 700, 65, 900], [1, 2, 1, 2], 1, 128, 64),     # six items on one workgroup
     ([1, 15, 16, 17, 129, 31, 33], [1, 1, 2, 1, 2, 1, 2], 12, 128, 64),
     ([0, 200, 64], [0, 2, 1], 5, 128, 64),                 # empty sequence without query
     ([64, 64, 130, 18], [1, 1, 1, 1], 1, 128, 64),         # one-round items back to back
     ([77, 300], [4, 1], 6, 16, 16),
     ([77, 300], [8, 1], 6, 16, 16),                        # longest draft
     ([700, 130], [2, 2], 64, 128, 256),                    # many splits, large pages
-])
-def test_w8_kernel_matches_oracle(kv_lens, q_lens, nwg, H, P, mode):
-    case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=37, num_heads=H, page_size=P,
-                     sm_scale=1 / math.sqrt(192), max_q_len=max(2, max(q_lens)))
-    out, lse, meta = harness.run(case, nwg, 1, env_extra={**MODES[mode], **W8})
-    _check(case, out, lse)
+]
+
+
+def test_w8_kernel_matches_oracle():
+    cases = [make_case(kv_lens=kv, q_lens=ql, seed=37, num_heads=H, page_size=P,
+                       sm_scale=1 / math.sqrt(192), max_q_len=max(2, max(ql)))
+             for kv, ql, _n, H, P in W8_CASES]
+    jobs = [(c, spec[2], 1, dict(env_extra={**MODES[mode], **W8}))
+            for c, spec in zip(cases, W8_CASES) for mode in ("wait-lockstep", "issue-drift")]
+    for (c, n, _p, kw), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
 
 
 def test_w8_kernel_restarts():
     # the drift schedules let one wave overshoot (and publish it) a whole
     # round ahead of the others: the round-parity flags keep them at one barrier
-    for case in (_late_dominant_key_case(), _rising_scores_case("bf16")):
-        for mode in ("wait-lockstep", "wait-drift", "issue-drift"):
-            out, lse, _ = harness.run(case, 1, 1, env_extra={**MODES[mode], **W8})
-            _check(case, out, lse)
+    jobs = [(c, 1, 1, dict(env_extra={**MODES[mode], **W8}))
+            for c in (_late_dominant_key_case(), _rising_scores_case("bf16"))
+            for mode in ("wait-lockstep", "wait-drift", "issue-drift")]
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
 
 
 def test_w8_kernel_fixed_shape_plan_and_full_length():
-    case = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
+    fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
+                      sm_scale=1 / math.sqrt(192))
+    full = make_case(kv_lens=[4096], q_lens=[2], num_heads=128, seed=51,
                      sm_scale=1 / math.sqrt(192))
-    out, lse, _ = harness.run(case, 8, 1, fixed=True, env_extra={**MODES["issue-drift"], **W8})
-    _check(case, out, lse)
-    case = make_case(kv_lens=[8192], q_lens=[2], num_heads=128, seed=51,
-                     sm_scale=1 / math.sqrt(192))
-    out, lse, _ = harness.run(case, 16, 1, env_extra={**MODES["wait-lockstep"], **W8},
-                              timeout=1200)
-    _check(case, out, lse)
+    jobs = [(fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **W8})),
+            (full, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **W8}, timeout=1200))]
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
 
 
 def test_w8_emulation_catches_a_missing_barrier(tmp_path):
