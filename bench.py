@@ -51,7 +51,7 @@ W8_KERNEL = "mla_decode_kernel_w8"
 
 
 def _w8_selected(kv_dtype: str, phases: int) -> bool:
-    return os.environ.get("MLA_DECODE_KERNEL") == "w8" and kv_dtype == "bf16" and phases == 1
+    return os.environ.get("MLA_DECODE_KERNEL") == "w8" and phases == 1
 
 
 def decode_kernel_name(kv_dtype: str, phases: int) -> str:
@@ -123,7 +123,7 @@ def code_object_hash(source: str, kernel: str):
 def decode_kernel_symbol(kv_dtype: str, phases: int) -> str:
     """The instantiation a plan launches, as the build's fingerprints name it."""
     if _w8_selected(kv_dtype, phases):
-        return "mla_decode_kernel_w8<0>"
+        return f"mla_decode_kernel_w8<{0 if kv_dtype == 'bf16' else 1}>"
     if kv_dtype == "bf16" and phases == 1:
         return "mla_decode_kernel_pairs<0>"
     return f"mla_decode_kernel<{0 if kv_dtype == 'bf16' else 1}, {phases}>"
@@ -511,8 +511,9 @@ def main() -> int:
                     help="plan the decode for this many workgroups instead of one per CU "
                          "(per-CU throughput against the number of CUs at work)")
     ap.add_argument("--decode-kernel", choices=("default", "w8"), default="default",
-                    help="w8: time the two-waves-per-SIMD candidate (bf16 cache, one-phase "
-                         "plans; not yet run on a GPU) instead of the library's default kernel")
+                    help="w8: time the two-waves-per-SIMD candidate (one-phase plans, bf16 or "
+                         "e4m3 cache; not yet run on a GPU) instead of the library's default "
+                         "kernel")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")

@@ -187,12 +187,11 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   a.phases = info->phases;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // MLA_DECODE_KERNEL=w8 selects the two-waves-per-SIMD candidate for the
-  // plans it covers (bf16 cache, one phase); every other plan, and the
+  // plans it covers (one phase, either cache type); every other plan, and the
   // default, runs the library's decode kernels.
   const char* variant = std::getenv("MLA_DECODE_KERNEL");
-  if (variant && std::strcmp(variant, "w8") == 0 && shape->kv_dtype == MLA_KV_BF16 &&
-      info->phases == 1)
-    return launch_decode_w8(a, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  if (variant && std::strcmp(variant, "w8") == 0 && info->phases == 1)
+    return launch_decode_w8(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   return launch_decode(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

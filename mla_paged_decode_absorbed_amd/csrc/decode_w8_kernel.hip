@@ -1,31 +1,40 @@
 // Weight-absorbed MLA decode over a paged latent cache, two waves per SIMD:
-// a candidate successor of mla_decode_kernel_pairs for bf16 caches and
-// one-phase plans.  It computes what the library's decode kernels compute
-// (same plan, same work items, same outputs and partials):
+// a candidate successor of the library's decode kernels for one-phase plans,
+// bf16 or e4m3 cache.  It computes what they compute (same plan, same work
+// items, same outputs and partials):
 //   s_j = scale * <q, c_j> over the visible cached rows, O = softmax(s) .
 //   latent, LSE (KsanaLLM 0.6.0 page, weight-absorbed MLA for decode;
 //   PaddlePaddle 3.0 inference page, draft tokens verified in one pass;
-//   FlashAttention-3 in DeepSeek-R1 page, chapter 2: LSE and split-K).
+//   FlashAttention-3 in DeepSeek-R1 page, chapter 2: LSE and split-K; same
+//   page, section 3.1: per-token fp8 cache scales).
 //
-// Why: with one wave per SIMD, mla_decode_kernel_pairs serialises each
-// wave's chain QK^T -> softmax -> PV, and the matrix unit sits idle during
-// the softmax and the LDS waits.  Here the 128 rows of a work item are spread
+// Why: with one wave per SIMD, the library kernels serialise each wave's
+// chain QK^T -> softmax -> PV, and the matrix unit sits idle during the
+// softmax and the LDS waits.  Here the 128 rows of a work item are spread
 // over eight waves of 16 rows, two per SIMD, so one wave's softmax and waits
 // can run under the other wave's MFMAs.  A wave then has 256 registers:
 // Q (16 rows x 576) takes 72, the output accumulator (16 rows x 512 fp32)
 // 128.  Every wave reads every key tile from LDS (twice the LDS reads per key
-// of the four-wave kernel; the layout keeps them free of bank conflicts).
+// of the four-wave kernels; the layout keeps them free of bank conflicts).
 //
 // Mapping onto CDNA4:
 //   * 512 threads (eight wave64s), one workgroup per CU, persistent over its
 //     plan items; wave w owns rows 16w .. 16w + 15 of an item.
-//   * Key tiles of 16 tokens stream HBM -> LDS through the same 8-stage ring
-//     and tile layout as the library kernels, in rounds of four tiles: tile t
-//     of a round is copied by waves t and t + 4, nine 1 KB copies each.
-//   * Keys are processed 32 at a time (two ring stages).  QK^T: S^T[16 keys x
-//     16 rows] = K . Q^T on v_mfma_f32_16x16x32_bf16 for each stage, 18 steps
-//     of 32 dimensions sharing the Q fragment; a lane holds keys 4(lane/16) +
-//     r of its row in each stage.
+//   * bf16: key tiles of 16 tokens stream HBM -> LDS through the library's
+//     8-stage ring and tile layout, in rounds of four tiles: tile t of a
+//     round is copied by waves t and t + 4, nine 1 KB copies each.
+//   * e4m3: a round of 64 keys (36 KB, contiguous in its page) is copied as
+//     it lies into a two-round ring, then widened once per CU, a 32-key pair
+//     at a time, into one of two pair buffers in the bf16 tile layout (exact:
+//     every e4m3 value is a bf16 value); the per-key scale multiplies the
+//     score and the probability, so Q keeps bf16 and the MFMA steps are the
+//     bf16 ones.  Widening in LDS costs each CU one conversion per cached
+//     value, where widening K and V fragments in registers would cost every
+//     wave one.
+//   * Keys are processed 32 at a time (two 16-key stages).  QK^T: S^T[16 keys
+//     x 16 rows] = K . Q^T on v_mfma_f32_16x16x32_bf16 for each stage, 18
+//     steps of 32 dimensions sharing the Q fragment; a lane holds keys
+//     4(lane/16) + r of its row in each stage.
 //   * PV: O^T[16 columns x 16 rows] += V^T . P^T on v_mfma_f32_16x16x32_bf16
 //     for 32 column blocks.  The contraction takes a lane's own 8 keys (four
 //     of each stage) in the order it holds them, so the probabilities are the
@@ -33,14 +42,16 @@
 //     keys of one stage per read.
 //   * The softmax keeps the library kernels' fixed reference max and their
 //     restart when a score overshoots it by more than 32 (log2 units).  The
-//     waves agree on a restart through per-wave flags kept by round parity:
-//     a wave publishes whether round j overshot before the barrier that
-//     opens round j + 1, and every wave reads all flags of round j after that
-//     barrier.  The next write to those flags (round j + 2) happens after the
-//     barrier that opens round j + 2, which every reader has reached, so all
-//     waves see the same flags and leave the round loop at the same barrier.
-//     (A single flag, set while a slower wave may not yet have read it after
-//     the same barrier, lets waves leave at different barriers.)
+//     waves agree on a restart through per-wave flags kept by round (bf16) or
+//     pair (e4m3) parity: a wave publishes whether step j overshot before the
+//     barrier that opens step j + 1, and every wave reads all flags of step j
+//     after that barrier.  The next write to those flags (step j + 2) happens
+//     after the barrier that opens step j + 2, which every reader has
+//     reached, so all waves see the same flags and leave the loop at the same
+//     barrier.  (A single flag, set while a slower wave may not yet have read
+//     it after the same barrier, lets waves leave at different barriers.)
+//   * An item's key range is clamped to the sequence's device length, so a
+//     plan made for longer lengths reads no row past the sequence's pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,9 +72,31 @@ constexpr int kRoundTiles = 4;                // stages per round
 constexpr int kRoundTok = kTileTok * kRoundTiles;
 constexpr int kRowBytes = 1152;               // one bf16 cache row
 constexpr int kTileBytes = kTileTok * kRowBytes;
-constexpr int kStages = 8;                    // two rounds in the ring
-constexpr int kFlagOff = kStages * kTileBytes;   // overshoot flags [2][8] (round parity, wave)
-constexpr int kSmemBytes = kFlagOff + 2 * 8 * 4;
+constexpr int kF8RowBytes = 576;              // one e4m3 cache row
+constexpr int kF8RoundBytes = kRoundTok * kF8RowBytes;   // one round of e4m3 rows, 36 KB
+constexpr int kF8Copies = kF8RoundBytes / 1024;          // its 1 KB copies
+constexpr int kScaleRoundBytes = kRoundTok * 4;          // one round's fp32 scales
+
+// LDS map.  bf16: an 8-stage ring of key tiles (two rounds), then the
+// restart flags [2][8] (round parity, wave).  e4m3: two pair buffers of two
+// bf16 tiles each (the keys being computed, widened), a ring of two e4m3
+// rounds in cache row order, the rounds' scales, the pair buffers' scales,
+// then the flags [2][8] (pair parity, wave).
+template <int KVD> struct Lds;
+template <> struct Lds<0> {
+  static constexpr int kStages = 8;
+  static constexpr int kFlagOff = kStages * kTileBytes;
+  static constexpr int kBytes = kFlagOff + 2 * 8 * 4;
+};
+template <> struct Lds<1> {
+  static constexpr int kStages = 4;
+  static constexpr int kRing = kStages * kTileBytes;
+  static constexpr int kRingScale = kRing + 2 * kF8RoundBytes;
+  static constexpr int kPairScale = kRingScale + 2 * kScaleRoundBytes;
+  static constexpr int kFlagOff = kPairScale + 2 * 2 * kTileTok * 4;
+  static constexpr int kBytes = kFlagOff + 2 * 8 * 4;
+};
+static_assert(Lds<1>::kBytes <= 160 * 1024, "e4m3 LDS map exceeds a workgroup's LDS");
 constexpr float kRestartMargin = 32.0f;       // log2 units above the reference max
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -120,7 +153,7 @@ struct Ring {
 template <int HALF>
 __device__ __forceinline__ void issue_half(const Ring& r, int t, int j) {
   const int tile = kRoundTiles * j + t;
-  const int stage = tile % kStages;
+  const int stage = tile % Lds<0>::kStages;
   const int kr = r.k0 + kRoundTok * j;          // first key of the round (< L)
   const bool real = tile < r.ntiles;
   const int kt = real ? r.k0 + kTileTok * tile : kr;
@@ -152,17 +185,220 @@ __device__ __forceinline__ void issue_round(const Ring& r, int t, int half, int 
   else issue_half<0>(r, t, j);
 }
 
+// ---- e4m3 caches.  A round of 64 keys is one run of one page (pages hold a
+// multiple of 64 rows and items start on a multiple of 64 keys), i.e. 36 KB
+// contiguous in the cache, copied as it lies; the 64 scales of the round are
+// contiguous too.
+struct RingF8 {
+  const uint8_t* kv;
+  const float* kv_scale;
+  const int32_t* bt_row;
+  uint32_t ring, ring_scale;   // LDS addresses
+  int page_shift, k0, L, wave, lane;
+};
+
+// This wave's share of round r into ring slot r & 1: copies wave, wave + 8,
+// ... (< 36) of the round's 36 KB (copy ins = bytes 1024 ins .. + 1023, lane
+// l taking 16 bytes at 16 l), and for wave 7 the round's 64 scales (a lane
+// past the sequence copies the round's first scale, so the slot holds no
+// stale value).  Rows past the sequence lie in the same page and are zeroed
+// when widened.
+__device__ __forceinline__ void issue_round_f8(const RingF8& r, int j) {
+  const int kr = r.k0 + kRoundTok * j;          // first key of the round (< L)
+  const int pmask = (1 << r.page_shift) - 1;
+  const int row0 = (r.bt_row[kr >> r.page_shift] << r.page_shift) + (kr & pmask);
+  const uint8_t* base = uniform_ptr(r.kv + (int64_t)row0 * kF8RowBytes);
+  const uint32_t lds = r.ring + (j & 1) * kF8RoundBytes;
+  const int lane = opaque(r.lane);
+  const int vo = 16 * lane;
+#pragma unroll
+  for (int k = 0; k < (kF8Copies + 7) / 8; ++k) {
+    const int ins = r.wave + 8 * k;
+    if (ins < kF8Copies) lds_dma_x4(lds + ins * 1024, vo, base + 1024 * ins);
+  }
+  if (r.wave == 7) {
+    const int tok = lane < r.L - kr ? lane : 0;
+    lds_dma_x1(r.ring_scale + (j & 1) * kScaleRoundBytes, tok * 4,
+               uniform_ptr(r.kv_scale + row0));
+  }
+}
+
+// Widen 8 e4m3 bytes to 8 bf16 values (exact: e4m3's values are bf16 values).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  bf16x8 v;
+  v[0] = (__bf16)a.x; v[1] = (__bf16)a.y; v[2] = (__bf16)b.x; v[3] = (__bf16)b.y;
+  v[4] = (__bf16)c.x; v[5] = (__bf16)c.y; v[6] = (__bf16)d.x; v[7] = (__bf16)d.y;
+  return v;
+}
+
+// Widen pair p of the item (keys kp .. kp + 31, the half p & 1 of round p >> 1
+// in ring slot (p >> 1) & 1) into pair buffer p & 1, in the bf16 tile layout
+// the MFMA steps read, and its 32 scales into the buffer's scale slot.  The
+// pair's 36 output blocks of 1 KB (stage bi / 18, block bi % 18 = 2 cg + rh)
+// go to the waves by bi % 8; lane l writes slot l of a block, i.e. row 8 rh +
+// r8, chunk 8 cg + c8 as the copy layout places them.  Rows at or past the
+// sequence's end become zeros.
+__device__ __forceinline__ void widen_pair_f8(char* smem, int p, int kp, int L, int wave,
+                                              int lane_id) {
+  // an opaque copy of the lane id keeps the per-lane offsets below inside the
+  // key loop rather than hoisted out of it (they would pin registers there)
+  const int lane = opaque(lane_id);
+  const int rh = wave & 1;
+  const int q = lane >> 4, lo = (lane >> 3) & 1;
+  const int c8 = 2 * q + (lo ^ rh);
+  const int r8 = (lane & 7) ^ (4 * (q & 1));
+  const int row = 8 * rh + r8;   // within a stage
+  const uint32_t src = Lds<1>::kRing + ((p >> 1) & 1) * kF8RoundBytes +
+                       (p & 1) * (2 * kTileTok * kF8RowBytes) + row * kF8RowBytes + 8 * c8;
+  const uint32_t dst = (p & 1) * 2 * kTileBytes + 16 * lane;
+#pragma unroll
+  for (int k = 0; k < (2 * 18 + 7) / 8; ++k) {
+    const int bi = wave + 8 * k;
+    if (bi < 2 * 18) {
+      const int st = bi >= 18 ? 1 : 0;
+      const int blk = bi - 18 * st, cg = blk >> 1;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 raw =
+          *(const LDS_PTR(u32x2))(smem + src + st * kTileTok * kF8RowBytes + 64 * cg);
+      bf16x8 v = e4m3x8_to_bf16(raw.x, raw.y);
+      if (kp + kTileTok * st + row >= L) v = bf16x8{};
+      *(LDS_PTR(bf16x8))(smem + dst + st * kTileBytes + blk * 1024) = v;
+    }
+  }
+  if (wave == 5 && lane < 2 * kTileTok) {
+    const float sc = *(const LDS_PTR(float))(smem + Lds<1>::kRingScale +
+                                             ((p >> 1) & 1) * kScaleRoundBytes +
+                                             ((p & 1) * 2 * kTileTok + lane) * 4);
+    *(LDS_PTR(float))(smem + Lds<1>::kPairScale + ((p & 1) * 2 * kTileTok + lane) * 4) = sc;
+  }
+}
+
+// Per-lane LDS read offsets of the MFMA operands (stage relative).
+struct Frag {
+  int kbase, vb_e, vb_o;
+};
+
+// QK^T, softmax and PV of one pair of 16-key stages (keys kp .. kp + 31) whose
+// bf16 tiles sit at LDS offset so and so + one tile.  For e4m3 the 32 per-key
+// scales at ksc_off multiply the scores and the probabilities.  Returns true
+// when the pair's scores overshoot the reference max (m raised; nothing
+// accumulated).
+template <int KVD>
+__device__ __forceinline__ bool pair_step(char* smem, const Frag& fr, int so, int ksc_off, int kp,
+                                          int lim, int lim_all, float scale_log2, int g4,
+                                          const bf16x8 (&qf)[18], f32x4 (&acc)[32], float& m,
+                                          float& l) {
+  constexpr int KW = 2;   // QK steps whose K fragments are in flight
+  constexpr int VW = 3;   // PV column blocks whose V fragments are in flight
+  // this pair's per-lane LDS bases: one add each per pair, through opaque
+  // copies so that the compiler keeps three registers here rather than
+  // precomputing a base per ring stage for the whole loop
+  const int kb_s = opaque(fr.kbase + so);
+  const int ve_s = opaque(fr.vb_e + so), vo_s = opaque(fr.vb_o + so);
+
+  // ---- S^T = K . Q^T for both stages, 18 steps of 32 dims
+  f32x4 SA = f32x4{}, SB = f32x4{};
+  {
+    auto kload = [&](int s, int c) -> bf16x8 {
+      return *(const LDS_PTR(bf16x8))(smem + kb_s + s * kTileBytes + 2048 * (c >> 1) +
+                                      512 * (c & 1));
+    };
+    bf16x8 ka[KW], kb[KW];
+#pragma unroll
+    for (int c = 0; c < KW - 1; ++c) {
+      ka[c] = kload(0, c);
+      kb[c] = kload(1, c);
+    }
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      if (c + KW - 1 < 18) {
+        ka[(c + KW - 1) % KW] = kload(0, c + KW - 1);
+        kb[(c + KW - 1) % KW] = kload(1, c + KW - 1);
+      }
+      SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c % KW], qf[c], SA, 0, 0, 0);
+      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c % KW], qf[c], SB, 0, 0, 0);
+    }
+  }
+
+  // ---- online softmax: keys kp + 4g4 + r (stage 0), kp + 16 + 4g4 + r
+  float s[8];
+  f32x4 ka4, kb4;   // e4m3: the per-key scales of those keys
+  if constexpr (KVD == 1) {
+    ka4 = *(const LDS_PTR(f32x4))(smem + ksc_off + 16 * g4);
+    kb4 = *(const LDS_PTR(f32x4))(smem + ksc_off + 64 + 16 * g4);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (KVD == 1) {
+      s[r] = SA[r] * (scale_log2 * ka4[r]);
+      s[4 + r] = SB[r] * (scale_log2 * kb4[r]);
+    } else {
+      s[r] = SA[r] * scale_log2;
+      s[4 + r] = SB[r] * scale_log2;
+    }
+  }
+  if (kp + 2 * kTileTok > lim_all) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int key = kp + 16 * (r >> 2) + 4 * g4 + (r & 3);
+      s[r] = key < lim ? s[r] : -INFINITY;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+  mx = quad_max(mx);
+  // a row's first visible pair fixes its reference max
+  m = (m == -INFINITY) ? mx : m;
+  if (__any(mx > m + kRestartMargin)) {
+    m = fmaxf(m, mx);
+    return true;
+  }
+  bf16x8 pf;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float p = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m);
+    l += p;
+    if constexpr (KVD == 1)
+      pf[r] = (__bf16)(p * (r < 4 ? ka4[r] : kb4[r - 4]));
+    else
+      pf[r] = (__bf16)p;
+  }
+
+  // ---- O^T[512 x 16] += V^T . P^T: 32 column blocks of 16
+  {
+    auto vload = [&](int cm) -> bf16x8 {
+      const int off = ((cm & 1) ? vo_s : ve_s) + 2048 * (cm >> 2) + 256 * (cm & 3);
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(smem + off));
+      const bf16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(smem + kTileBytes + off));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vf[VW];
+#pragma unroll
+    for (int n = 0; n < VW - 1; ++n) vf[n] = vload(n);
+#pragma unroll
+    for (int cm = 0; cm < 32; ++cm) {
+      if (cm + VW - 1 < 32) vf[(cm + VW - 1) % VW] = vload(cm + VW - 1);
+      acc[cm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cm % VW], pf, acc[cm], 0, 0, 0);
+    }
+  }
+  return false;
+}
+
 template <int KVD>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
     const DecodeArgs a, const int32_t* __restrict__ plan, const uint8_t* __restrict__ qg,
-    const uint8_t* __restrict__ kvg, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ q_lens,
-    uint8_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
-  static_assert(KVD == 0, "bf16 caches only");
-  constexpr int KW = 2;   // QK steps whose K fragments are in flight
-  constexpr int VW = 3;   // PV column blocks whose V fragments are in flight
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+    const uint8_t* __restrict__ kvg, const float* __restrict__ kv_scale,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_lens,
+    const int32_t* __restrict__ q_lens, uint8_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(1024))) char smem[Lds<KVD>::kBytes];
   const uint32_t smem_base = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -187,22 +423,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
   // ---- per-lane LDS read offsets (stage relative), constant over the run.
   // K fragment of QK step c (A operand, 16 keys x 32 dims): key l16 of the
   // stage, dims 32c + 8g4 .. +7, at kbase + 2048(c>>1) + 512(c&1).
-  const int kh = g4 >> 1, krh = l16 >> 3, kr8 = l16 & 7;
-  const int kbase = krh * 1024 + (16 * kh + 8 * ((g4 & 1) ^ krh) + (kr8 ^ (4 * kh))) * 16;
-  // V^T fragment of PV column block m (A operand, 16 columns x 4 keys of a
-  // stage): the lane names row 4g4 + l16/4, columns 16m + 4(l16%4) .. +3 and
-  // receives column 16m + l16, rows 4g4 .. 4g4 + 3; at vb[m&1] + 2048(m>>2) +
-  // 256(m&3).
-  const int vr = 4 * g4 + (l16 >> 2), vrh = vr >> 3, vr8 = vr & 7, vx = (l16 & 3) >> 1;
-  const int vb_e = vrh * 1024 + 16 * (8 * (vx ^ vrh) + vr8) + 8 * (l16 & 1);
-  const int vb_o = vrh * 1024 + 16 * (8 * (vx ^ vrh) + (vr8 ^ 4)) + 8 * (l16 & 1);
-  volatile LDS_PTR(int) flags = (volatile LDS_PTR(int))(smem + kFlagOff);   // [parity][wave]
+  Frag fr;
+  {
+    const int kh = g4 >> 1, krh = l16 >> 3, kr8 = l16 & 7;
+    fr.kbase = krh * 1024 + (16 * kh + 8 * ((g4 & 1) ^ krh) + (kr8 ^ (4 * kh))) * 16;
+    // V^T fragment of PV column block m (A operand, 16 columns x 4 keys of a
+    // stage): the lane names row 4g4 + l16/4, columns 16m + 4(l16%4) .. +3
+    // and receives column 16m + l16, rows 4g4 .. 4g4 + 3; at vb[m&1] +
+    // 2048(m>>2) + 256(m&3).
+    const int vr = 4 * g4 + (l16 >> 2), vrh = vr >> 3, vr8 = vr & 7, vx = (l16 & 3) >> 1;
+    fr.vb_e = vrh * 1024 + 16 * (8 * (vx ^ vrh) + vr8) + 8 * (l16 & 1);
+    fr.vb_o = vrh * 1024 + 16 * (8 * (vx ^ vrh) + (vr8 ^ 4)) + 8 * (l16 & 1);
+  }
+  // [parity][wave]
+  volatile LDS_PTR(int) flags = (volatile LDS_PTR(int))(smem + Lds<KVD>::kFlagOff);
 
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* item = items + it * kItemWords;
-    const int b = item[0], row_base = item[1], k0 = item[2], k1 = item[3], slot = item[4];
+    const int b = item[0], row_base = item[1], slot = item[4];
     const int slot_row = item[5];
     const int L = kv_lens[b];
+    // a plan made for other lengths never reads past the sequence
+    const int k1 = min(item[3], L), k0 = min(item[2], k1);
     const int qb = q_lens ? q_lens[b] : a.max_q_len;
     const int R = qb * H;
     const int ntiles = k1 > k0 ? (k1 - k0 + kTileTok - 1) / kTileTok : 0;
@@ -216,12 +458,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
     // rows past the sequence's last query row run over all keys (never
     // written), so that they never force the masked path
     const int lim = valid ? min(vis, k1) : k1;
-    int lim_all = lim;
-    lim_all = min(lim_all, __shfl_xor(lim_all, 1));
-    lim_all = min(lim_all, __shfl_xor(lim_all, 2));
-    lim_all = min(lim_all, __shfl_xor(lim_all, 4));
-    lim_all = min(lim_all, __shfl_xor(lim_all, 8));
-    lim_all = __builtin_amdgcn_readfirstlane(lim_all);
+    // the smallest lim of the wave's rows: visibility grows with the token,
+    // so it is the wave's first row's (all rows are past the end if it is)
+    const int first = row_base + 16 * wave;
+    const int lim_all =
+        first < R ? min(a.causal ? L - qb + first / H + 1 : L, k1) : k1;
 
     // ---- Q^T fragments (B operand): row, dims 32c + 8g4 .. +7
     bf16x8 qf[18];
@@ -231,140 +472,137 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       for (int c = 0; c < 18; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 64);
     }
 
-    Ring ring;
-    ring.kv = kvg;
-    ring.bt_row = block_table + (int64_t)b * a.max_pages;
-    ring.lds = smem_base;
-    ring.page_shift = a.page_shift;
-    ring.k0 = k0;
-    ring.L = L;
-    ring.ntiles = ntiles;
-    ring.lane = lane;
-
     f32x4 acc[32];
     float m = -INFINITY, l = 0.f;
-    for (;;) {   // runs once unless a score overshoots the reference max
-      if (nrounds > 0) issue_round(ring, tq, half, 0);
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
-      l = 0.f;
-      bool again = false;       // workgroup-uniform: some wave overshot
-      bool overshoot = false;   // wave-uniform: this wave overshot in the last round
+    if constexpr (KVD == 0) {
+      Ring ring;
+      ring.kv = kvg;
+      ring.bt_row = block_table + (int64_t)b * a.max_pages;
+      ring.lds = smem_base;
+      ring.page_shift = a.page_shift;
+      ring.k0 = k0;
+      ring.L = L;
+      ring.ntiles = ntiles;
+      ring.lane = lane;
 
-      // Round j opens by publishing round j-1's overshoot, waiting for this
-      // wave's copies and the barrier, and stopping the pass if any wave
-      // overshot in round j-1; after the last round the same is done once more.
-      for (int j = 0; j < nrounds; ++j) {
-        if (j > 0 && lane == 0) flags[((j - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
-        MLA_VM_WAIT(0);
-        barrier();   // tiles of round j come from all waves
-        if (j > 0 && any_flag(flags, (j - 1) & 1)) {
-          again = true;
-          break;
-        }
-        if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1);
-        overshoot = false;
+      for (;;) {   // runs once unless a score overshoots the reference max
+        if (nrounds > 0) issue_round(ring, tq, half, 0);
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
+        l = 0.f;
+        bool again = false;       // workgroup-uniform: some wave overshot
+        bool overshoot = false;   // wave-uniform: this wave overshot in the last round
 
-#pragma unroll
-        for (int pp = 0; pp < kRoundTiles / 2; ++pp) {
-          const int tile = kRoundTiles * j + 2 * pp;   // first stage of the pair
-          if (tile >= ntiles) break;
-          const int kp = k0 + kTileTok * tile;          // first key of the pair
-          // this pair's per-lane LDS bases: one add each per pair, through
-          // opaque copies so that the compiler keeps three registers here
-          // rather than precomputing a base per ring stage for the whole loop
-          const int so = (tile % kStages) * kTileBytes;
-          const int kb_s = opaque(kbase + so);
-          const int ve_s = opaque(vb_e + so), vo_s = opaque(vb_o + so);
-
-          // ---- S^T = K . Q^T for both stages, 18 steps of 32 dims
-          f32x4 SA = f32x4{}, SB = f32x4{};
-          {
-            auto kload = [&](int s, int c) -> bf16x8 {
-              return *(const LDS_PTR(bf16x8))(smem + kb_s + s * kTileBytes + 2048 * (c >> 1) +
-                                              512 * (c & 1));
-            };
-            bf16x8 ka[KW], kb[KW];
-#pragma unroll
-            for (int c = 0; c < KW - 1; ++c) {
-              ka[c] = kload(0, c);
-              kb[c] = kload(1, c);
-            }
-#pragma unroll
-            for (int c = 0; c < 18; ++c) {
-              if (c + KW - 1 < 18) {
-                ka[(c + KW - 1) % KW] = kload(0, c + KW - 1);
-                kb[(c + KW - 1) % KW] = kload(1, c + KW - 1);
-              }
-              SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c % KW], qf[c], SA, 0, 0, 0);
-              SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c % KW], qf[c], SB, 0, 0, 0);
-            }
-          }
-
-          // ---- online softmax: keys kp + 4g4 + r (stage 0), kp + 16 + 4g4 + r
-          float s[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            s[r] = SA[r] * a.scale_log2;
-            s[4 + r] = SB[r] * a.scale_log2;
-          }
-          if (kp + 2 * kTileTok > lim_all) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const int key = kp + 16 * (r >> 2) + 4 * g4 + (r & 3);
-              s[r] = key < lim ? s[r] : -INFINITY;
-            }
-          }
-          float mx = s[0];
-#pragma unroll
-          for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
-          mx = quad_max(mx);
-          // a row's first visible pair fixes its reference max
-          m = (m == -INFINITY) ? mx : m;
-          if (__any(mx > m + kRestartMargin)) {
-            m = fmaxf(m, mx);
-            overshoot = true;
+        // Round j opens by publishing round j-1's overshoot, waiting for this
+        // wave's copies and the barrier, and stopping the pass if any wave
+        // overshot in round j-1; after the last round the same is done once
+        // more.
+        for (int j = 0; j < nrounds; ++j) {
+          if (j > 0 && lane == 0) flags[((j - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
+          MLA_VM_WAIT(0);
+          barrier();   // tiles of round j come from all waves
+          if (j > 0 && any_flag(flags, (j - 1) & 1)) {
+            again = true;
             break;
           }
-          bf16x8 pf;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const float p = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m);
-            l += p;
-            pf[r] = (__bf16)p;
-          }
+          if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1);
+          overshoot = false;
 
-          // ---- O^T[512 x 16] += V^T . P^T: 32 column blocks of 16
-          {
-            auto vload = [&](int cm) -> bf16x8 {
-              const int off = ((cm & 1) ? vo_s : ve_s) + 2048 * (cm >> 2) + 256 * (cm & 3);
-              const bf16x4 v0 =
-                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(smem + off));
-              const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                  (LDS_PTR(bf16x4))(smem + kTileBytes + off));
-              return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            bf16x8 vf[VW];
 #pragma unroll
-            for (int n = 0; n < VW - 1; ++n) vf[n] = vload(n);
-#pragma unroll
-            for (int cm = 0; cm < 32; ++cm) {
-              if (cm + VW - 1 < 32) vf[(cm + VW - 1) % VW] = vload(cm + VW - 1);
-              acc[cm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cm % VW], pf, acc[cm], 0, 0, 0);
+          for (int pp = 0; pp < kRoundTiles / 2; ++pp) {
+            const int tile = kRoundTiles * j + 2 * pp;   // first stage of the pair
+            if (tile >= ntiles) break;
+            const int kp = k0 + kTileTok * tile;          // first key of the pair
+            const int so = (tile % Lds<0>::kStages) * kTileBytes;
+            if (pair_step<0>(smem, fr, so, 0, kp, lim, lim_all, a.scale_log2, g4, qf, acc, m,
+                             l)) {
+              overshoot = true;
+              break;
             }
           }
         }
+        if (!again && nrounds > 0) {   // the loop ran out: check its last round
+          if (lane == 0) flags[((nrounds - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
+          MLA_VM_WAIT(0);
+          barrier();
+          again = any_flag(flags, (nrounds - 1) & 1);
+        }
+        // Every wave left at the same barrier with the same `again`; no copy
+        // is in flight (the last wait drained them) and no wave reads the
+        // ring after that barrier, so a new pass may refill it.
+        if (!again) break;
       }
-      if (!again && nrounds > 0) {   // the loop ran out: check its last round
-        if (lane == 0) flags[((nrounds - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
-        MLA_VM_WAIT(0);
-        barrier();
-        again = any_flag(flags, (nrounds - 1) & 1);
+    } else {
+      RingF8 ring;
+      ring.kv = kvg;
+      ring.kv_scale = kv_scale;
+      ring.bt_row = block_table + (int64_t)b * a.max_pages;
+      ring.ring = smem_base + Lds<1>::kRing;
+      ring.ring_scale = smem_base + Lds<1>::kRingScale;
+      ring.page_shift = a.page_shift;
+      ring.k0 = k0;
+      ring.L = L;
+      ring.wave = wave;
+      ring.lane = lane;
+      const int npairs = (ntiles + 1) >> 1;
+
+      // Three stages per pair of 32 keys: copy (a round of two pairs at a
+      // time), widen into a pair buffer, compute.  Iteration p widens pair
+      // p + 1 and computes pair p between two barriers; round r + 1 is issued
+      // in iteration 2r - 1, into the ring slot whose round was widened by
+      // then, and waited for in iteration 2r + 1, the first to widen it.  Only
+      // that round is in flight at the wait.
+      for (;;) {   // runs once unless a score overshoots the reference max
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
+        l = 0.f;
+        bool again = false;
+        bool overshoot = false;
+        if (npairs > 0) {
+          issue_round_f8(ring, 0);
+          MLA_VM_WAIT(0);
+          barrier();   // round 0 comes from all waves
+          widen_pair_f8(smem, 0, k0, L, wave, lane);
+          if (nrounds > 1) issue_round_f8(ring, 1);
+        }
+        // Pair p opens by publishing pair p-1's overshoot and the barrier, and
+        // stops the pass if any wave overshot in pair p-1 (the flags are kept
+        // by pair parity, as for the bf16 rounds).  The two pairs of a round
+        // are written out, so that a pair's parity (its buffer, whether it
+        // waits and issues) is known at compile time.
+        for (int j = 0; j < nrounds && !again; ++j) {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const int p = 2 * j + pp;
+            if (p >= npairs) break;
+            if (p > 0 && lane == 0) flags[(1 - pp) * 8 + wave] = overshoot ? 1 : 0;
+            if (pp == 1) MLA_VM_WAIT(0);
+            barrier();   // pair p widened by all waves; for odd p, round j + 1 copied
+            if (p > 0 && any_flag(flags, 1 - pp)) {
+              again = true;
+              break;
+            }
+            if (pp == 1 && j + 2 < nrounds) issue_round_f8(ring, j + 2);
+            if (p + 1 < npairs)
+              widen_pair_f8(smem, p + 1, k0 + 2 * kTileTok * (p + 1), L, wave, lane);
+            overshoot = pair_step<1>(smem, fr, pp * 2 * kTileBytes,
+                                     Lds<1>::kPairScale + pp * 2 * kTileTok * 4,
+                                     k0 + 2 * kTileTok * p, lim, lim_all, a.scale_log2, g4, qf,
+                                     acc, m, l);
+          }
+        }
+        if (!again && npairs > 0) {   // the loop ran out: check its last pair
+          if (lane == 0) flags[((npairs - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
+          MLA_VM_WAIT(0);
+          barrier();
+          again = any_flag(flags, (npairs - 1) & 1);
+        } else if (again) {
+          // a round may still be landing: drain it before the ring is refilled
+          MLA_VM_WAIT(0);
+          barrier();
+        }
+        if (!again) break;
       }
-      // Every wave left at the same barrier with the same `again`; no copy is
-      // in flight (the last wait drained them) and no wave reads the ring
-      // after that barrier, so a new pass may refill it.
-      if (!again) break;
     }
 
     // ---- epilogue: lane owns row l16, columns 16cm + 4g4 + r.  The lane's
@@ -409,11 +647,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
 
 }  // namespace
 
-hipError_t launch_decode_w8(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   if (a.phases != 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mla_decode_kernel_w8<0>), dim3(a.num_wg), dim3(kThreads), 0, stream, a,
-                     a.plan, a.q, a.kv, a.block_table, a.kv_lens, a.q_lens, a.o, a.lse, a.part_o,
-                     a.part_lse);
+  if (kv_dtype == 0) {
+    hipLaunchKernelGGL((mla_decode_kernel_w8<0>), dim3(a.num_wg), dim3(kThreads), 0, stream, a,
+                       a.plan, a.q, a.kv, a.kv_scale, a.block_table, a.kv_lens, a.q_lens, a.o,
+                       a.lse, a.part_o, a.part_lse);
+  } else {
+    hipLaunchKernelGGL((mla_decode_kernel_w8<1>), dim3(a.num_wg), dim3(kThreads), 0, stream, a,
+                       a.plan, a.q, a.kv, a.kv_scale, a.block_table, a.kv_lens, a.q_lens, a.o,
+                       a.lse, a.part_o, a.part_lse);
+  }
   return hipGetLastError();
 }
 

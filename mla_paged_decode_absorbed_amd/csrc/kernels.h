@@ -40,9 +40,9 @@ struct CombineArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
-// Candidate decode kernel with two waves per SIMD (bf16 cache, one-phase
-// plans); chosen only when MLA_DECODE_KERNEL=w8.
-hipError_t launch_decode_w8(const DecodeArgs& a, hipStream_t stream);
+// Candidate decode kernel with two waves per SIMD (one-phase plans, bf16 or
+// e4m3 cache); chosen only when MLA_DECODE_KERNEL=w8.
+hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace mla

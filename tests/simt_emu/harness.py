@@ -34,11 +34,13 @@ def _stale() -> bool:
 
 def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 600.0,
         env_extra: dict | None = None, binary: str | None = None, fixed: bool = False,
-        tree_mask=None, want_plan: bool = False):
+        tree_mask=None, want_plan: bool = False, plan_kv_lens=None):
     """Returns (out bf16 bits [B, qmax, H, 512] uint16, lse [B, qmax, H] f32, meta).
     ``fixed`` plans with mla_decode_plan_fixed (launch bounds, padded plan);
     ``tree_mask`` [B, qmax] runs the tree-draft path (prefix decode + merge);
-    ``want_plan`` adds the plan image the kernels ran (int32 words) to meta."""
+    ``want_plan`` adds the plan image the kernels ran (int32 words) to meta;
+    ``plan_kv_lens`` plans for these lengths instead of the case's (a stale
+    plan: the kernels still get the case's lengths)."""
     B, H, qmax = case.batch, case.num_heads, case.max_q_len
     kv_dtype = {"bf16": 0, "fp8_e4m3": 1}[case.kv_dtype]
     magic = MAGIC if tree_mask is None else TREE_MAGIC
@@ -64,6 +66,8 @@ def run(case, num_workgroups: int, phases: int | None = None, timeout: float = 6
             env["MLA_PHASES"] = str(phases)
         if env_extra:
             env.update(env_extra)
+        if plan_kv_lens is not None:
+            env["EMU_PLAN_KV_LENS"] = ",".join(str(int(x)) for x in plan_kv_lens)
         fplan = os.path.join(d, "plan.bin")
         if want_plan:
             env["EMU_PLAN_OUT"] = fplan

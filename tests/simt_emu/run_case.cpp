@@ -357,9 +357,21 @@ int main(int argc, char** argv) {
   if (bound == 0) die("shape rejected by mla_plan_bytes_bound");
   std::vector<int32_t> host_plan(bound / 4 + 1);
   mla_plan_info info{};
-  mla_status st = hd[11] ? mla_decode_plan_fixed(&s, kvl, ql, nwg, host_plan.data(),
+  // EMU_PLAN_KV_LENS="l0,l1,...": plan for these lengths instead of the
+  // device ones (a stale plan)
+  std::vector<int32_t> plan_kvl(kvl, kvl + s.batch);
+  if (const char* pk = std::getenv("EMU_PLAN_KV_LENS")) {
+    const char* c = pk;
+    for (int b = 0; b < s.batch; ++b) {
+      char* end = nullptr;
+      plan_kvl[b] = int32_t(std::strtol(c, &end, 10));
+      if (end == c) die("EMU_PLAN_KV_LENS: too few lengths");
+      c = *end == ',' ? end + 1 : end;
+    }
+  }
+  mla_status st = hd[11] ? mla_decode_plan_fixed(&s, plan_kvl.data(), ql, nwg, host_plan.data(),
                                                   host_plan.size() * 4, &info)
-                         : mla_decode_plan(&s, kvl, ql, nwg, host_plan.data(),
+                         : mla_decode_plan(&s, plan_kvl.data(), ql, nwg, host_plan.data(),
                                            host_plan.size() * 4, &info);
   if (st != MLA_OK) die("mla_decode_plan failed");
   // the "device" plan image: exactly plan_bytes long

@@ -106,8 +106,10 @@ def test_candidate_kernel_naming(monkeypatch):
     monkeypatch.setenv("MLA_DECODE_KERNEL", "w8")
     assert bench.decode_kernel_name("bf16", 1) == "mla_decode_kernel_w8"
     assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_w8<0>"
-    # plans the candidate does not cover keep the library kernels
-    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel<1, 1>"
+    assert bench.decode_kernel_name("fp8_e4m3", 1) == "mla_decode_kernel_w8"
+    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel_w8<1>"
+    # plans the candidate does not cover (several phases) keep the library kernels
     assert bench.decode_kernel_name("bf16", 4) == "mla_decode_kernel"
+    assert bench.decode_kernel_symbol("fp8_e4m3", 2) == "mla_decode_kernel<1, 2>"
     monkeypatch.delenv("MLA_DECODE_KERNEL")
     assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"

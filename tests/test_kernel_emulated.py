@@ -313,11 +313,12 @@ def test_emulated_full_length_sequences():
 
 # ---------------------------------------------------------------- two waves per SIMD
 # The candidate decode kernel (decode_w8_kernel.hip, chosen by
-# MLA_DECODE_KERNEL=w8 for bf16 one-phase plans): eight waves of 16 rows, two
-# per SIMD.  The same cases as the default kernel's, in both copy-landing
-# modes: several items per workgroup, ragged tails inside a pair's second
-# stage, empty sequences, up to 8 draft tokens over several row blocks,
-# small and large pages, the restart paths and a full-length sequence.
+# MLA_DECODE_KERNEL=w8 for one-phase plans): eight waves of 16 rows, two per
+# SIMD.  The same cases as the default kernel's, in both copy-landing modes:
+# several items per workgroup, ragged tails inside a pair's second stage,
+# empty sequences, up to 8 draft tokens over several row blocks, small and
+# large pages, the restart paths and a full-length sequence; for e4m3 caches
+# also the widening stage (copy, widen, compute pipelined over pairs).
 
 W8 = {"MLA_DECODE_KERNEL": "w8"}
 
@@ -378,3 +379,122 @@ def test_w8_emulation_catches_a_missing_barrier(tmp_path):
     out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={**MODES["issue-drift"], **W8})
     with pytest.raises(AssertionError):
         _check(case, out, lse)
+
+
+W8_F8_CASES = [
+    # (kv_lens, q_lens, num_workgroups, H, page size): e4m3 pages hold 64 or more rows
+    ([1500, 700, 65, 900], [1, 2, 1, 2], 1, 128, 64),     # several items on one workgroup
+    ([1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129], [1, 1, 2, 1, 2, 1, 2, 1, 1, 2, 1], 12, 128, 64),
+    ([0, 200, 64], [0, 2, 1], 5, 128, 64),                 # empty sequence without query
+    ([64, 64, 130, 18], [1, 1, 1, 1], 1, 128, 64),         # one-round items back to back
+    ([77, 300], [8, 1], 6, 16, 64),                        # longest draft
+    ([700, 130], [2, 2], 64, 128, 256),                    # many splits, large pages
+    ([257, 191, 96], [1, 2, 1], 2, 32, 256),               # three-pair and odd-pair items
+]
+
+
+def _dominant_key_case_f8():
+    # an e4m3 row equal to sign(q) (codes of +-448, scale 1/448) scores far
+    # above the first pairs' reference max: the restart path
+    case = make_case(kv_lens=[700], q_lens=[1], seed=19, kv_dtype="fp8_e4m3",
+                     sm_scale=1 / math.sqrt(192))
+    q = oracle.decode_bf16(case.q[0, 0])[0]
+    j = 650
+    page, slot = case.block_table[0, j // 64], j % 64
+    case.kv[page, slot] = np.where(q >= 0, 0x7E, 0xFE).astype(np.uint8)
+    case.kv_scale[page, slot] = np.float32(1.0 / 448.0)
+    return case
+
+
+def test_w8_e4m3_kernel_matches_oracle():
+    cases = [make_case(kv_lens=kv, q_lens=ql, seed=39, num_heads=H, page_size=P,
+                       kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192),
+                       max_q_len=max(2, max(ql)))
+             for kv, ql, _n, H, P in W8_F8_CASES]
+    jobs = [(c, spec[2], 1, dict(env_extra={**MODES[mode], **W8}))
+            for c, spec in zip(cases, W8_F8_CASES) for mode in ("wait-lockstep", "issue-drift")]
+    for (c, n, _p, kw), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
+
+
+def test_w8_e4m3_kernel_restarts():
+    jobs = [(c, 1, 1, dict(env_extra={**MODES[mode], **W8}))
+            for c in (_dominant_key_case_f8(), _rising_scores_case("fp8_e4m3"))
+            for mode in ("wait-lockstep", "wait-drift", "issue-drift")]
+    O, L = oracle.mla_decode_ref(jobs[0][0])
+    assert L[0, 0].max() * math.log2(math.e) > 40   # the dominant key is far above the rest
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
+
+
+def test_w8_e4m3_kernel_fixed_shape_plan_and_full_length():
+    fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
+                      kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192))
+    full = make_case(kv_lens=[32768], q_lens=[1], num_heads=128, seed=51, kv_dtype="fp8_e4m3",
+                     sm_scale=1 / math.sqrt(192))
+    jobs = [(fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **W8})),
+            (full, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **W8}, timeout=1500))]
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
+
+
+@pytest.mark.parametrize("marker", [
+    "barrier();   // pair p widened by all waves; for odd p, round j + 1 copied",
+    "if (pp == 1) MLA_VM_WAIT(0);",
+])
+def test_w8_e4m3_emulation_catches_a_missing_wait(tmp_path, marker):
+    # the e4m3 pipeline with its per-pair barrier, or its wait for a round's
+    # copies, taken out (planted on the CPU): a wave widens a pair before the
+    # other waves' copies of it landed, or refills a buffer still read
+    from tests.simt_emu import build as _b
+    src = open(os.path.join(_b.CSRC, "decode_w8_kernel.hip")).read()
+    assert src.count(marker) == 1
+    binary = _b.build(tag="w8_f8_planted_" + str(abs(hash(marker)) % 1000), patches={
+        "decode_w8_kernel.hip": [(marker, "/* removed */")]})
+    case = make_case(kv_lens=[700, 300], q_lens=[2, 1], seed=5, kv_dtype="fp8_e4m3",
+                     sm_scale=1 / math.sqrt(192))
+    mode = "issue-drift" if "barrier" in marker else "wait-drift"
+    with pytest.raises((AssertionError, RuntimeError)):
+        out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={**MODES[mode], **W8})
+        _check(case, out, lse)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_w8_stale_longer_plan_stays_inside_the_sequence(kv_dtype):
+    # A plan made for longer lengths than the device holds (a fixed-shape
+    # graph replayed after the lengths shrank, say): the candidate clamps every
+    # item's key range to the device length, so it reads no row past the
+    # sequence's pages (whose block-table entries are padding here) and, with
+    # the same query lengths, computes the result for the device lengths;
+    # pieces that lie wholly past the end become empty partials.
+    case = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=47, kv_dtype=kv_dtype,
+                     max_q_len=2, sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
+    # unused entries name the page just past the pool: a read through one
+    # starts in the allocation's redzone, which AddressSanitizer reports
+    assert np.all(case.block_table[0, 11:] < 0)
+    case.block_table[case.block_table < 0] = case.num_pages
+    plan_lens = [1200, 900, 300]
+    jobs = [(case, nwg, 1, dict(env_extra={**MODES["issue-drift"], **W8},
+                                plan_kv_lens=plan_lens))
+            for nwg in (3, 16)]
+    for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
+    assert meta["num_partials"] > 0
+
+
+def test_w8_stale_plan_without_the_clamp_reads_outside_the_cache():
+    # the candidate with its key-range clamp taken out (planted on the CPU):
+    # the stale plan above makes it read pages past the sequence's end
+    from tests.simt_emu import build as _b
+    marker = "const int k1 = min(item[3], L), k0 = min(item[2], k1);"
+    src = open(os.path.join(_b.CSRC, "decode_w8_kernel.hip")).read()
+    assert src.count(marker) == 1
+    binary = _b.build(tag="w8_planted_noclamp", patches={"decode_w8_kernel.hip": [
+        (marker, "const int k1 = item[3], k0 = item[2];")]})
+    for kv_dtype in ("bf16", "fp8_e4m3"):
+        case = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=47, kv_dtype=kv_dtype,
+                         max_q_len=2, sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
+        case.block_table[case.block_table < 0] = case.num_pages
+        with pytest.raises(RuntimeError, match="AddressSanitizer"):
+            harness.run(case, 3, 1, binary=binary, plan_kv_lens=[1200, 900, 300],
+                        env_extra={**MODES["issue-drift"], **W8})
