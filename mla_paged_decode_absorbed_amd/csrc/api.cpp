@@ -37,6 +37,16 @@ mla_status check_info(const mla_shape* s, const mla_plan_info* info) {
   return MLA_OK;
 }
 
+// MLA_DECODE_KERNEL=w8 selects the two-waves-per-SIMD candidate decode
+// kernel for the plans it covers (one phase, either cache type), and with it
+// the merge of the bf16 partials it writes; every other plan, and the
+// default, runs the library's decode and combine kernels.  mla_decode_fwd and
+// mla_combine of one step must see the same setting.
+bool candidate_selected(const mla_plan_info* info) {
+  const char* variant = std::getenv("MLA_DECODE_KERNEL");
+  return variant && std::strcmp(variant, "w8") == 0 && info->phases == 1;
+}
+
 mla_status host_plan(const mla_shape* shape, const int32_t* kv_lens_host,
                      const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
                      uint64_t plan_bytes, mla_plan_info* info, bool fixed_shape) {
@@ -186,11 +196,7 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   a.num_wg = info->num_workgroups;
   a.phases = info->phases;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // MLA_DECODE_KERNEL=w8 selects the two-waves-per-SIMD candidate for the
-  // plans it covers (one phase, either cache type); every other plan, and the
-  // default, runs the library's decode kernels.
-  const char* variant = std::getenv("MLA_DECODE_KERNEL");
-  if (variant && std::strcmp(variant, "w8") == 0 && info->phases == 1)
+  if (candidate_selected(info))
     return launch_decode_w8(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   return launch_decode(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -257,8 +263,9 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info, const 
   a.num_heads = shape->num_heads;
   a.max_q_len = shape->max_q_len;
   a.num_combine = info->num_combine;
-  return launch_combine(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK
-                                                                                 : MLA_ERR_HIP;
+  const hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = candidate_selected(info) ? launch_combine_bf16(a, cs) : launch_combine(a, cs);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status mla_kv_append(const mla_shape* shape, int32_t max_new_tokens, const void* new_rows,

@@ -62,12 +62,62 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineArgs a) {
   *reinterpret_cast<bf16x8*>(a.o + orow * (kDLatent * 2) + lane * 16) = out;
 }
 
+// The same merge over bf16 partials (the two-waves-per-SIMD candidate writes
+// them: [partials][128][512] bf16 in the first half of the fp32 partial area,
+// the LSE where it always is).  Kept apart from mla_combine_kernel, whose
+// compiled code stays as validated.
+__global__ __launch_bounds__(256) void mla_combine_kernel_bf16(const CombineArgs a) {
+  if (int(blockIdx.x) >= a.plan[kWNumCombine]) return;
+  const int32_t* comb = a.plan + a.plan[kWOffCombine] + blockIdx.x * kCombineWords;
+  const int b = comb[0], row0 = comb[1], first = comb[2], n = comb[3];
+  const int rb = blockIdx.y * kRowsPerCta + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int H = a.num_heads;
+  const int qb = a.q_lens ? a.q_lens[b] : a.max_q_len;
+  const int row = row0 + rb;
+  if (row >= qb * H) return;
+  const int t = row / H, h = row - t * H;
+  const __bf16* part = reinterpret_cast<const __bf16*>(a.part_o);
+
+  float m = -INFINITY;
+  for (int s = 0; s < n; ++s) m = fmaxf(m, a.part_lse[(int64_t)(first + s) * kRowsPerBlock + rb]);
+  const int64_t orow = (int64_t)(b * a.max_q_len + t) * H + h;
+  bf16x8 out;
+  if (m == -INFINITY) {
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)0.f;
+    if (a.lse && lane == 0) a.lse[orow] = -INFINITY;
+  } else {
+    float acc[8] = {};
+    float tot = 0.f;
+    for (int s = 0; s < n; ++s) {
+      const float w = __expf(a.part_lse[(int64_t)(first + s) * kRowsPerBlock + rb] - m);
+      if (w > 0.f) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(
+            part + ((int64_t)(first + s) * kRowsPerBlock + rb) * kDLatent + lane * 8);
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+        tot += w;
+      }
+    }
+    const float inv = 1.f / tot;
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+    if (a.lse && lane == 0) a.lse[orow] = m + __logf(tot);
+  }
+  *reinterpret_cast<bf16x8*>(a.o + orow * (kDLatent * 2) + lane * 16) = out;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.num_combine <= 0) return hipSuccess;
   const dim3 grid(a.num_combine, kRowsPerBlock / kRowsPerCta), block(256);
   hipLaunchKernelGGL(mla_combine_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t stream) {
+  if (a.num_combine <= 0) return hipSuccess;
+  const dim3 grid(a.num_combine, kRowsPerBlock / kRowsPerCta), block(256);
+  hipLaunchKernelGGL(mla_combine_kernel_bf16, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,9 @@
 //     it after the same barrier, lets waves leave at different barriers.)
 //   * An item's key range is clamped to the sequence's device length, so a
 //     plan made for longer lengths reads no row past the sequence's pages.
+//   * Split row blocks leave bf16 partials (normalised O) and fp32 LSE, which
+//     mla_combine_kernel_bf16 merges: half the partial bytes of the library
+//     kernels' fp32 partials, written once and read once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -627,14 +630,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
           }
           if (lse && ge == 0) lse[(b * a.max_q_len + t) * H + h] = lse_v;
         } else {
+          // bf16 partials: half the bytes of fp32 ones, written here and
+          // read back by the combine (mla_combine_kernel_bf16)
           const int rb = slot_row + 16 * wave + l16;
-          float* pp = part_o + ((int64_t)slot * kRowsPerBlock + rb) * kDLatent;
+          uint8_t* pp = reinterpret_cast<uint8_t*>(part_o) +
+                        ((int64_t)slot * kRowsPerBlock + rb) * (kDLatent * 2);
 #pragma unroll
           for (int cm = 0; cm < 32; ++cm) {
-            f32x4 v;
+            bf16x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[cm][e] * inv;
-            *reinterpret_cast<f32x4*>(pp + 16 * cm + 4 * ge) = v;
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cm][e] * inv);
+            *reinterpret_cast<bf16x4*>(pp + (16 * cm + 4 * ge) * 2) = v;
           }
           if (ge == 0) part_lse[(int64_t)slot * kRowsPerBlock + rb] = lse_v;
         }

@@ -44,5 +44,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 // e4m3 cache); chosen only when MLA_DECODE_KERNEL=w8.
 hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// The merge over bf16 partials, as the candidate decode kernel writes them.
+hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace mla

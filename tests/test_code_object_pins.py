@@ -75,6 +75,11 @@ NOT_YET_RUN_ON_GPU = (
     "check_kernel.hip",       # mla_decode_check, opt-in debug mode
     "decode_w8_kernel.hip",   # two-waves-per-SIMD candidate, only under MLA_DECODE_KERNEL=w8
 )
+# Kernels added since to a pinned source, beside its validated kernels; none
+# of them is on the default path either.
+NEW_KERNELS_IN_PINNED_SOURCES = {
+    "combine_kernel.hip": {"mla_combine_kernel_bf16"},   # merge of the candidate's bf16 partials
+}
 
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="ROCm toolchain not available")
 
@@ -121,6 +126,12 @@ def test_validated_kernels_are_unchanged(fingerprints, src):
         assert got[kernel] == pin, (
             f"{src}: {kernel} changed ({got[kernel]} != pinned {pin}); code that has not "
             "passed the GPU suites must not replace a validated kernel")
+
+
+@pytest.mark.parametrize("src", sorted(PINS))
+def test_every_kernel_of_a_pinned_source_is_pinned_or_new(fingerprints, src):
+    extra = set(fingerprints[src]) - set(PINS[src])
+    assert extra == NEW_KERNELS_IN_PINNED_SOURCES.get(src, set()), (src, sorted(extra))
 
 
 def test_every_library_kernel_source_is_pinned_or_new():

@@ -84,3 +84,43 @@ def test_w8_e4m3_long_context():
     (out, lse), pl = run_gpu(case, phases=1)
     assert pl.phases == 1
     check(case, out, lse)
+
+
+def test_w8_combine_of_bf16_partials_matches_combine_ref():
+    # the merge the candidate's split rows take: bf16 partials (the first half
+    # of the fp32 partial area), fp32 LSE where it always is
+    import oracle
+    import mla_paged_decode_absorbed_amd as mla
+    from tests.test_gpu_parity import DEV, as_f64, shape_of
+    case = make_case(kv_lens=[3000, 2500], q_lens=[2, 1], seed=25, sm_scale=1 / math.sqrt(192))
+    shape = shape_of(case)
+    pl = mla.plan(shape, case.kv_lens, case.q_lens, num_workgroups=64)
+    assert pl.info.num_combine > 0 and pl.phases == 1
+    rng = np.random.default_rng(0)
+    P = pl.info.num_partials
+    po = torch.from_numpy(rng.standard_normal((P, 128, 512)).astype(np.float32))
+    po_b = po.to(torch.bfloat16)
+    plse = (rng.standard_normal((P, 128)) * 3).astype(np.float32)
+    plse[::5, ::7] = -np.inf      # empty partials: their O (NaN here) must be ignored
+    po_b[::5, ::7] = float("nan")
+    print("w8: combine of bf16 partials", flush=True)
+    ws = mla.alloc_workspace(pl)
+    ws.view(torch.bfloat16)[: P * 128 * 512].copy_(po_b.reshape(-1))
+    base = ws.view(torch.float32)
+    base[P * 128 * 512: P * 128 * 512 + P * 128].copy_(torch.from_numpy(plse.reshape(-1)))
+    out = torch.zeros((case.batch, 2, case.num_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((case.batch, 2, case.num_heads), dtype=torch.float32, device=DEV)
+    mla.combine(shape, pl, ws, torch.from_numpy(case.q_lens).to(DEV), out, lse)
+    torch.cuda.synchronize()
+    o, l = as_f64(out, lse)
+    pof = po_b.float().numpy().astype(np.float64)
+    for b, row0, first, n in pl.combine_entries():
+        Oc, Lc = oracle.combine_ref(pof[first:first + n], plse[first:first + n])
+        rows = min(128, int(case.q_lens[b]) * case.num_heads - int(row0))
+        for r in range(rows):
+            t, h = divmod(int(row0) + r, case.num_heads)
+            if np.isneginf(Lc[r]):
+                assert np.isneginf(l[b, t, h]) and np.all(o[b, t, h] == 0)
+                continue
+            assert abs(l[b, t, h] - Lc[r]) <= 1e-4 * max(1.0, abs(Lc[r]))
+            assert np.abs(o[b, t, h] - Oc[r]).max() <= 4e-3 * np.abs(Oc[r]).max()

@@ -271,11 +271,12 @@ def test_append_kernel_machine_code(append_isa):
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_k_kernel"),
                                         ("prefill_quant_kernel.hip", "mla_prefill_quant_v_kernel"),
                                         ("prefill_attn_kernel.hip", "mla_prefill_attn_kernel"),
-                                        ("check_kernel.hip", "mla_check_kernel")])
+                                        ("check_kernel.hip", "mla_check_kernel"),
+                                        ("combine_kernel.hip", "mla_combine_kernel_bf16")])
 def test_small_kernels_machine_code(tmp_path, src, kernel):
-    # the device planner, the tree-draft merge, the prefill kernels and the
-    # debug check: no scratch, no scalar stores, LDS within the 160 KB a
-    # workgroup may use
+    # the device planner, the tree-draft merge, the prefill kernels, the
+    # debug check and the merge of bf16 partials: no scratch, no scalar
+    # stores, LDS within the 160 KB a workgroup may use
     out = tmp_path / "k.s"
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
