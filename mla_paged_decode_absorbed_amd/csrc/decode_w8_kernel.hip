@@ -202,10 +202,11 @@ struct RingF8 {
 
 // This wave's share of round r into ring slot r & 1: copies wave, wave + 8,
 // ... (< 36) of the round's 36 KB (copy ins = bytes 1024 ins .. + 1023, lane
-// l taking 16 bytes at 16 l), and for wave 7 the round's 64 scales (a lane
-// past the sequence copies the round's first scale, so the slot holds no
-// stale value).  Rows past the sequence lie in the same page and are zeroed
-// when widened.
+// l taking 16 bytes at 16 l; a row is 36 such pieces, so a piece lies in one
+// row), and for wave 7 the round's 64 scales.  Lanes whose piece lies in a
+// row past the sequence's end are masked off, so no cache slot past the
+// sequence is read (the widening zeroes those rows; a scale lane past the end
+// copies the round's first scale).
 __device__ __forceinline__ void issue_round_f8(const RingF8& r, int j) {
   const int kr = r.k0 + kRoundTok * j;          // first key of the round (< L)
   const int pmask = (1 << r.page_shift) - 1;
@@ -214,10 +215,13 @@ __device__ __forceinline__ void issue_round_f8(const RingF8& r, int j) {
   const uint32_t lds = r.ring + (j & 1) * kF8RoundBytes;
   const int lane = opaque(r.lane);
   const int vo = 16 * lane;
+  // bytes of the round inside the sequence (rows < L - kr)
+  const int valid_bytes = min(r.L - kr, kRoundTok) * kF8RowBytes;
 #pragma unroll
   for (int k = 0; k < (kF8Copies + 7) / 8; ++k) {
     const int ins = r.wave + 8 * k;
-    if (ins < kF8Copies) lds_dma_x4(lds + ins * 1024, vo, base + 1024 * ins);
+    if (ins < kF8Copies && vo + 1024 * ins < valid_bytes)
+      lds_dma_x4(lds + ins * 1024, vo, base + 1024 * ins);
   }
   if (r.wave == 7) {
     const int tok = lane < r.L - kr ? lane : 0;
@@ -470,7 +474,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
     // ---- Q^T fragments (B operand): row, dims 32c + 8g4 .. +7
     bf16x8 qf[18];
     {
-      const uint8_t* qp = qg + ((int64_t)((b * a.max_q_len + t) * H + h)) * (kDQK * 2) + g4 * 16;
+      // (through an opaque lane id: a per-lane base hoisted out of the item
+      // loop would hold two registers through the key loop)
+      const uint8_t* qp = qg + ((int64_t)((b * a.max_q_len + t) * H + h)) * (kDQK * 2) +
+                          (opaque(lane) >> 4) * 16;
 #pragma unroll
       for (int c = 0; c < 18; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 64);
     }
