@@ -73,3 +73,19 @@ def test_tree_partial_head_groups(H, qmax):
     mask = tree_masks(case.q_lens, case.max_q_len, "random", seed=6)
     out, lse, _ = harness.run(case, 5, 1, tree_mask=mask)
     check_tree(case, mask, out, lse)
+
+
+def test_tree_drafts_through_the_candidate_decode_kernel():
+    # the prefix decode on the two-waves-per-SIMD candidate (MLA_DECODE_KERNEL
+    # =w8: its bf16 partials and their merge), then the draft merge
+    jobs, masks = [], []
+    for dtype, P in (("bf16", 16), ("fp8_e4m3", 64)):
+        case = make_case(kv_lens=[300, 8, 70, 1000], q_lens=[4, 8, 3, 0], seed=55, kv_dtype=dtype,
+                         num_heads=16, page_size=P, sm_scale=1 / math.sqrt(192), max_q_len=8)
+        mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=4)
+        jobs.append((case, 6, 1, dict(tree_mask=mask, env_extra={
+            "MLA_DECODE_KERNEL": "w8", "EMU_DMA_LAND": "issue", "EMU_SCHED": "drift"})))
+        masks.append(mask)
+    for (case, *_), mask, (out, lse, meta) in zip(jobs, masks, harness.run_many(jobs)):
+        assert meta["num_partials"] > 0
+        check_tree(case, mask, out, lse)
