@@ -40,16 +40,16 @@
 //     of each stage) in the order it holds them, so the probabilities are the
 //     B operand with no lane exchange; V^T is read by ds_read_b64_tr_b16, four
 //     keys of one stage per read.
-//   * The softmax keeps the library kernels' fixed reference max and their
-//     restart when a score overshoots it by more than 32 (log2 units).  The
-//     waves agree on a restart through per-wave flags kept by round (bf16) or
-//     pair (e4m3) parity: a wave publishes whether step j overshot before the
-//     barrier that opens step j + 1, and every wave reads all flags of step j
-//     after that barrier.  The next write to those flags (step j + 2) happens
-//     after the barrier that opens step j + 2, which every reader has
-//     reached, so all waves see the same flags and leave the loop at the same
-//     barrier.  (A single flag, set while a slower wave may not yet have read
-//     it after the same barrier, lets waves leave at different barriers.)
+//   * The softmax keeps the library kernels' fixed reference max: a row's
+//     reference is its first visible pair's max, and probabilities are taken
+//     against it with no rescaling while scores stay within 32 (log2 units)
+//     of it (fp32 and bf16 keep full relative precision below 2^32).  When a
+//     row's score overshoots by more, the library kernels restart the item;
+//     here the accumulator is in VGPRs, so the wave raises the reference of
+//     its overshooting rows and rescales their sums in place (128
+//     multiplications per lane), with no exchange between waves: each wave's
+//     rows are its own.  An item's cost is then linear in its length for any
+//     scores.
 //   * An item's key range is clamped to the sequence's device length, so a
 //     plan made for longer lengths reads no row past the sequence's pages.
 //   * Split row blocks leave bf16 partials (normalised O) and fp32 LSE, which
@@ -80,27 +80,24 @@ constexpr int kF8RoundBytes = kRoundTok * kF8RowBytes;   // one round of e4m3 ro
 constexpr int kF8Copies = kF8RoundBytes / 1024;          // its 1 KB copies
 constexpr int kScaleRoundBytes = kRoundTok * 4;          // one round's fp32 scales
 
-// LDS map.  bf16: an 8-stage ring of key tiles (two rounds), then the
-// restart flags [2][8] (round parity, wave).  e4m3: two pair buffers of two
-// bf16 tiles each (the keys being computed, widened), a ring of two e4m3
-// rounds in cache row order, the rounds' scales, the pair buffers' scales,
-// then the flags [2][8] (pair parity, wave).
+// LDS map.  bf16: an 8-stage ring of key tiles (two rounds).  e4m3: two pair
+// buffers of two bf16 tiles each (the keys being computed, widened), a ring
+// of two e4m3 rounds in cache row order, the rounds' scales and the pair
+// buffers' scales.
 template <int KVD> struct Lds;
 template <> struct Lds<0> {
   static constexpr int kStages = 8;
-  static constexpr int kFlagOff = kStages * kTileBytes;
-  static constexpr int kBytes = kFlagOff + 2 * 8 * 4;
+  static constexpr int kBytes = kStages * kTileBytes;
 };
 template <> struct Lds<1> {
   static constexpr int kStages = 4;
   static constexpr int kRing = kStages * kTileBytes;
   static constexpr int kRingScale = kRing + 2 * kF8RoundBytes;
   static constexpr int kPairScale = kRingScale + 2 * kScaleRoundBytes;
-  static constexpr int kFlagOff = kPairScale + 2 * 2 * kTileTok * 4;
-  static constexpr int kBytes = kFlagOff + 2 * 8 * 4;
+  static constexpr int kBytes = kPairScale + 2 * 2 * kTileTok * 4;
 };
 static_assert(Lds<1>::kBytes <= 160 * 1024, "e4m3 LDS map exceeds a workgroup's LDS");
-constexpr float kRestartMargin = 32.0f;       // log2 units above the reference max
+constexpr float kRescaleMargin = 32.0f;       // log2 units above the reference max
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // A wave-uniform pointer, kept in SGPRs (the copies take a scalar base).
@@ -128,16 +125,6 @@ __device__ __forceinline__ float quad_sum(float x) {
   const unsigned v = __float_as_uint(x);
   auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-}
-
-// Whether any of the 8 waves published an overshoot in the flags of one
-// round parity (two 16-byte LDS reads).
-__device__ __forceinline__ bool any_flag(volatile LDS_PTR(int) flags, int parity) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const i32x4 a = *(const LDS_PTR(i32x4))((LDS_PTR(int))flags + parity * 8);
-  const i32x4 b = *(const LDS_PTR(i32x4))((LDS_PTR(int))flags + parity * 8 + 4);
-  const i32x4 o = a | b;
-  return (o.x | o.y | o.z | o.w) != 0;
 }
 
 struct Ring {
@@ -217,13 +204,14 @@ __device__ __forceinline__ void issue_round_f8(const RingF8& r, int j) {
   const int vo = 16 * lane;
   // bytes of the round inside the sequence (rows < L - kr)
   const int valid_bytes = min(r.L - kr, kRoundTok) * kF8RowBytes;
+  const int wave = opaque_s(r.wave);
 #pragma unroll
   for (int k = 0; k < (kF8Copies + 7) / 8; ++k) {
-    const int ins = r.wave + 8 * k;
+    const int ins = wave + 8 * k;
     if (ins < kF8Copies && vo + 1024 * ins < valid_bytes)
       lds_dma_x4(lds + ins * 1024, vo, base + 1024 * ins);
   }
-  if (r.wave == 7) {
+  if (wave == 7) {
     const int tok = lane < r.L - kr ? lane : 0;
     lds_dma_x1(r.ring_scale + (j & 1) * kScaleRoundBytes, tok * 4,
                uniform_ptr(r.kv_scale + row0));
@@ -250,11 +238,13 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // go to the waves by bi % 8; lane l writes slot l of a block, i.e. row 8 rh +
 // r8, chunk 8 cg + c8 as the copy layout places them.  Rows at or past the
 // sequence's end become zeros.
-__device__ __forceinline__ void widen_pair_f8(char* smem, int p, int kp, int L, int wave,
+__device__ __forceinline__ void widen_pair_f8(char* smem, int p, int kp, int L, int wave_id,
                                               int lane_id) {
-  // an opaque copy of the lane id keeps the per-lane offsets below inside the
-  // key loop rather than hoisted out of it (they would pin registers there)
+  // opaque copies of the lane and wave ids keep the per-lane offsets and the
+  // per-wave conditions below inside the key loop rather than hoisted out of
+  // it (they would pin registers there)
   const int lane = opaque(lane_id);
+  const int wave = opaque_s(wave_id);
   const int rh = wave & 1;
   const int q = lane >> 4, lo = (lane >> 3) & 1;
   const int c8 = 2 * q + (lo ^ rh);
@@ -292,11 +282,9 @@ struct Frag {
 
 // QK^T, softmax and PV of one pair of 16-key stages (keys kp .. kp + 31) whose
 // bf16 tiles sit at LDS offset so and so + one tile.  For e4m3 the 32 per-key
-// scales at ksc_off multiply the scores and the probabilities.  Returns true
-// when the pair's scores overshoot the reference max (m raised; nothing
-// accumulated).
+// scales at ksc_off multiply the scores and the probabilities.
 template <int KVD>
-__device__ __forceinline__ bool pair_step(char* smem, const Frag& fr, int so, int ksc_off, int kp,
+__device__ __forceinline__ void pair_step(char* smem, const Frag& fr, int so, int ksc_off, int kp,
                                           int lim, int lim_all, float scale_log2, int g4,
                                           const bf16x8 (&qf)[18], f32x4 (&acc)[32], float& m,
                                           float& l) {
@@ -362,9 +350,14 @@ __device__ __forceinline__ bool pair_step(char* smem, const Frag& fr, int so, in
   mx = quad_max(mx);
   // a row's first visible pair fixes its reference max
   m = (m == -INFINITY) ? mx : m;
-  if (__any(mx > m + kRestartMargin)) {
-    m = fmaxf(m, mx);
-    return true;
+  if (__any(mx > m + kRescaleMargin)) {
+    // raise the overshooting rows' reference to this pair's max and rescale
+    // their sums (a factor of at most 2^-32; 1 for the other rows)
+    const float alpha = mx > m + kRescaleMargin ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+    m = mx > m + kRescaleMargin ? mx : m;
+    l *= alpha;
+#pragma unroll
+    for (int cm = 0; cm < 32; ++cm) acc[cm] *= alpha;
   }
   bf16x8 pf;
 #pragma unroll
@@ -395,7 +388,6 @@ __device__ __forceinline__ bool pair_step(char* smem, const Frag& fr, int so, in
       acc[cm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cm % VW], pf, acc[cm], 0, 0, 0);
     }
   }
-  return false;
 }
 
 template <int KVD>
@@ -442,8 +434,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
     fr.vb_e = vrh * 1024 + 16 * (8 * (vx ^ vrh) + vr8) + 8 * (l16 & 1);
     fr.vb_o = vrh * 1024 + 16 * (8 * (vx ^ vrh) + (vr8 ^ 4)) + 8 * (l16 & 1);
   }
-  // [parity][wave]
-  volatile LDS_PTR(int) flags = (volatile LDS_PTR(int))(smem + Lds<KVD>::kFlagOff);
 
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* item = items + it * kItemWords;
@@ -495,52 +485,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       ring.ntiles = ntiles;
       ring.lane = lane;
 
-      for (;;) {   // runs once unless a score overshoots the reference max
-        if (nrounds > 0) issue_round(ring, tq, half, 0);
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
-        l = 0.f;
-        bool again = false;       // workgroup-uniform: some wave overshot
-        bool overshoot = false;   // wave-uniform: this wave overshot in the last round
-
-        // Round j opens by publishing round j-1's overshoot, waiting for this
-        // wave's copies and the barrier, and stopping the pass if any wave
-        // overshot in round j-1; after the last round the same is done once
-        // more.
-        for (int j = 0; j < nrounds; ++j) {
-          if (j > 0 && lane == 0) flags[((j - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
-          MLA_VM_WAIT(0);
-          barrier();   // tiles of round j come from all waves
-          if (j > 0 && any_flag(flags, (j - 1) & 1)) {
-            again = true;
-            break;
-          }
-          if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1);
-          overshoot = false;
-
+      for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
+      if (nrounds > 0) issue_round(ring, tq, half, 0);
+      // Round j opens by waiting for this wave's copies and the barrier (the
+      // round's tiles come from all waves, and every wave is done with the
+      // stages round j + 1 refills); round j + 1 is then issued.
+      for (int j = 0; j < nrounds; ++j) {
+        MLA_VM_WAIT(0);
+        barrier();   // tiles of round j come from all waves
+        if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1);
 #pragma unroll
-          for (int pp = 0; pp < kRoundTiles / 2; ++pp) {
-            const int tile = kRoundTiles * j + 2 * pp;   // first stage of the pair
-            if (tile >= ntiles) break;
-            const int kp = k0 + kTileTok * tile;          // first key of the pair
-            const int so = (tile % Lds<0>::kStages) * kTileBytes;
-            if (pair_step<0>(smem, fr, so, 0, kp, lim, lim_all, a.scale_log2, g4, qf, acc, m,
-                             l)) {
-              overshoot = true;
-              break;
-            }
-          }
+        for (int pp = 0; pp < kRoundTiles / 2; ++pp) {
+          const int tile = kRoundTiles * j + 2 * pp;   // first stage of the pair
+          if (tile >= ntiles) break;
+          const int kp = k0 + kTileTok * tile;          // first key of the pair
+          const int so = (tile % Lds<0>::kStages) * kTileBytes;
+          pair_step<0>(smem, fr, so, 0, kp, lim, lim_all, a.scale_log2, g4, qf, acc, m, l);
         }
-        if (!again && nrounds > 0) {   // the loop ran out: check its last round
-          if (lane == 0) flags[((nrounds - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
-          MLA_VM_WAIT(0);
-          barrier();
-          again = any_flag(flags, (nrounds - 1) & 1);
-        }
-        // Every wave left at the same barrier with the same `again`; no copy
-        // is in flight (the last wait drained them) and no wave reads the
-        // ring after that barrier, so a new pass may refill it.
-        if (!again) break;
       }
     } else {
       RingF8 ring;
@@ -562,56 +524,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       // in iteration 2r - 1, into the ring slot whose round was widened by
       // then, and waited for in iteration 2r + 1, the first to widen it.  Only
       // that round is in flight at the wait.
-      for (;;) {   // runs once unless a score overshoots the reference max
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
-        l = 0.f;
-        bool again = false;
-        bool overshoot = false;
-        if (npairs > 0) {
-          issue_round_f8(ring, 0);
-          MLA_VM_WAIT(0);
-          barrier();   // round 0 comes from all waves
-          widen_pair_f8(smem, 0, k0, L, wave, lane);
-          if (nrounds > 1) issue_round_f8(ring, 1);
-        }
-        // Pair p opens by publishing pair p-1's overshoot and the barrier, and
-        // stops the pass if any wave overshot in pair p-1 (the flags are kept
-        // by pair parity, as for the bf16 rounds).  The two pairs of a round
-        // are written out, so that a pair's parity (its buffer, whether it
-        // waits and issues) is known at compile time.
-        for (int j = 0; j < nrounds && !again; ++j) {
+      for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
+      if (npairs > 0) {
+        issue_round_f8(ring, 0);
+        MLA_VM_WAIT(0);
+        barrier();   // round 0 comes from all waves
+        widen_pair_f8(smem, 0, k0, L, wave, lane);
+        if (nrounds > 1) issue_round_f8(ring, 1);
+      }
+      // Pair p opens with the barrier after which pair p is widened by all
+      // waves (and, for odd p, round (p + 1) / 2 has landed).  The two pairs
+      // of a round are written out, so that a pair's parity (its buffer,
+      // whether it waits and issues) is known at compile time.
+      for (int j = 0; j < nrounds; ++j) {
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const int p = 2 * j + pp;
-            if (p >= npairs) break;
-            if (p > 0 && lane == 0) flags[(1 - pp) * 8 + wave] = overshoot ? 1 : 0;
-            if (pp == 1) MLA_VM_WAIT(0);
-            barrier();   // pair p widened by all waves; for odd p, round j + 1 copied
-            if (p > 0 && any_flag(flags, 1 - pp)) {
-              again = true;
-              break;
-            }
-            if (pp == 1 && j + 2 < nrounds) issue_round_f8(ring, j + 2);
-            if (p + 1 < npairs)
-              widen_pair_f8(smem, p + 1, k0 + 2 * kTileTok * (p + 1), L, wave, lane);
-            overshoot = pair_step<1>(smem, fr, pp * 2 * kTileBytes,
-                                     Lds<1>::kPairScale + pp * 2 * kTileTok * 4,
-                                     k0 + 2 * kTileTok * p, lim, lim_all, a.scale_log2, g4, qf,
-                                     acc, m, l);
-          }
+        for (int pp = 0; pp < 2; ++pp) {
+          const int p = 2 * j + pp;
+          if (p >= npairs) break;
+          if (pp == 1) MLA_VM_WAIT(0);
+          barrier();   // pair p widened by all waves; for odd p, round j + 1 copied
+          if (pp == 1 && j + 2 < nrounds) issue_round_f8(ring, j + 2);
+          if (p + 1 < npairs)
+            widen_pair_f8(smem, p + 1, k0 + 2 * kTileTok * (p + 1), L, wave, lane);
+          pair_step<1>(smem, fr, pp * 2 * kTileBytes, Lds<1>::kPairScale + pp * 2 * kTileTok * 4,
+                       k0 + 2 * kTileTok * p, lim, lim_all, a.scale_log2, g4, qf, acc, m, l);
         }
-        if (!again && npairs > 0) {   // the loop ran out: check its last pair
-          if (lane == 0) flags[((npairs - 1) & 1) * 8 + wave] = overshoot ? 1 : 0;
-          MLA_VM_WAIT(0);
-          barrier();
-          again = any_flag(flags, (npairs - 1) & 1);
-        } else if (again) {
-          // a round may still be landing: drain it before the ring is refilled
-          MLA_VM_WAIT(0);
-          barrier();
-        }
-        if (!again) break;
       }
     }
 

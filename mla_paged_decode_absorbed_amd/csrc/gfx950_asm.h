@@ -63,6 +63,14 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// An opaque copy of a wave-uniform value, kept in an SGPR: conditions on it
+// are evaluated where they are used (a few scalar instructions) rather than
+// hoisted out of the loop, where each would hold a register.
+__device__ __forceinline__ int opaque_s(int x) {
+  asm volatile("" : "=s"(x) : "0"(x));
+  return x;
+}
+
 // Require v to be resident in VGPRs here (the compiler then places its wait
 // for the load that produced v at this point).
 template <typename T>

@@ -25,6 +25,7 @@ inline void lds_dma_x1(uint32_t lds_base, int voff, const void* sbase) {
 #define MLA_VM_WAIT(N) emu::vm_wait(N)
 inline void barrier() { emu::block_barrier(); }
 inline int opaque(int x) { return x; }
+inline int opaque_s(int x) { return x; }
 template <typename T>
 inline void require_vgpr(const T&) {}
 }  // namespace mla

@@ -250,13 +250,15 @@ def test_fifth_fault_case_replays_in_bounds_with_its_plan():
 # check the result through all the restarts.
 
 
-def _rising_scores_case(kv_dtype, L=300, H=16):
+def _rising_scores_case(kv_dtype, L=300, H=16, q_value=1.0):
+    # q_value (a power of two) scales the query up and the cached values down
+    # by the same factor: the same scores, smaller outputs
     import torch
     case = make_case(kv_lens=[L], q_lens=[1], num_heads=H, seed=41, kv_dtype=kv_dtype,
                      sm_scale=1 / math.sqrt(192))
-    ones = torch.ones(576, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
-    case.q[0, 0, :] = ones.view(np.uint16)
-    c = (np.arange(L, dtype=np.float32) * np.float32(0.6 / 32)).astype(np.float32)
+    qv = torch.full((576,), float(q_value)).to(torch.bfloat16).view(torch.int16).numpy()
+    case.q[0, 0, :] = qv.view(np.uint16)
+    c = (np.arange(L, dtype=np.float32) * np.float32(0.6 / 32 / q_value)).astype(np.float32)
     for j in range(L):
         page, slot = case.block_table[0, j // case.page_size], j % case.page_size
         if kv_dtype == "bf16":
@@ -265,7 +267,7 @@ def _rising_scores_case(kv_dtype, L=300, H=16):
         else:
             # every code 448 (0x7E) with scale c_j / 448: the row decodes to c_j
             case.kv[page, slot] = 0x7E
-            case.kv_scale[page, slot] = np.float32(max(c[j], 1e-3) / 448.0)
+            case.kv_scale[page, slot] = np.float32(max(c[j], 1e-3 / q_value) / 448.0)
     return case
 
 
@@ -274,8 +276,8 @@ def _rising_scores_case(kv_dtype, L=300, H=16):
     "a faster wave set it in the same round leaves the round loop one barrier early; the "
     "drift schedule reaches it and reports the barrier deadlock.  On the GPU the flag is read "
     "right after the barrier and set no sooner than one QK step and softmax later (one wave per "
-    "SIMD); the fix (per-wave flags by round parity) is in decode_w8_kernel.hip and would "
-    "change the validated machine code"))
+    "SIMD); a fix (per-wave flags by round parity) would change the validated machine code, "
+    "and the candidate kernel in decode_w8_kernel.hip rescales instead of restarting"))
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
 def test_library_restart_flag_under_drift(kv_dtype):
     case = _rising_scores_case(kv_dtype, L=160)
@@ -345,9 +347,10 @@ def test_w8_kernel_matches_oracle():
         _check(c, out, lse)
 
 
-def test_w8_kernel_restarts():
-    # the drift schedules let one wave overshoot (and publish it) a whole
-    # round ahead of the others: the round-parity flags keep them at one barrier
+def test_w8_kernel_rescales():
+    # scores that overshoot the reference max (a late dominant key, scores
+    # rising by 36 log2 units every 32 keys): each wave raises its rows'
+    # reference and rescales their sums in place, in every schedule
     jobs = [(c, 1, 1, dict(env_extra={**MODES[mode], **W8}))
             for c in (_late_dominant_key_case(), _rising_scores_case("bf16"))
             for mode in ("wait-lockstep", "wait-drift", "issue-drift")]
@@ -417,7 +420,7 @@ def test_w8_e4m3_kernel_matches_oracle():
         _check(c, out, lse)
 
 
-def test_w8_e4m3_kernel_restarts():
+def test_w8_e4m3_kernel_rescales():
     jobs = [(c, 1, 1, dict(env_extra={**MODES[mode], **W8}))
             for c in (_dominant_key_case_f8(), _rising_scores_case("fp8_e4m3"))
             for mode in ("wait-lockstep", "wait-drift", "issue-drift")]
@@ -498,3 +501,17 @@ def test_w8_stale_plan_without_the_clamp_reads_outside_the_cache():
         with pytest.raises(RuntimeError, match="AddressSanitizer"):
             harness.run(case, 3, 1, binary=binary, plan_kv_lens=[1200, 900, 300],
                         env_extra={**MODES["issue-drift"], **W8})
+
+
+
+def test_w8_rescaling_keeps_long_rising_sequences_linear():
+    # 2048 keys whose scores rise by about 36 log2 units every 32 keys: the
+    # library kernels would restart the item at every 32-key step (64 passes
+    # over a growing prefix); the candidate rescales and passes over the keys
+    # once.  Checked against the oracle for both cache types.
+    cases = [_rising_scores_case(kvd, L=2048, q_value=16.0) for kvd in ("bf16", "fp8_e4m3")]
+    O, L = oracle.mla_decode_ref(cases[0])
+    assert L[0, 0, 0] * math.log2(math.e) > 60 * 32
+    jobs = [(c, 1, 1, dict(env_extra={**MODES["issue-drift"], **W8})) for c in cases]
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+        _check(c, out, lse)
