@@ -303,12 +303,14 @@ def test_emulated_restart_storm_with_rising_scores(kv_dtype):
 
 
 def test_emulated_full_length_sequences():
+    # the library kernels and the two-waves-per-SIMD candidate (below) on the
+    # same two sequences, all four runs at once
     cases = [make_case(kv_lens=[L], q_lens=[q], num_heads=128, seed=51, kv_dtype=kvd,
                        sm_scale=1 / math.sqrt(192))
              for L, q, kvd in ((32768, 1, "fp8_e4m3"), (4096, 2, "bf16"))]
-    res = harness.run_many([(c, 16, 1, dict(env_extra=MODES["wait-lockstep"], timeout=1200))
-                            for c in cases])
-    for c, (out, lse, meta) in zip(cases, res):
+    jobs = [(c, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **extra}, timeout=1500))
+            for extra in ({}, {"MLA_DECODE_KERNEL": "w8"}) for c in cases]
+    for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
         assert meta["num_partials"] >= 8
         _check(c, out, lse)
 
@@ -358,15 +360,12 @@ def test_w8_kernel_rescales():
         _check(c, out, lse)
 
 
-def test_w8_kernel_fixed_shape_plan_and_full_length():
+def test_w8_kernel_fixed_shape_plan():
+    # (its full-length sequences run in test_emulated_full_length_sequences)
     fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
                       sm_scale=1 / math.sqrt(192))
-    full = make_case(kv_lens=[4096], q_lens=[2], num_heads=128, seed=51,
-                     sm_scale=1 / math.sqrt(192))
-    jobs = [(fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **W8})),
-            (full, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **W8}, timeout=1200))]
-    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
-        _check(c, out, lse)
+    out, lse, _ = harness.run(fixed, 8, 1, fixed=True, env_extra={**MODES["issue-drift"], **W8})
+    _check(fixed, out, lse)
 
 
 def test_w8_emulation_catches_a_missing_barrier(tmp_path):
@@ -430,15 +429,11 @@ def test_w8_e4m3_kernel_rescales():
         _check(c, out, lse)
 
 
-def test_w8_e4m3_kernel_fixed_shape_plan_and_full_length():
+def test_w8_e4m3_kernel_fixed_shape_plan():
     fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
                       kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192))
-    full = make_case(kv_lens=[32768], q_lens=[1], num_heads=128, seed=51, kv_dtype="fp8_e4m3",
-                     sm_scale=1 / math.sqrt(192))
-    jobs = [(fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **W8})),
-            (full, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **W8}, timeout=1500))]
-    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
-        _check(c, out, lse)
+    out, lse, _ = harness.run(fixed, 8, 1, fixed=True, env_extra={**MODES["issue-drift"], **W8})
+    _check(fixed, out, lse)
 
 
 @pytest.mark.parametrize("marker", [
