@@ -234,10 +234,13 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // Widen pair p of the item (keys kp .. kp + 31, the half p & 1 of round p >> 1
 // in ring slot (p >> 1) & 1) into pair buffer p & 1, in the bf16 tile layout
 // the MFMA steps read, and its 32 scales into the buffer's scale slot.  The
-// pair's 36 output blocks of 1 KB (stage bi / 18, block bi % 18 = 2 cg + rh)
-// go to the waves by bi % 8; lane l writes slot l of a block, i.e. row 8 rh +
-// r8, chunk 8 cg + c8 as the copy layout places them.  Rows at or past the
-// sequence's end become zeros.
+// pair's 36 output blocks of 1 KB (stage bi / 18, block bi % 18 = 2 cg + rh:
+// rows 8 rh .. + 7, chunks 8 cg .. + 7) go to the waves by bi % 8.  Lane l
+// takes chunk c8 = l % 8 of row r8 = c8 ^ (l / 8): each 16 lanes then read
+// one 8-byte piece per bank pair (rows 576 bytes apart fall on alternate
+// halves of the banks, and the two rows of a chunk have opposite parity), and
+// each 8 lanes write distinct 16-byte bank groups of the tile layout.  Rows at
+// or past the sequence's end become zeros.
 __device__ __forceinline__ void widen_pair_f8(char* smem, int p, int kp, int L, int wave_id,
                                               int lane_id) {
   // opaque copies of the lane and wave ids keep the per-lane offsets and the
@@ -246,13 +249,13 @@ __device__ __forceinline__ void widen_pair_f8(char* smem, int p, int kp, int L, 
   const int lane = opaque(lane_id);
   const int wave = opaque_s(wave_id);
   const int rh = wave & 1;
-  const int q = lane >> 4, lo = (lane >> 3) & 1;
-  const int c8 = 2 * q + (lo ^ rh);
-  const int r8 = (lane & 7) ^ (4 * (q & 1));
+  const int c8 = lane & 7;
+  const int r8 = c8 ^ (lane >> 3);
   const int row = 8 * rh + r8;   // within a stage
+  const int slot = 16 * (c8 >> 1) + 8 * ((c8 & 1) ^ rh) + (r8 ^ (4 * ((c8 >> 1) & 1)));
   const uint32_t src = Lds<1>::kRing + ((p >> 1) & 1) * kF8RoundBytes +
                        (p & 1) * (2 * kTileTok * kF8RowBytes) + row * kF8RowBytes + 8 * c8;
-  const uint32_t dst = (p & 1) * 2 * kTileBytes + 16 * lane;
+  const uint32_t dst = (p & 1) * 2 * kTileBytes + 16 * slot;
 #pragma unroll
   for (int k = 0; k < (2 * 18 + 7) / 8; ++k) {
     const int bi = wave + 8 * k;
