@@ -48,7 +48,7 @@ def test_w8_small_cases(kv_lens, q_lens, nwg):
     check(case, out, lse)
 
 
-def test_w8_restarts():
+def test_w8_peaky_softmax():
     case = make_case(kv_lens=[2000, 513], q_lens=[1, 2], seed=18, q_std=8.0,
                      sm_scale=1 / math.sqrt(192))
     print("w8: peaky softmax", flush=True)
@@ -56,11 +56,17 @@ def test_w8_restarts():
     check(case, out, lse)
 
 
-def test_w8_deepseek_v3_decode():
-    case = workload("v3_decode_bf16")
-    print("w8: v3_decode_bf16", flush=True)
-    (out, lse), _ = run_gpu(case)
-    check(case, out, lse)
+@pytest.mark.parametrize("name", ["v3_decode_bf16", "mtp_verify_bf16", "long_ctx_fp8",
+                                  "ragged_serving_bf16"])
+def test_w8_full_size_workloads(name):
+    # every sequence of the four workloads at full size, in the launch
+    # configuration bench.py times, one-phase plans
+    case = workload(name)
+    print(f"w8: {name}", flush=True)
+    (out, lse), pl = run_gpu(case, phases=1)
+    assert pl.phases == 1
+    worst, rel = check(case, out, lse)
+    print(f"w8: {name}: max-abs {worst:.3g} rel-L2 {rel:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("kv_lens,q_lens,nwg,P", [
@@ -74,14 +80,6 @@ def test_w8_e4m3_small_cases(kv_lens, q_lens, nwg, P):
                      kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192))
     print(f"w8 e4m3: lengths {kv_lens} q {q_lens} workgroups {nwg} pages {P}", flush=True)
     (out, lse), pl = run_gpu(case, num_workgroups=nwg, phases=1)
-    assert pl.phases == 1
-    check(case, out, lse)
-
-
-def test_w8_e4m3_long_context():
-    case = workload("long_ctx_fp8")
-    print("w8: long_ctx_fp8 (every sequence)", flush=True)
-    (out, lse), pl = run_gpu(case, phases=1)
     assert pl.phases == 1
     check(case, out, lse)
 
