@@ -243,6 +243,13 @@ mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups
  *                fp32 O [num_partials][128][d_latent], then fp32 LSE
  *                [num_partials][128].
  *
+ * Kernel choice: the environment variable MLA_DECODE_KERNEL=w8 selects, for
+ * one-phase plans, a candidate kernel with two waves per SIMD (not yet run on
+ * a GPU).  It writes the partial O as bf16 [num_partials][128][d_latent] in
+ * the first half of the same area (the LSE where it always is), and
+ * mla_combine, seeing the same setting, merges that layout: both calls of a
+ * step must see the same value.
+ *
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, BAD_PLAN,
  * WORKSPACE_TOO_SMALL, HIP (launch failure).
  */
@@ -258,7 +265,8 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info,
  * split-K key partition of the FlashAttention-3 in DeepSeek-R1 page, chapter
  * 2, exact up to rounding): for each combine entry of the plan,
  *   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) * O_s  -> bf16,
- * reading the workspace partials laid out as described for mla_decode_fwd.
+ * reading the workspace partials laid out as described for mla_decode_fwd
+ * (bf16 O under MLA_DECODE_KERNEL=w8 for one-phase plans, fp32 otherwise).
  * A row whose partials are all empty (LSE_s = -inf) gets O = 0, LSE = -inf.
  * No-op when info->num_combine == 0.  Must run after mla_decode_fwd on the
  * same stream (or after the caller filled the partials itself).
