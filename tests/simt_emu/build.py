@@ -26,6 +26,25 @@ KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
                 "check.h", "check_kernel.hip", "decode_w8_kernel.hip"]
 
 
+# compilation units of the library built into the emulator binary
+UNITS = ("decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip", "plan_kernel.hip",
+         "tree_kernel.hip", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip",
+         "check_kernel.hip", "decode_w8_kernel.hip", "api.cpp", "plan.cpp")
+
+
+def _includes(path: str, src: str, seen=None) -> set:
+    """Local headers a source includes, directly or through other local
+    headers (#include "name" found in src)."""
+    import re
+    seen = set() if seen is None else seen
+    for name in re.findall(r'^\s*#include\s+"([^"]+)"', open(path).read(), re.M):
+        h = os.path.join(src, name)
+        if name not in seen and os.path.exists(h):
+            seen.add(name)
+            _includes(h, src, seen)
+    return seen
+
+
 def compiler() -> str:
     for c in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
         if c and os.path.exists(c):
@@ -60,14 +79,22 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
              f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument", "-Wno-psabi"]
     if sanitize:
         flags.append("-fsanitize=address")
-    units = [os.path.join(src, f) for f in ("decode_kernel.hip", "combine_kernel.hip",
-                                             "append_kernel.hip", "plan_kernel.hip",
-                                             "tree_kernel.hip", "prefill_quant_kernel.hip",
-                                             "prefill_attn_kernel.hip", "check_kernel.hip",
-                                             "decode_w8_kernel.hip", "api.cpp", "plan.cpp")]
+    units = [os.path.join(src, f) for f in UNITS]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
+    # A variant recompiles only the units that are, or include, a changed
+    # file, and links the base build's other objects (brought up to date
+    # first).
+    changed = set(patches or {}) | ({"decode_kernel.hip"} if decode_source else set())
+    reuse = bool(tag) and sanitize
+    if reuse:
+        from tests.simt_emu import harness as _h
+        _h.ensure_built()
+
     def compile_unit(u):
-        obj = os.path.join(out, os.path.basename(u) + ".o")
+        name = os.path.basename(u)
+        if reuse and not (_includes(u, src) & changed) and name not in changed:
+            return os.path.join(OUT, name + ".o")
+        obj = os.path.join(out, name + ".o")
         cmd = [compiler(), *flags, "-x", "c++", "-c", u, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:

@@ -447,7 +447,7 @@ def test_w8_e4m3_emulation_catches_a_missing_wait(tmp_path, marker):
     from tests.simt_emu import build as _b
     src = open(os.path.join(_b.CSRC, "decode_w8_kernel.hip")).read()
     assert src.count(marker) == 1
-    binary = _b.build(tag="w8_f8_planted_" + str(abs(hash(marker)) % 1000), patches={
+    binary = _b.build(tag="w8_f8_planted_" + ("barrier" if "barrier" in marker else "wait"), patches={
         "decode_w8_kernel.hip": [(marker, "/* removed */")]})
     case = make_case(kv_lens=[700, 300], q_lens=[2, 1], seed=5, kv_dtype="fp8_e4m3",
                      sm_scale=1 / math.sqrt(192))
