@@ -142,9 +142,30 @@ def _wait_states(i):
     return int(i.split()[1]) + 1 if op == "s_nop" else 1
 
 
+EXEC = {"exec", "exec_lo", "exec_hi"}
+
+
+def _valu_sgpr_writes(p):
+    """SGPRs a VALU instruction writes (its first operand if scalar), with
+    EXEC named "exec" (v_cmpx_* write it, in either encoding)."""
+    op = p.split()[0]
+    out = set()
+    if not op.startswith("v_") or " " not in p:
+        return out
+    dst = p.split(None, 1)[1].split(",")[0].strip()
+    out |= _sgprs(dst)
+    if dst in EXEC or op.startswith("v_cmpx"):
+        out.add("exec")
+    return out
+
+
 def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
     """Walks back from every copy over all control-flow paths (through
-    branches and fall-throughs), not only inside the copy's own block."""
+    branches and fall-throughs), not only inside the copy's own block.  The
+    registers a copy reads are its scalar base and EXEC (the lanes that copy):
+    the compiler's hazard recognizer does not see that inline assembly reads
+    EXEC, so a VALU write of EXEC (v_cmpx) is held to the same five wait
+    states."""
     for name, blocks in _kernels(isa[1]).items():
         preds = _predecessors(blocks)
 
@@ -154,9 +175,7 @@ def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
                 if ws >= 5:
                     return
                 p = ins[j]
-                if p.split()[0].startswith("v_") and " " in p:
-                    dst = p.split(None, 1)[1].split(",")[0].strip()
-                    assert not (_sgprs(dst) & used), f"{name} {lab}: {p} reaches a copy"
+                assert not (_valu_sgpr_writes(p) & used), f"{name} {lab}: {p} reaches a copy"
                 ws += _wait_states(p)
             if ws < 5 and depth < 8:
                 for q in preds[k]:
@@ -168,11 +187,19 @@ def test_valu_written_sgpr_not_read_by_lds_copy_within_five_wait_states(isa):
                 if not i.startswith("global_load_lds"):
                     continue
                 copies += 1
-                used = set()
+                used = {"exec"}
                 for tok in i.split(None, 1)[1].split(","):
                     used |= _sgprs(tok.strip().split()[0])
                 walk(k, j, used, 0, 0)
         assert copies > 0, name
+
+
+def test_valu_exec_write_walk_catches_a_planted_cmpx():
+    assert _valu_sgpr_writes("v_cmpx_gt_i32_e32 vcc, s94, v3") == {"exec"}
+    assert _valu_sgpr_writes("v_cmpx_lt_u32_e64 s[4:5], v1, v2") == {4, 5, "exec"}
+    assert _valu_sgpr_writes("v_readlane_b32 exec_lo, v1, 0") == {"exec"}
+    assert _valu_sgpr_writes("v_readfirstlane_b32 s7, v1") == {7}
+    assert _valu_sgpr_writes("s_and_saveexec_b64 s[2:3], vcc") == set()
 
 
 def test_hazard_walk_follows_branches():
