@@ -758,6 +758,12 @@ def main() -> int:
         "us_tree_merge": None if tree_avg is None else round(tree_avg * 1e3, 2),
         "tflops": round(tflops, 2),
         "pct_roofline_call": round(100 * max(t_hbm, t_mfma) / t_step, 1),
+        # the decode kernel's algorithmic MFMA work over its time, as a
+        # fraction of the dense bf16 peak: a lower bound on the matrix units'
+        # busy fraction (the kernel issues at least this work, more where a
+        # key tile or a row block is padded), and the same for HBM bytes
+        "mfma_frac_fwd": round(cnt["flops"] / t_fwd / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+        "hbm_frac_fwd": round(cnt["alg_bytes"] / t_fwd / (HBM_PEAK_GBS * 1e9), 4),
         "roofline": {
             "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
