@@ -510,3 +510,27 @@ def test_w8_rescaling_keeps_long_rising_sequences_linear():
     jobs = [(c, 1, 1, dict(env_extra={**MODES["issue-drift"], **W8})) for c in cases]
     for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
         _check(c, out, lse)
+
+
+def test_w8_random_shapes():
+    """Seeded random shapes through the candidate, both cache types and both
+    copy-landing modes: batch, heads, draft tokens (with idle and zero-length
+    sequences), page size, lengths and workgroup count drawn at random."""
+    rng = np.random.default_rng(77)
+    jobs = []
+    for trial in range(40):
+        kvd = ("bf16", "fp8_e4m3")[trial % 2]
+        B = int(rng.integers(1, 6))
+        H = int(rng.choice([16, 32, 128]))
+        qmax = int(rng.integers(1, 5))
+        P = int(rng.choice([64, 256] if kvd == "fp8_e4m3" else [16, 64, 256]))
+        ql = rng.integers(0, qmax + 1, size=B)
+        kvl = np.where(ql > 0, rng.integers(0, 700, size=B) + ql, rng.integers(0, 40, size=B))
+        nwg = int(rng.integers(1, 20))
+        case = make_case(kv_lens=kvl.tolist(), q_lens=ql.tolist(), num_heads=H, page_size=P,
+                         kv_dtype=kvd, max_q_len=qmax, seed=100 + trial,
+                         sm_scale=1 / math.sqrt(192))
+        mode = ("wait-lockstep", "issue-drift")[(trial // 2) % 2]
+        jobs.append((case, nwg, 1, dict(env_extra={**MODES[mode], **W8})))
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs, workers=8)):
+        _check(c, out, lse)
