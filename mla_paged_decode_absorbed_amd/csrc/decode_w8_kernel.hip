@@ -491,6 +491,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
       if (nrounds > 0) issue_round(ring, tq, half, 0);
+      // Q must be resident before the key loop: otherwise the compiler,
+      // which does not see the copies, keeps its loads pending into the loop
+      // and waits for them there with vmcnt literals that, at run time, also
+      // count the next round's copies in flight.  Here the wave waits for
+      // round 0 anyway (the loop's first wait).
+#pragma unroll
+      for (int c = 0; c < 18; ++c) require_vgpr(qf[c]);
       // Round j opens by waiting for this wave's copies and the barrier (the
       // round's tiles come from all waves, and every wave is done with the
       // stages round j + 1 refills); round j + 1 is then issued.
@@ -532,6 +539,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       if (npairs > 0) {
         issue_round_f8(ring, 0);
         MLA_VM_WAIT(0);
+        // Q resident before the key loop (see the bf16 path)
+#pragma unroll
+        for (int c = 0; c < 18; ++c) require_vgpr(qf[c]);
         barrier();   // round 0 comes from all waves
         widen_pair_f8(smem, 0, k0, L, wave, lane);
         if (nrounds > 1) issue_round_f8(ring, 1);
