@@ -248,7 +248,10 @@ mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups
  * a GPU).  It writes the partial O as bf16 [num_partials][128][d_latent] in
  * the first half of the same area (the LSE where it always is), and
  * mla_combine, seeing the same setting, merges that layout: both calls of a
- * step must see the same value.
+ * step must see the same value.  MLA_DECODE_KERNEL=qres selects, for e4m3
+ * caches, the library's e4m3 kernels rebuilt with the query fragments
+ * resident before the key loop (same partials, same merge; not yet run on a
+ * GPU either).
  *
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, BAD_PLAN,
  * WORKSPACE_TOO_SMALL, HIP (launch failure).

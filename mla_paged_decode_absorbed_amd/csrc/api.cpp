@@ -47,6 +47,14 @@ bool candidate_selected(const mla_plan_info* info) {
   return variant && std::strcmp(variant, "w8") == 0 && info->phases == 1;
 }
 
+// MLA_DECODE_KERNEL=qres selects, for e4m3 caches, the library's e4m3
+// kernels rebuilt with the query fragments resident before the key loop
+// (same plans, same fp32 partials and merge).
+bool qres_selected(const mla_shape* shape) {
+  const char* variant = std::getenv("MLA_DECODE_KERNEL");
+  return variant && std::strcmp(variant, "qres") == 0 && shape->kv_dtype == MLA_KV_FP8_E4M3;
+}
+
 mla_status host_plan(const mla_shape* shape, const int32_t* kv_lens_host,
                      const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
                      uint64_t plan_bytes, mla_plan_info* info, bool fixed_shape) {
@@ -198,6 +206,8 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (candidate_selected(info))
     return launch_decode_w8(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  if (qres_selected(shape))
+    return launch_decode_qres(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   return launch_decode(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

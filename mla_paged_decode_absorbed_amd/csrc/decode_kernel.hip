@@ -321,6 +321,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(
         qA[c] = *reinterpret_cast<const bf16x8*>(pa + c * 64);
         qB[c] = *reinterpret_cast<const bf16x8*>(pb + c * 64);
       }
+#ifdef MLA_DECODE_Q_RESIDENT
+      // Q resident before any copy is issued: otherwise the compiler, which
+      // does not see the copies, waits for the Q loads inside the key loop
+      // with vmcnt literals that at run time also count the rounds issued
+      // ahead (decode_kernel_qres.hip)
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        require_vgpr(qA[c]);
+        require_vgpr(qB[c]);
+      }
+#endif
     }
 
     DmaCtx<KVD> dc;
@@ -958,8 +969,14 @@ hipError_t launch_kvd(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+#ifdef MLA_DECODE_Q_RESIDENT
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  return kv_dtype == 1 ? launch_kvd<1>(a, stream) : hipErrorInvalidValue;
+}
+#else
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   return kv_dtype == 0 ? launch_kvd<0>(a, stream) : launch_kvd<1>(a, stream);
 }
+#endif
 
 }  // namespace mla

@@ -40,6 +40,10 @@ struct CombineArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
+// The library's e4m3 decode kernels with the query fragments forced resident
+// before the key loop (decode_kernel_qres.hip); chosen only when
+// MLA_DECODE_KERNEL=qres, e4m3 caches only.
+hipError_t launch_decode_qres(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 // Candidate decode kernel with two waves per SIMD (one-phase plans, bf16 or
 // e4m3 cache); chosen only when MLA_DECODE_KERNEL=w8.
 hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream);

@@ -111,5 +111,9 @@ def test_candidate_kernel_naming(monkeypatch):
     # plans the candidate does not cover (several phases) keep the library kernels
     assert bench.decode_kernel_name("bf16", 4) == "mla_decode_kernel"
     assert bench.decode_kernel_symbol("fp8_e4m3", 2) == "mla_decode_kernel<1, 2>"
+    monkeypatch.setenv("MLA_DECODE_KERNEL", "qres")
+    assert bench.decode_kernel_name("fp8_e4m3", 1) == "mla_decode_kernel_qres"
+    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel_qres<1, 1>"
+    assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"
     monkeypatch.delenv("MLA_DECODE_KERNEL")
     assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"

@@ -534,3 +534,28 @@ def test_w8_random_shapes():
         jobs.append((case, nwg, 1, dict(env_extra={**MODES[mode], **W8})))
     for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs, workers=8)):
         _check(c, out, lse)
+
+
+# ---------------------------------------------------------------- Q-resident e4m3 rebuild
+# decode_kernel_qres.hip (MLA_DECODE_KERNEL=qres): the library's e4m3 kernels
+# with the query fragments forced resident before any copy.  The change only
+# moves the compiler's waits, which the emulator does not model, so these
+# runs check that the rebuilt kernels (renamed, compiled a second time from
+# the same source) compute what the library's do, for every phase count.
+QRES = {"MLA_DECODE_KERNEL": "qres"}
+
+
+def test_qres_kernels_match_oracle():
+    specs = [([900, 70], [1, 2], 16, 4), ([700, 130, 5], [2, 2, 1], 8, 2),
+             ([64, 64, 130, 18], [1, 1, 1, 1], 1, 1), ([1500, 700, 65, 900], [1, 2, 1, 2], 12, 1)]
+    jobs = []
+    for kv, ql, nwg, ph in specs:
+        case = make_case(kv_lens=kv, q_lens=ql, seed=29, kv_dtype="fp8_e4m3",
+                         sm_scale=1 / math.sqrt(192), max_q_len=2)
+        for mode in ("wait-lockstep", "issue-drift"):
+            jobs.append((case, nwg, ph, dict(env_extra={**MODES[mode], **QRES})))
+    jobs.append((_rising_scores_case("fp8_e4m3"), 1, 1,
+                 dict(env_extra={**MODES["wait-lockstep"], **QRES})))
+    for (c, _n, ph, _kw), (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
+        assert meta["phases"] == ph
+        _check(c, out, lse)

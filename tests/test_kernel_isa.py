@@ -34,13 +34,16 @@ SOURCES = {
     "library": os.path.join(CSRC, "decode_kernel.hip"),
     # the two-waves-per-SIMD candidate (opt-in, MLA_DECODE_KERNEL=w8)
     "w8": os.path.join(CSRC, "decode_w8_kernel.hip"),
+    # the library's e4m3 kernels with Q resident (opt-in, MLA_DECODE_KERNEL=qres)
+    "qres": os.path.join(CSRC, "decode_kernel_qres.hip"),
 }
 # kernels per source, and copies per wave and round (a branch-free run);
 # None: the kernel waits for its copies with vmcnt(0) only, so no count of
 # copies per round enters a wait
-EXPECTED_KERNELS = {"library": 6, "w8": 2}
+EXPECTED_KERNELS = {"library": 6, "w8": 2, "qres": 3}
 COPIES_PER_ROUND = {"library": {"bf16": (18, 0), "e4m3": (9, 1)},
-                    "w8": {"bf16": (9, 0), "e4m3": None}}
+                    "w8": {"bf16": (9, 0), "e4m3": None},
+                    "qres": {"e4m3": (9, 1)}}
 
 
 @pytest.fixture(scope="module", params=sorted(SOURCES))
@@ -603,7 +606,10 @@ def test_two_waves_per_simd_register_budget(isa):
 # them inside it (vmcnt 35 down to 9 across the QK step): at run time these
 # literals also count the copies of the rounds issued ahead, so the step
 # waits for most of them.  Fixing it changes their validated machine code.
-KNOWN_LOOP_VMCNT = {"mla_decode_kernelILi1E"}
+# The four-phase e4m3 kernel (opt-in MLA_PHASES=4, never chosen by the
+# planner) reloads spilled registers inside its key loop, and the compiler
+# waits for those reloads there; its Q-resident rebuild keeps that.
+KNOWN_LOOP_VMCNT = {"mla_decode_kernelILi1E", "mla_decode_kernel_qresILi1ELi4E"}
 
 
 def test_no_compiler_vmcnt_wait_in_key_loop(isa):
