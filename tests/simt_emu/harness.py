@@ -28,7 +28,7 @@ def _stale() -> bool:
     t = os.path.getmtime(BIN)
     srcs = [os.path.join(_b.CSRC, f) for f in _b.KERNEL_FILES]
     srcs += [os.path.join(HERE, f) for f in ("gfx950_asm.h", "emu_runtime.cpp", "run_case.cpp",
-                                              os.path.join("hip", "hip_runtime.h"))]
+                                              os.path.join("hip", "hip_runtime.h"), "build.py")]
     return any(os.path.getmtime(s) > t for s in srcs)
 
 
