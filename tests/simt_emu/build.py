@@ -76,8 +76,9 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
         with open(path, "w") as fh:
             fh.write(text)
     shutil.copyfile(os.path.join(HERE, "gfx950_asm.h"), os.path.join(src, "gfx950_asm.h"))
-    # -O2 (EMU_OPT overrides): AddressSanitizer instruments every access at
-    # any level, and the emulation runs about 1.5 times faster than at -O1
+    # -O2 (EMU_OPT overrides): AddressSanitizer checks every memory access the
+    # optimised code still makes (the planted out-of-bounds cases fail as at
+    # -O1), and the emulation runs about 1.5 times faster
     flags = ["-std=c++20", os.environ.get("EMU_OPT", "-O2"), "-g", "-pthread", "-fno-omit-frame-pointer",
              f"-I{HERE}", f"-I{src}", f"-I{INCLUDE}", "-Wno-unused-command-line-argument", "-Wno-psabi"]
     if sanitize:
