@@ -52,7 +52,7 @@ def _check(case, out_bits, lse):
         num += float((d ** 2).sum())
         den += float((O[b, :qb] ** 2).sum())
         assert float(np.abs(lse[b, :qb] - L[b, :qb]).max()) <= 1e-3
-        # padded query rows keep the sentinel the driver wrote
+        # padded query rows keep the sentinel run_case wrote before the launch
         if qb < case.max_q_len:
             assert np.all(out_bits[b, qb:] == 0xC1C1)
             assert np.all(lse[b, qb:] == 12345.0)
