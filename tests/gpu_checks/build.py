@@ -1,7 +1,7 @@
 """Build the GPU check libraries of tests/gpu_checks in-tree (gfx950).
 
-Test infrastructure only: each library holds one checking kernel that a
-``-m gpu`` test loads with ctypes.
+Test infrastructure only: each library holds one checking or measuring
+kernel that a ``-m gpu`` test loads with ctypes.
 """
 from __future__ import annotations
 
@@ -9,7 +9,8 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-CHECKS = {"e4m3_convert_check.hip": "libe4m3_convert_check.so"}
+CHECKS = {"e4m3_convert_check.hip": "libe4m3_convert_check.so",
+          "lds_read_probe.hip": "liblds_read_probe.so"}
 
 
 def build(verbose: bool = False) -> list[str]:
