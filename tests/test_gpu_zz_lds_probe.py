@@ -4,13 +4,20 @@ transposed value fragments) with four and with eight waves per workgroup, one
 workgroup per CU (tests/gpu_checks/lds_read_probe.hip).  A measurement, not a
 parity test: it prints bytes per clock per CU (at the 2.4 GHz peak engine
 clock) and checks only that the figures are plausible.  The figure bounds how
-busy a decode kernel with two waves per SIMD can keep its matrix units."""
+busy a decode kernel with two waves per SIMD can keep its matrix units.
+Skipped, like the candidate kernels' tests, until its first GPU run.  (Named
+to run after every validated suite.)"""
 import ctypes
 import os
 
 import pytest
 
-pytestmark = pytest.mark.gpu
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(os.environ.get("MLA_RUN_UNVALIDATED") != "1",
+                       reason="probe kernel not yet run on a GPU: set MLA_RUN_UNVALIDATED=1 "
+                              "for its first run"),
+]
 
 torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
