@@ -636,3 +636,22 @@ def test_known_loop_vmcnt_waits_are_still_there(isa):
                     a is None and re.match(r"s_waitcnt .*vmcnt", i) for i, a in ins):
                 found.add(name)
     assert found and all(any(k in n for k in KNOWN_LOOP_VMCNT) for n in found), sorted(found)
+
+
+@pytest.mark.parametrize("src", ["e4m3_convert_check.hip", "lds_read_probe.hip"])
+def test_gpu_check_kernels_machine_code(tmp_path, src):
+    # the GPU check and measurement kernels of tests/gpu_checks: no scratch,
+    # no scalar stores, LDS within the 160 KB a workgroup may use
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument",
+           os.path.join(ROOT, "tests", "gpu_checks", src), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    text = out.read_text()
+    ins = [l.split(";")[0].strip() for l in text.splitlines()]
+    assert not [i for i in ins if i.startswith("scratch_")]
+    assert not [i for i in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|scratch_store)", i)]
+    for lds in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", text):
+        assert int(lds) <= 160 * 1024
