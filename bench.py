@@ -49,6 +49,7 @@ PAIRS_KERNEL = "mla_decode_kernel_pairs"
 
 W8_KERNEL = "mla_decode_kernel_w8"
 QRES_KERNEL = "mla_decode_kernel_qres"
+SPLIT_KERNEL = "mla_decode_kernel_split"
 
 
 def _w8_selected(kv_dtype: str, phases: int) -> bool:
@@ -59,11 +60,17 @@ def _qres_selected(kv_dtype: str) -> bool:
     return os.environ.get("MLA_DECODE_KERNEL") == "qres" and kv_dtype != "bf16"
 
 
+def _split_selected(kv_dtype: str, phases: int) -> bool:
+    return os.environ.get("MLA_DECODE_KERNEL") == "split" and kv_dtype == "bf16" and phases == 1
+
+
 def decode_kernel_name(kv_dtype: str, phases: int) -> str:
     if _w8_selected(kv_dtype, phases):
         return W8_KERNEL
     if _qres_selected(kv_dtype):
         return QRES_KERNEL
+    if _split_selected(kv_dtype, phases):
+        return SPLIT_KERNEL
     return PAIRS_KERNEL if kv_dtype == "bf16" and phases == 1 else DECODE_KERNEL
 
 
@@ -133,6 +140,8 @@ def decode_kernel_symbol(kv_dtype: str, phases: int) -> str:
         return f"mla_decode_kernel_w8<{0 if kv_dtype == 'bf16' else 1}>"
     if _qres_selected(kv_dtype):
         return f"mla_decode_kernel_qres<1, {phases}>"
+    if _split_selected(kv_dtype, phases):
+        return SPLIT_KERNEL
     if kv_dtype == "bf16" and phases == 1:
         return "mla_decode_kernel_pairs<0>"
     return f"mla_decode_kernel<{0 if kv_dtype == 'bf16' else 1}, {phases}>"
@@ -519,10 +528,12 @@ def main() -> int:
     ap.add_argument("--num-workgroups", type=int, default=0,
                     help="plan the decode for this many workgroups instead of one per CU "
                          "(per-CU throughput against the number of CUs at work)")
-    ap.add_argument("--decode-kernel", choices=("default", "w8", "qres"), default="default",
+    ap.add_argument("--decode-kernel", choices=("default", "w8", "qres", "split"),
+                    default="default",
                     help="w8: time the two-waves-per-SIMD candidate (one-phase plans, bf16 or "
                          "e4m3 cache); qres: the library's e4m3 kernels with Q resident before "
-                         "the key loop (e4m3 caches); neither has run on a GPU yet")
+                         "the key loop (e4m3 caches); split: the candidate whose pairs of waves "
+                         "share 32 rows (one-phase plans, bf16 cache); none has run on a GPU yet")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")
@@ -734,8 +745,8 @@ def main() -> int:
             "TFLOP/s", "mfma"
     kernel_name = decode_kernel_name(case.kv_dtype, pl.phases)
     kernel_sym = decode_kernel_symbol(case.kv_dtype, pl.phases)
-    kernel_src = {W8_KERNEL: "decode_w8_kernel.hip",
-                  QRES_KERNEL: "decode_kernel_qres.hip"}.get(kernel_name, "decode_kernel.hip")
+    kernel_src = {W8_KERNEL: "decode_w8_kernel.hip", QRES_KERNEL: "decode_kernel_qres.hip",
+                  SPLIT_KERNEL: "decode_split_kernel.hip"}.get(kernel_name, "decode_kernel.hip")
     traffic = read_traffic(args.workload, kernel_name, (kernel_src,), symbol=kernel_sym)
 
     res = {

@@ -32,7 +32,7 @@ LLVM_BIN = "/opt/rocm/llvm/bin"
 SOURCES = ["api.cpp", "plan.cpp", "decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
            "plan_kernel.hip", "tree_kernel.hip", "prefill_quant_kernel.hip",
            "prefill_attn_kernel.hip", "check_kernel.hip", "decode_w8_kernel.hip",
-           "decode_kernel_qres.hip"]
+           "decode_kernel_qres.hip", "decode_split_kernel.hip"]
 ARCH = "gfx950"
 
 

@@ -71,6 +71,26 @@ __device__ __forceinline__ int opaque_s(int x) {
   return x;
 }
 
+// Store `value` to the LDS word at p once this wave's earlier LDS operations
+// have completed, so that a wave that sees the value also sees those writes.
+__device__ __forceinline__ void lds_publish(LDS_PTR(int) p, int value) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  *(volatile LDS_PTR(int))p = value;
+}
+
+// Wait until the LDS word at p, which another wave of the workgroup raises
+// with lds_publish, holds at least `target`; later LDS reads stay after the
+// wait.  The polls are bounded (about 2^20 of them, tens of milliseconds), so
+// that a kernel whose invariant broke returns with wrong results instead of
+// holding the GPU.
+__device__ __forceinline__ void lds_wait_at_least(const LDS_PTR(int) p, int target) {
+  for (int n = 0; n < (1 << 20); ++n) {
+    if (__builtin_amdgcn_readfirstlane(*(const volatile LDS_PTR(int))p) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 // Require v to be resident in VGPRs here (the compiler then places its wait
 // for the load that produced v at this point).
 template <typename T>

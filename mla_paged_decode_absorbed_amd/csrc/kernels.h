@@ -47,8 +47,12 @@ hipError_t launch_decode_qres(const DecodeArgs& a, int kv_dtype, hipStream_t str
 // Candidate decode kernel with two waves per SIMD (one-phase plans, bf16 or
 // e4m3 cache); chosen only when MLA_DECODE_KERNEL=w8.
 hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
+// Candidate decode kernel with two waves per SIMD sharing each 32-row group
+// (decode_split_kernel.hip; one-phase plans, bf16 cache); chosen only when
+// MLA_DECODE_KERNEL=split.
+hipError_t launch_decode_split(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
-// The merge over bf16 partials, as the candidate decode kernel writes them.
+// The merge over bf16 partials, as the candidate decode kernels write them.
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -23,14 +23,15 @@ KERNEL_FILES = ["decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip",
                 "plan_kernel.hip", "tree_kernel.hip", "api.cpp", "plan.cpp", "kernels.h",
                 "append.h", "plan_core.h", "plan_device.h", "tree.h", "plan_layout.h",
                 "validate.h", "prefill.h", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip",
-                "check.h", "check_kernel.hip", "decode_w8_kernel.hip", "decode_kernel_qres.hip"]
+                "check.h", "check_kernel.hip", "decode_w8_kernel.hip", "decode_kernel_qres.hip",
+                "decode_split_kernel.hip"]
 
 
 # compilation units of the library built into the emulator binary
 UNITS = ("decode_kernel.hip", "combine_kernel.hip", "append_kernel.hip", "plan_kernel.hip",
          "tree_kernel.hip", "prefill_quant_kernel.hip", "prefill_attn_kernel.hip",
-         "check_kernel.hip", "decode_w8_kernel.hip", "decode_kernel_qres.hip", "api.cpp",
-         "plan.cpp")
+         "check_kernel.hip", "decode_w8_kernel.hip", "decode_kernel_qres.hip",
+         "decode_split_kernel.hip", "api.cpp", "plan.cpp")
 
 
 def _includes(path: str, src: str, seen=None) -> set:

@@ -97,6 +97,8 @@ struct Fiber {
   Wave* wave = nullptr;
   Barrier* wait_bar = nullptr;
   unsigned wait_gen = 0;
+  const int* wait_flag = nullptr;   // blocked until *wait_flag >= wait_target
+  int wait_target = 0;
   bool done = false;
   std::deque<Pending> dma;
 };
@@ -208,6 +210,7 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           f.lane = t & 63;
           f.wave = S.waves[t >> 6].get();
           f.wait_bar = nullptr;
+          f.wait_flag = nullptr;
           f.done = false;
           f.dma.clear();
           // initial frame: six zeroed callee-saved registers, then the entry
@@ -224,7 +227,10 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           Fiber& f = fib[t];
           if (f.done) return false;
           if (f.wait_bar && f.wait_bar->gen == f.wait_gen) return false;
+          if (f.wait_flag && *static_cast<const volatile int*>(f.wait_flag) < f.wait_target)
+            return false;
           f.wait_bar = nullptr;
+          f.wait_flag = nullptr;
           threadIdx = EmuIdx{unsigned(t), 0u, 0u};
           blockIdx = EmuIdx{bx, by, bz};
           gridDim = EmuIdx{grid.x, grid.y, grid.z};
@@ -256,7 +262,9 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           } else {
             for (int t = 0; t < nt; ++t) progressed |= resume(t);
           }
-          if (!progressed) fail("deadlock: every live lane waits at a barrier no lane can complete");
+          if (!progressed)
+            fail("deadlock: every live lane waits at a barrier no lane can complete, or for an "
+                 "LDS word no lane raises");
         }
       }
   for (Fiber& f : fib) munmap(f.stack, kStackBytes + page);
@@ -307,6 +315,29 @@ void vm_wait(int n) {
 }
 
 void block_barrier() { wait_on(S.block_bar); }
+
+// Publishing an LDS word is a wave operation: every lane of the wave has
+// made its earlier LDS writes before any lane stores the word.
+void flag_publish(int* p, int value) {
+  const unsigned char* b = lds_base.load();
+  const unsigned char* c = reinterpret_cast<const unsigned char*>(p);
+  if (!b || c < b || c + sizeof(int) > b + kLdsLimit) fail("flag store outside the LDS");
+  wait_on(S.cur->wave->bar);
+  *static_cast<volatile int*>(p) = value;
+}
+
+// A lane waiting for an LDS word another wave publishes is not resumed until
+// the word reaches the target (so under EMU_SCHED=drift the other waves run
+// meanwhile), and a wait that nothing can end is reported as a deadlock.
+void flag_wait(const int* p, int target) {
+  const unsigned char* b = lds_base.load();
+  const unsigned char* c = reinterpret_cast<const unsigned char*>(p);
+  if (!b || c < b || c + sizeof(int) > b + kLdsLimit) fail("flag wait outside the LDS");
+  if (*static_cast<const volatile int*>(p) >= target) return;
+  S.cur->wait_flag = p;
+  S.cur->wait_target = target;
+  yield_to_scheduler(false);
+}
 
 uint32_t readfirstlane(uint32_t v) {
   return wave_op(v, [](int, auto get) { return get(0); });

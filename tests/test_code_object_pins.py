@@ -75,6 +75,7 @@ NOT_YET_RUN_ON_GPU = (
     "check_kernel.hip",       # mla_decode_check, opt-in debug mode
     "decode_w8_kernel.hip",   # two-waves-per-SIMD candidate, only under MLA_DECODE_KERNEL=w8
     "decode_kernel_qres.hip", # e4m3 kernels with Q resident, only under MLA_DECODE_KERNEL=qres
+    "decode_split_kernel.hip",  # pairs of waves sharing 32 rows, only under MLA_DECODE_KERNEL=split
 )
 # Kernels added since to a pinned source, beside its validated kernels; none
 # of them is on the default path either.

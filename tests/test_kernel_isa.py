@@ -36,11 +36,13 @@ SOURCES = {
     "w8": os.path.join(CSRC, "decode_w8_kernel.hip"),
     # the library's e4m3 kernels with Q resident (opt-in, MLA_DECODE_KERNEL=qres)
     "qres": os.path.join(CSRC, "decode_kernel_qres.hip"),
+    # pairs of waves sharing 32 rows (opt-in, MLA_DECODE_KERNEL=split)
+    "split": os.path.join(CSRC, "decode_split_kernel.hip"),
 }
 # kernels per source, and copies per wave and round (a branch-free run);
 # None: the kernel waits for its copies with vmcnt(0) only, so no count of
 # copies per round enters a wait
-EXPECTED_KERNELS = {"library": 6, "w8": 2, "qres": 3}
+EXPECTED_KERNELS = {"library": 6, "w8": 2, "qres": 3, "split": 1}
 COPIES_PER_ROUND = {"library": {"bf16": (18, 0), "e4m3": (9, 1)},
                     "w8": {"bf16": (9, 0), "e4m3": None},
                     "qres": {"e4m3": (9, 1)}}
@@ -539,6 +541,8 @@ def test_literal_vmcnt_waits_count_whole_rounds(isa):
     lane for the keys, 1 of 4 bytes for the scales) and vector-memory
     operations complete in issue order: any other vector-memory operation only
     adds to the count."""
+    if isa[0] == "split":
+        pytest.skip("its copy runs are checked below")
     for name, blocks in _kernels_asm(isa[1]).items():
         e4m3 = "ILi1E" in name
         literals = {int(m.group(1)) for _, ins in blocks for i, a in ins if a is not None
@@ -598,6 +602,69 @@ def test_two_waves_per_simd_register_budget(isa):
                                                                     4 * widen[0]), widen
         else:
             assert widen == (0, 0, 0), widen
+
+
+def test_split_copy_runs_and_waits(isa):
+    """The split candidate waits for a round with vmcnt(4) while the next
+    round is in flight (else vmcnt(0)), which is sound when every wave issues
+    at least four copies per round after the awaited ones: each round is one
+    branch-free run of four copies, followed (for waves 0..3) by a fifth in
+    a block of its own, and no other vector-memory operation."""
+    which, text = isa
+    if which != "split":
+        pytest.skip("the split candidate")
+    for name, blocks in _kernels_asm(text).items():
+        literals = {int(m.group(1)) for _, ins in blocks for i, a in ins if a is not None
+                    for m in [re.match(r"s_waitcnt vmcnt\((\d+)\)$", i)] if m}
+        assert literals == {0, 4}, literals
+        shapes = []
+        for lab, ins in blocks:
+            idx = [j for j, (i, _a) in enumerate(ins) if i.startswith("global_load_lds")]
+            if not idx:
+                continue
+            run = [i for i, _a in ins[idx[0]: idx[-1] + 1]]
+            assert all(i.startswith("global_load_lds_dwordx4") for i in run
+                       if i.startswith("global_load_lds")), (lab, run)
+            assert not [i for i in run if i.startswith(("s_branch", "global_load_d",
+                                                         "global_store", "buffer_", "scratch_",
+                                                         "flat_"))], lab
+            # C: a copy, B: a conditional branch (the one around the fifth copy)
+            shapes.append("".join("C" if i.startswith("global_load_lds") else "B" for i in run
+                                  if i.startswith(("global_load_lds", "s_cbranch"))))
+        # rounds 0 and 1 in the prologue, round j + 2 in the loop: three
+        # issue sites, each a run of four copies, then the branch around the
+        # fifth
+        assert sorted(shapes) == ["CCCCBC"] * 3, shapes
+
+
+def test_split_register_budget_and_loop_work(isa):
+    """The split candidate runs eight waves per CU, two per SIMD: each wave
+    fits 256 registers with nothing spilled, and per 32 keys its key loop
+    issues 18 QK and 16 PV steps of v_mfma_f32_32x32x16_bf16 (half the
+    dimensions, half the columns), 18 K-fragment reads and 32 transposing V
+    reads, and exchanges its partial scores (four 16-byte writes, four reads),
+    waiting for its partner's round counter with s_sleep between polls."""
+    which, text = isa
+    if which != "split":
+        pytest.skip("the split candidate")
+    vs = [int(x) for x in re.findall(r"\.vgpr_count:\s+(\d+)", text)]
+    as_ = [int(x) for x in re.findall(r"\.agpr_count:\s+(\d+)", text)]
+    assert len(vs) == len(as_) == 1 and vs[0] + as_[0] <= 256, (vs, as_)
+    assert set(re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)) == {"0"}
+    assert set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)) == {"0"}
+    lds = [int(x) for x in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", text)]
+    assert lds == [3 * 2 * 16 * 1152 + 8 * 4096 + 32], lds
+    for name, blocks in _kernels(text).items():
+        loop = [(lab, ins) for lab, ins in blocks if any("v_mfma" in i for i in ins)]
+
+        def count(prefix, where=loop):
+            return sum(sum(i.startswith(prefix) for i in ins) for _, ins in where)
+        # (the kernel's only MFMAs, 16-byte LDS reads and writes are these)
+        assert count("v_mfma_f32_32x32x16_bf16") == count("v_mfma", blocks) == 34
+        assert count("ds_read_b64_tr_b16") == count("ds_read_b64_tr_b16", blocks) == 32
+        assert count("ds_read_b128", blocks) == 18 + 4
+        assert count("ds_write_b128", blocks) == 4
+        assert count("s_sleep", blocks) >= 1
 
 
 # The library's e4m3 16-key kernels load Q before the key loop without
