@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_split(
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ q_lens,
     uint8_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
-  constexpr int KW = 3;   // K fragments in flight in the QK step
-  constexpr int VW = 3;   // V fragments in flight in the PV step
+  constexpr int KW = 4;   // K fragments in flight in the QK step
+  constexpr int VW = 4;   // V fragments in flight in the PV step
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const uint32_t smem_base = lds_address(smem);
 
