@@ -61,7 +61,7 @@ def _qres_selected(kv_dtype: str) -> bool:
 
 
 def _split_selected(kv_dtype: str, phases: int) -> bool:
-    return os.environ.get("MLA_DECODE_KERNEL") == "split" and kv_dtype == "bf16" and phases == 1
+    return os.environ.get("MLA_DECODE_KERNEL") == "split" and phases == 1
 
 
 def decode_kernel_name(kv_dtype: str, phases: int) -> str:
@@ -141,7 +141,7 @@ def decode_kernel_symbol(kv_dtype: str, phases: int) -> str:
     if _qres_selected(kv_dtype):
         return f"mla_decode_kernel_qres<1, {phases}>"
     if _split_selected(kv_dtype, phases):
-        return SPLIT_KERNEL
+        return f"mla_decode_kernel_split<{0 if kv_dtype == 'bf16' else 1}>"
     if kv_dtype == "bf16" and phases == 1:
         return "mla_decode_kernel_pairs<0>"
     return f"mla_decode_kernel<{0 if kv_dtype == 'bf16' else 1}, {phases}>"
@@ -533,7 +533,8 @@ def main() -> int:
                     help="w8: time the two-waves-per-SIMD candidate (one-phase plans, bf16 or "
                          "e4m3 cache); qres: the library's e4m3 kernels with Q resident before "
                          "the key loop (e4m3 caches); split: the candidate whose pairs of waves "
-                         "share 32 rows (one-phase plans, bf16 cache); none has run on a GPU yet")
+                         "share 32 rows (one-phase plans, bf16 or e4m3 cache); none has run on a "
+                         "GPU yet")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")

@@ -249,10 +249,10 @@ mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups
  * the first half of the same area (the LSE where it always is), and
  * mla_combine, seeing the same setting, merges that layout: both calls of a
  * step must see the same value.  MLA_DECODE_KERNEL=split selects, for
- * one-phase plans over bf16 caches, a second two-waves-per-SIMD candidate in
- * which each pair of waves shares 32 query rows (half the dimensions and
- * half the output columns each); it writes and merges the same bf16
- * partials, and is not yet run on a GPU either.  MLA_DECODE_KERNEL=qres
+ * one-phase plans, a second two-waves-per-SIMD candidate (bf16 or e4m3
+ * cache) in which each pair of waves shares 32 query rows (half the
+ * dimensions and half the output columns each); it writes and merges the
+ * same bf16 partials, and is not yet run on a GPU either.  MLA_DECODE_KERNEL=qres
  * selects, for e4m3 caches, the library's e4m3 kernels rebuilt with the
  * query fragments resident before the key loop (same partials, same merge;
  * not yet run on a GPU either).
@@ -273,9 +273,8 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info,
  * 2, exact up to rounding): for each combine entry of the plan,
  *   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) * O_s  -> bf16,
  * reading the workspace partials laid out as described for mla_decode_fwd
- * (bf16 O under MLA_DECODE_KERNEL=w8 for one-phase plans, and under
- * MLA_DECODE_KERNEL=split for one-phase plans over bf16 caches; fp32
- * otherwise).
+ * (bf16 O under MLA_DECODE_KERNEL=w8 or MLA_DECODE_KERNEL=split for
+ * one-phase plans, fp32 otherwise).
  * A row whose partials are all empty (LSE_s = -inf) gets O = 0, LSE = -inf.
  * No-op when info->num_combine == 0.  Must run after mla_decode_fwd on the
  * same stream (or after the caller filled the partials itself).

@@ -48,13 +48,12 @@ bool candidate_selected(const mla_plan_info* info) {
 }
 
 // MLA_DECODE_KERNEL=split selects the candidate whose pairs of waves share
-// each 32-row group (one phase, bf16 caches), and with it the merge of the
-// bf16 partials it writes; e4m3 caches and other plans run the library's
+// each 32-row group (one-phase plans, either cache type), and with it the
+// merge of the bf16 partials it writes; other plans run the library's
 // kernels.
-bool split_selected(const mla_shape* shape, const mla_plan_info* info) {
+bool split_selected(const mla_plan_info* info) {
   const char* variant = std::getenv("MLA_DECODE_KERNEL");
-  return variant && std::strcmp(variant, "split") == 0 && info->phases == 1 &&
-         shape->kv_dtype == MLA_KV_BF16;
+  return variant && std::strcmp(variant, "split") == 0 && info->phases == 1;
 }
 
 // MLA_DECODE_KERNEL=qres selects, for e4m3 caches, the library's e4m3
@@ -216,7 +215,7 @@ mla_status mla_decode_fwd(const mla_shape* shape, const mla_plan_info* info, con
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (candidate_selected(info))
     return launch_decode_w8(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-  if (split_selected(shape, info))
+  if (split_selected(info))
     return launch_decode_split(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   if (qres_selected(shape))
     return launch_decode_qres(a, shape->kv_dtype, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -286,7 +285,7 @@ mla_status mla_combine(const mla_shape* shape, const mla_plan_info* info, const 
   a.max_q_len = shape->max_q_len;
   a.num_combine = info->num_combine;
   const hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
-  const bool bf16_partials = candidate_selected(info) || split_selected(shape, info);
+  const bool bf16_partials = candidate_selected(info) || split_selected(info);
   const hipError_t e = bf16_partials ? launch_combine_bf16(a, cs) : launch_combine(a, cs);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -48,7 +48,7 @@ hipError_t launch_decode_qres(const DecodeArgs& a, int kv_dtype, hipStream_t str
 // e4m3 cache); chosen only when MLA_DECODE_KERNEL=w8.
 hipError_t launch_decode_w8(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 // Candidate decode kernel with two waves per SIMD sharing each 32-row group
-// (decode_split_kernel.hip; one-phase plans, bf16 cache); chosen only when
+// (decode_split_kernel.hip; one-phase plans, bf16 or e4m3 cache); chosen only when
 // MLA_DECODE_KERNEL=split.
 hipError_t launch_decode_split(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -117,9 +117,10 @@ def test_candidate_kernel_naming(monkeypatch):
     assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"
     monkeypatch.setenv("MLA_DECODE_KERNEL", "split")
     assert bench.decode_kernel_name("bf16", 1) == "mla_decode_kernel_split"
-    assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_split"
-    # e4m3 caches and several phases keep the library kernels
-    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel<1, 1>"
+    assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_split<0>"
+    assert bench.decode_kernel_name("fp8_e4m3", 1) == "mla_decode_kernel_split"
+    assert bench.decode_kernel_symbol("fp8_e4m3", 1) == "mla_decode_kernel_split<1>"
+    # several phases keep the library kernels
     assert bench.decode_kernel_symbol("bf16", 2) == "mla_decode_kernel<0, 2>"
     monkeypatch.delenv("MLA_DECODE_KERNEL")
     assert bench.decode_kernel_symbol("bf16", 1) == "mla_decode_kernel_pairs<0>"

@@ -48,6 +48,7 @@ DECODE_MODES = [
     (("--workload", "long_ctx_fp8", "--decode-kernel", "w8"), "mla_decode_kernel_w8"),
     (("--workload", "long_ctx_fp8", "--decode-kernel", "qres"), "mla_decode_kernel_qres"),
     (("--decode-kernel", "split"), "mla_decode_kernel_split"),
+    (("--workload", "long_ctx_fp8", "--decode-kernel", "split"), "mla_decode_kernel_split"),
     (("--workload", "mtp_verify_bf16", "--num-workgroups", "128"), "mla_decode_kernel_pairs"),
     (("--workload", "tree_verify_bf16",), None),
 ]

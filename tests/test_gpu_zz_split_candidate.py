@@ -1,7 +1,7 @@
 """GPU parity of the candidate decode kernel whose pairs of waves share 32
 rows (decode_split_kernel.hip, selected by MLA_DECODE_KERNEL=split for
-one-phase plans over bf16 caches) against the float64 oracle, at the decode
-bars.
+one-phase plans, bf16 or e4m3 cache) against the float64 oracle, at the
+decode bars.
 
 The candidate has passed the CPU emulator (both copy-landing modes, the
 lockstep and drift schedules, planted synchronisation mistakes;
@@ -58,9 +58,25 @@ def test_split_peaky_softmax():
     check(case, out, lse)
 
 
-@pytest.mark.parametrize("name", ["v3_decode_bf16", "mtp_verify_bf16", "ragged_serving_bf16"])
+@pytest.mark.parametrize("kv_lens,q_lens,nwg,P", [
+    ([1, 15, 16, 17, 31, 33, 63, 65, 129], [1, 1, 2, 1, 2, 1, 2, 1, 2], 12, 64),
+    ([3000, 700, 65, 1800], [1, 2, 1, 2], 1, 64),
+    ([3000, 700, 65, 1800], [1, 2, 1, 2], 256, 256),
+    ([0, 200, 64], [0, 2, 1], 5, 64),
+])
+def test_split_e4m3_small_cases(kv_lens, q_lens, nwg, P):
+    case = make_case(kv_lens=kv_lens, q_lens=q_lens, seed=39, max_q_len=2, page_size=P,
+                     kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192))
+    print(f"split e4m3: lengths {kv_lens} q {q_lens} workgroups {nwg} pages {P}", flush=True)
+    (out, lse), pl = run_gpu(case, num_workgroups=nwg, phases=1)
+    assert pl.phases == 1
+    check(case, out, lse)
+
+
+@pytest.mark.parametrize("name", ["v3_decode_bf16", "mtp_verify_bf16", "long_ctx_fp8",
+                                  "ragged_serving_bf16"])
 def test_split_full_size_workloads(name):
-    # every sequence of the bf16 workloads at full size, in the launch
+    # every sequence of the four workloads at full size, in the launch
     # configuration bench.py times, one-phase plans
     case = workload(name)
     print(f"split: {name}", flush=True)

@@ -304,15 +304,15 @@ def test_emulated_restart_storm_with_rising_scores(kv_dtype):
 
 def test_emulated_full_length_sequences():
     # the library kernels and the two-waves-per-SIMD candidates (below) on the
-    # same sequences, all five runs at once
+    # same sequences, all six runs at once
     cases = [make_case(kv_lens=[L], q_lens=[q], num_heads=128, seed=51, kv_dtype=kvd,
                        sm_scale=1 / math.sqrt(192))
              for L, q, kvd in ((32768, 1, "fp8_e4m3"), (4096, 2, "bf16"))]
     jobs = [(c, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **extra}, timeout=1500))
             for extra in ({}, {"MLA_DECODE_KERNEL": "w8"}) for c in cases]
-    # and the split candidate (bf16 caches) on the bf16 sequence
-    jobs.append((cases[1], 16, 1, dict(env_extra={**MODES["wait-lockstep"], **SPLIT},
-                                       timeout=1500)))
+    # and the split candidate on both
+    jobs += [(c, 16, 1, dict(env_extra={**MODES["wait-lockstep"], **SPLIT}, timeout=1500))
+             for c in cases]
     for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
         assert meta["num_partials"] >= 8
         _check(c, out, lse)
@@ -566,21 +566,26 @@ def test_qres_kernels_match_oracle():
 
 
 # ---------------------------------------------------------------- pairs of waves sharing 32 rows
-# decode_split_kernel.hip (MLA_DECODE_KERNEL=split, one-phase plans, bf16
-# caches): waves w and w ^ 1 share 32 rows, each scoring half of the 576
+# decode_split_kernel.hip (MLA_DECODE_KERNEL=split, one-phase plans, bf16 or
+# e4m3 caches): waves w and w ^ 1 share 32 rows, each scoring half of the 576
 # dimensions and accumulating half of the 512 columns; the partial scores go
 # through LDS, guarded by a round counter per wave.  Every schedule matters
 # here: lockstep interleaves the waves, drift runs a wave alone up to its next
 # barrier (its partner has not scored the round yet when it reaches the
-# counter wait, so the wait must hold it).
+# counter wait, so the wait must hold it).  For e4m3 caches each 32-key round
+# is copied as it lies, widened once per CU into a pair buffer, then computed.
 
 
 def test_split_kernel_matches_oracle():
-    cases = [make_case(kv_lens=kv, q_lens=ql, seed=37, num_heads=H, page_size=P,
-                       sm_scale=1 / math.sqrt(192), max_q_len=max(2, max(ql)))
-             for kv, ql, _n, H, P in W8_CASES]
-    jobs = [(c, spec[2], 1, dict(env_extra={**MODES[mode], **SPLIT}))
-            for c, spec in zip(cases, W8_CASES) for mode in sorted(MODES)]
+    cases = [(make_case(kv_lens=kv, q_lens=ql, seed=37, num_heads=H, page_size=P,
+                        sm_scale=1 / math.sqrt(192), max_q_len=max(2, max(ql))), n)
+             for kv, ql, n, H, P in W8_CASES]
+    cases += [(make_case(kv_lens=kv, q_lens=ql, seed=39, num_heads=H, page_size=P,
+                         kv_dtype="fp8_e4m3", sm_scale=1 / math.sqrt(192),
+                         max_q_len=max(2, max(ql))), n)
+              for kv, ql, n, H, P in W8_F8_CASES]
+    jobs = [(c, n, 1, dict(env_extra={**MODES[mode], **SPLIT}))
+            for c, n in cases for mode in sorted(MODES)]
     for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs, workers=8)):
         assert meta["phases"] == 1
         _check(c, out, lse)
@@ -590,53 +595,57 @@ def test_split_kernel_rescales():
     # a late dominant key, and scores rising by 36 log2 units every 32 keys
     # (2048 keys: the library kernels would restart the item at every step):
     # both waves of a pair raise their rows' reference alike and rescale
-    # their own columns in place
+    # their own columns in place, for either cache type
+    overshoot = (_late_dominant_key_case(), _rising_scores_case("bf16"),
+                 _dominant_key_case_f8(), _rising_scores_case("fp8_e4m3"))
     jobs = [(c, 1, 1, dict(env_extra={**MODES[mode], **SPLIT}))
-            for c in (_late_dominant_key_case(), _rising_scores_case("bf16"))
-            for mode in sorted(MODES)]
-    jobs.append((_rising_scores_case("bf16", L=2048, q_value=16.0), 1, 1,
-                 dict(env_extra={**MODES["issue-drift"], **SPLIT})))
-    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
+            for c in overshoot for mode in sorted(MODES)]
+    jobs += [(_rising_scores_case(kvd, L=2048, q_value=16.0), 1, 1,
+              dict(env_extra={**MODES["issue-drift"], **SPLIT})) for kvd in ("bf16", "fp8_e4m3")]
+    for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs, workers=8)):
         _check(c, out, lse)
 
 
 def test_split_kernel_fixed_shape_plan_and_stale_plan():
-    fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
-                      sm_scale=1 / math.sqrt(192))
-    stale = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=47, max_q_len=2,
-                      sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
-    stale.block_table[stale.block_table < 0] = stale.num_pages
-    jobs = [(fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **SPLIT}))]
-    # a plan made for longer lengths: the clamp keeps every read inside the
-    # sequence (the padding entries name the page just past the pool)
-    jobs += [(stale, nwg, 1, dict(env_extra={**MODES["wait-drift"], **SPLIT},
-                                  plan_kv_lens=[1200, 900, 300])) for nwg in (3, 16)]
+    jobs = []
+    for kvd in ("bf16", "fp8_e4m3"):
+        fixed = make_case(kv_lens=[700, 130, 5], q_lens=[2, 2, 1], seed=43, max_q_len=2,
+                          kv_dtype=kvd, sm_scale=1 / math.sqrt(192))
+        stale = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=47, max_q_len=2,
+                          kv_dtype=kvd, sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
+        stale.block_table[stale.block_table < 0] = stale.num_pages
+        jobs.append((fixed, 8, 1, dict(fixed=True, env_extra={**MODES["issue-drift"], **SPLIT})))
+        # a plan made for longer lengths: the clamp keeps every read inside
+        # the sequence (the padding entries name the page just past the pool)
+        jobs += [(stale, nwg, 1, dict(env_extra={**MODES["wait-drift"], **SPLIT},
+                                      plan_kv_lens=[1200, 900, 300])) for nwg in (3, 16)]
     for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs)):
         _check(c, out, lse)
 
 
-def test_split_e4m3_cache_runs_the_library_kernels():
-    # the candidate takes bf16 caches only; an e4m3 cache under the switch
-    # runs (and merges) as without it
-    case = make_case(kv_lens=[700, 130], q_lens=[2, 2], seed=29, kv_dtype="fp8_e4m3",
-                     sm_scale=1 / math.sqrt(192), max_q_len=2)
-    out, lse, meta = harness.run(case, 8, 1, env_extra={**MODES["wait-lockstep"], **SPLIT})
-    assert meta["num_partials"] > 0
-    _check(case, out, lse)
-
-
+# (source text, replacement, schedule, cache type)
 SPLIT_PLANTS = {
     # the counter wait: a wave adds its partner's slot before the partner wrote it
-    "partner_wait": ("lds_wait_at_least(flag_par, seq);", "/* removed */", "wait-drift"),
+    "partner_wait": ("lds_wait_at_least(flag_par, seq);", "/* removed */", "wait-drift", "bf16"),
     # the per-round barrier: copies refill a slot other waves still read
     "barrier": ("barrier();   // round j from all waves; round j - 1 and its exchange done",
-                "/* removed */", "issue-drift"),
+                "/* removed */", "issue-drift", "bf16"),
     # the wait for a round's copies: a stage is read before it landed
     "copy_wait": ("if (j + 1 < nrounds) MLA_VM_WAIT(4);", "if (j + 1 < nrounds) MLA_VM_WAIT(8);",
-                  "wait-drift"),
+                  "wait-drift", "bf16"),
+    # e4m3: the per-round barrier (a round is widened before all its copies
+    # landed, or a pair buffer is refilled while another wave computes it)
+    "f8_barrier": ("barrier();   // round p widened and round p + 1 copied by all waves; "
+                   "round p - 1 done", "/* removed */", "issue-drift", "fp8_e4m3"),
+    # e4m3: the wait for the round about to be widened
+    "f8_copy_wait": ("if (p + 2 < nrounds) MLA_VM_WAIT(2);", "if (p + 2 < nrounds) MLA_VM_WAIT(5);",
+                     "wait-drift", "fp8_e4m3"),
+    # e4m3: the prologue's wait for round 0
+    "f8_first_wait": ("MLA_VM_WAIT(0);   // this wave's copies of round 0 (and its Q loads)",
+                      "/* removed */", "wait-lockstep", "fp8_e4m3"),
     # the key-range clamp: the stale plan reads pages past the sequence
     "clamp": ("const int k1 = min(item[3], L), k0 = min(item[2], k1);",
-              "const int k1 = item[3], k0 = item[2];", "issue-drift"),
+              "const int k1 = item[3], k0 = item[2];", "issue-drift", None),
 }
 
 
@@ -644,22 +653,23 @@ SPLIT_PLANTS = {
 def test_split_emulation_catches_planted_mistakes(plant):
     # each synchronisation step and the clamp taken out (on the CPU only)
     from tests.simt_emu import build as _b
-    old, new, mode = SPLIT_PLANTS[plant]
+    old, new, mode, kvd = SPLIT_PLANTS[plant]
     src = open(os.path.join(_b.CSRC, "decode_split_kernel.hip")).read()
     assert src.count(old) == 1
     binary = _b.build(tag="split_planted_" + plant,
                       patches={"decode_split_kernel.hip": [(old, new)]})
-    case = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=5, max_q_len=2,
-                     sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
-    case.block_table[case.block_table < 0] = case.num_pages
-    if plant == "clamp":
-        with pytest.raises(RuntimeError, match="AddressSanitizer"):
-            harness.run(case, 3, 1, binary=binary, env_extra={**MODES[mode], **SPLIT},
-                        plan_kv_lens=[1200, 900, 300])
-        return
-    out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={**MODES[mode], **SPLIT})
-    with pytest.raises(AssertionError):
-        _check(case, out, lse)
+    for kv_dtype in ((kvd,) if kvd else ("bf16", "fp8_e4m3")):
+        case = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=5, max_q_len=2,
+                         kv_dtype=kv_dtype, sm_scale=1 / math.sqrt(192), extra_pages_per_seq=8)
+        case.block_table[case.block_table < 0] = case.num_pages
+        if plant == "clamp":
+            with pytest.raises(RuntimeError, match="AddressSanitizer"):
+                harness.run(case, 3, 1, binary=binary, env_extra={**MODES[mode], **SPLIT},
+                            plan_kv_lens=[1200, 900, 300])
+            continue
+        out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={**MODES[mode], **SPLIT})
+        with pytest.raises(AssertionError):
+            _check(case, out, lse)
 
 
 def test_split_emulation_reports_a_counter_nobody_raises():
@@ -677,22 +687,24 @@ def test_split_emulation_reports_a_counter_nobody_raises():
 
 
 def test_split_random_shapes():
-    """Seeded random shapes through the split candidate (bf16 caches), in
+    """Seeded random shapes through the split candidate, both cache types, in
     every schedule: batch, heads, draft tokens (with idle and zero-length
     sequences), page size, lengths and workgroup count drawn at random."""
     rng = np.random.default_rng(79)
     jobs = []
     modes = sorted(MODES)
     for trial in range(30):
+        kvd = ("bf16", "fp8_e4m3")[trial % 2]
         B = int(rng.integers(1, 6))
         H = int(rng.choice([16, 32, 128]))
         qmax = int(rng.integers(1, 5))
-        P = int(rng.choice([16, 64, 256]))
+        P = int(rng.choice([64, 256] if kvd == "fp8_e4m3" else [16, 64, 256]))
         ql = rng.integers(0, qmax + 1, size=B)
         kvl = np.where(ql > 0, rng.integers(0, 700, size=B) + ql, rng.integers(0, 40, size=B))
         nwg = int(rng.integers(1, 20))
         case = make_case(kv_lens=kvl.tolist(), q_lens=ql.tolist(), num_heads=H, page_size=P,
-                         max_q_len=qmax, seed=200 + trial, sm_scale=1 / math.sqrt(192))
-        jobs.append((case, nwg, 1, dict(env_extra={**MODES[modes[trial % 3]], **SPLIT})))
+                         kv_dtype=kvd, max_q_len=qmax, seed=200 + trial,
+                         sm_scale=1 / math.sqrt(192))
+        jobs.append((case, nwg, 1, dict(env_extra={**MODES[modes[(trial // 2) % 3]], **SPLIT})))
     for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs, workers=8)):
         _check(c, out, lse)

@@ -42,7 +42,7 @@ SOURCES = {
 # kernels per source, and copies per wave and round (a branch-free run);
 # None: the kernel waits for its copies with vmcnt(0) only, so no count of
 # copies per round enters a wait
-EXPECTED_KERNELS = {"library": 6, "w8": 2, "qres": 3, "split": 1}
+EXPECTED_KERNELS = {"library": 6, "w8": 2, "qres": 3, "split": 2}
 COPIES_PER_ROUND = {"library": {"bf16": (18, 0), "e4m3": (9, 1)},
                     "w8": {"bf16": (9, 0), "e4m3": None},
                     "qres": {"e4m3": (9, 1)}}
@@ -605,66 +605,85 @@ def test_two_waves_per_simd_register_budget(isa):
 
 
 def test_split_copy_runs_and_waits(isa):
-    """The split candidate waits for a round with vmcnt(4) while the next
-    round is in flight (else vmcnt(0)), which is sound when every wave issues
-    at least four copies per round after the awaited ones: each round is one
-    branch-free run of four copies, followed (for waves 0..3) by a fifth in
-    a block of its own, and no other vector-memory operation."""
+    """The split candidate waits for a round with one vmcnt literal while the
+    next round is in flight (else vmcnt(0)): 4 for bf16, whose waves issue
+    four or five copies per round, 2 for e4m3, whose waves issue two or three
+    (and wave 7 the scales).  That is sound when every wave issues at least
+    that many copies per round after the awaited ones: each round is one
+    branch-free run of four (bf16) or two (e4m3) copies, followed by the
+    copies only some waves issue, each in a block of its own, and no other
+    vector-memory operation."""
     which, text = isa
     if which != "split":
         pytest.skip("the split candidate")
     for name, blocks in _kernels_asm(text).items():
+        e4m3 = "ILi1E" in name
         literals = {int(m.group(1)) for _, ins in blocks for i, a in ins if a is not None
                     for m in [re.match(r"s_waitcnt vmcnt\((\d+)\)$", i)] if m}
-        assert literals == {0, 4}, literals
+        assert literals == ({0, 2} if e4m3 else {0, 4}), (name, literals)
         shapes = []
         for lab, ins in blocks:
             idx = [j for j, (i, _a) in enumerate(ins) if i.startswith("global_load_lds")]
             if not idx:
                 continue
             run = [i for i, _a in ins[idx[0]: idx[-1] + 1]]
-            assert all(i.startswith("global_load_lds_dwordx4") for i in run
-                       if i.startswith("global_load_lds")), (lab, run)
             assert not [i for i in run if i.startswith(("s_branch", "global_load_d",
                                                          "global_store", "buffer_", "scratch_",
                                                          "flat_"))], lab
-            # C: a copy, B: a conditional branch (the one around the fifth copy)
-            shapes.append("".join("C" if i.startswith("global_load_lds") else "B" for i in run
-                                  if i.startswith(("global_load_lds", "s_cbranch"))))
-        # rounds 0 and 1 in the prologue, round j + 2 in the loop: three
-        # issue sites, each a run of four copies, then the branch around the
-        # fifth
-        assert sorted(shapes) == ["CCCCBC"] * 3, shapes
+            # C: a 16-byte copy, S: a 4-byte copy (the e4m3 scales), B: a
+            # conditional branch (around the copies only some waves issue)
+            shapes.append("".join(
+                ("C" if i.startswith("global_load_lds_dwordx4") else "S")
+                if i.startswith("global_load_lds") else "B"
+                for i in run if i.startswith(("global_load_lds", "s_cbranch"))))
+        # bf16: rounds 0 and 1 in the prologue and round j + 2 in the loop,
+        # each four copies, then the branch around the fifth; e4m3: rounds 0,
+        # 1, 2 in the prologue and p + 3 in the loop, each two copies, the
+        # branch around the third, and the scales' copy in a block of its own
+        want = ["CCBC"] * 4 + ["S"] * 4 if e4m3 else ["CCCCBC"] * 3
+        assert sorted(shapes) == sorted(want), (name, shapes)
 
 
 def test_split_register_budget_and_loop_work(isa):
     """The split candidate runs eight waves per CU, two per SIMD: each wave
-    fits 256 registers with nothing spilled, and per 32 keys its key loop
-    issues 18 QK and 16 PV steps of v_mfma_f32_32x32x16_bf16 (half the
-    dimensions, half the columns), 18 K-fragment reads and 32 transposing V
-    reads, and exchanges its partial scores (four 16-byte writes, four reads),
-    waiting for its partner's round counter with s_sleep between polls."""
+    fits 256 registers with nothing spilled, and per 32 keys issues 18 QK and
+    16 PV steps of v_mfma_f32_32x32x16_bf16 (half the dimensions, half the
+    columns), 18 K-fragment reads and 32 transposing V reads, and exchanges
+    its partial scores (four 16-byte writes, four reads), waiting for its
+    partner's round counter with s_sleep between polls.  For e4m3 it also
+    reads its keys' scales (four 16-byte reads) and widens rounds once per CU:
+    at most five 1 KB blocks per wave and round (one 8-byte read, four
+    conversions of two values, one 16-byte write each), in the prologue and
+    in the loop."""
     which, text = isa
     if which != "split":
         pytest.skip("the split candidate")
     vs = [int(x) for x in re.findall(r"\.vgpr_count:\s+(\d+)", text)]
     as_ = [int(x) for x in re.findall(r"\.agpr_count:\s+(\d+)", text)]
-    assert len(vs) == len(as_) == 1 and vs[0] + as_[0] <= 256, (vs, as_)
+    assert len(vs) == len(as_) == 2 and all(v + a <= 256 for v, a in zip(vs, as_)), (vs, as_)
     assert set(re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)) == {"0"}
     assert set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)) == {"0"}
-    lds = [int(x) for x in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", text)]
-    assert lds == [3 * 2 * 16 * 1152 + 8 * 4096 + 32], lds
+    lds = sorted(int(x) for x in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", text))
+    exch = 8 * 4096 + 32   # exchange slots and round counters
+    assert lds == sorted([3 * 36864 + exch,                            # bf16 ring
+                          2 * 36864 + 3 * 18432 + 3 * 256 + 256 + exch]), lds   # e4m3
     for name, blocks in _kernels(text).items():
+        e4m3 = "ILi1E" in name
         loop = [(lab, ins) for lab, ins in blocks if any("v_mfma" in i for i in ins)]
 
         def count(prefix, where=loop):
             return sum(sum(i.startswith(prefix) for i in ins) for _, ins in where)
-        # (the kernel's only MFMAs, 16-byte LDS reads and writes are these)
-        assert count("v_mfma_f32_32x32x16_bf16") == count("v_mfma", blocks) == 34
-        assert count("ds_read_b64_tr_b16") == count("ds_read_b64_tr_b16", blocks) == 32
-        assert count("ds_read_b128", blocks) == 18 + 4
-        assert count("ds_write_b128", blocks) == 4
-        assert count("s_sleep", blocks) >= 1
+        # (the kernel's only MFMAs and transposing reads are these)
+        assert count("v_mfma_f32_32x32x16_bf16") == count("v_mfma", blocks) == 34, name
+        assert count("ds_read_b64_tr_b16") == count("ds_read_b64_tr_b16", blocks) == 32, name
+        assert count("ds_read_b128", blocks) == 18 + 4 + (4 if e4m3 else 0), name
+        assert count("s_sleep", blocks) >= 1, name
+        widen = (count("ds_read_b64 ", blocks), count("ds_write_b128", blocks) - 4,
+                 count("v_cvt_pk_f32_fp8", blocks))
+        if e4m3:
+            assert widen == (10, 10, 40), widen
+        else:
+            assert widen == (0, 0, 0), widen
 
 
 # The library's e4m3 16-key kernels load Q before the key loop without

@@ -93,14 +93,17 @@ def test_tree_drafts_through_the_candidate_decode_kernel():
 
 def test_tree_drafts_through_the_split_decode_kernel():
     # the prefix decode on the candidate whose pairs of waves share 32 rows
-    # (MLA_DECODE_KERNEL=split, bf16 caches: its bf16 partials and their
-    # merge), then the draft merge, in both schedules
-    case = make_case(kv_lens=[300, 8, 70, 1000], q_lens=[4, 8, 3, 0], seed=56, num_heads=16,
-                     page_size=16, sm_scale=1 / math.sqrt(192), max_q_len=8)
-    mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=5)
-    jobs = [(case, 6, 1, dict(tree_mask=mask, env_extra={
-        "MLA_DECODE_KERNEL": "split", "EMU_DMA_LAND": land, "EMU_SCHED": sched}))
-        for land, sched in (("issue", "drift"), ("wait", "lockstep"))]
-    for _job, (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
+    # (MLA_DECODE_KERNEL=split: its bf16 partials and their merge), then the
+    # draft merge, for both cache types and in two schedules
+    jobs, masks = [], []
+    for dtype, P in (("bf16", 16), ("fp8_e4m3", 64)):
+        case = make_case(kv_lens=[300, 8, 70, 1000], q_lens=[4, 8, 3, 0], seed=56, kv_dtype=dtype,
+                         num_heads=16, page_size=P, sm_scale=1 / math.sqrt(192), max_q_len=8)
+        mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=5)
+        for land, sched in (("issue", "drift"), ("wait", "lockstep")):
+            jobs.append((case, 6, 1, dict(tree_mask=mask, env_extra={
+                "MLA_DECODE_KERNEL": "split", "EMU_DMA_LAND": land, "EMU_SCHED": sched})))
+            masks.append(mask)
+    for (case, *_), mask, (out, lse, meta) in zip(jobs, masks, harness.run_many(jobs)):
         assert meta["num_partials"] > 0
         check_tree(case, mask, out, lse)
