@@ -686,6 +686,38 @@ def test_split_register_budget_and_loop_work(isa):
             assert widen == (0, 0, 0), widen
 
 
+def test_split_exchange_order(isa):
+    """The exchange in program order: the four 16-byte writes of the partial
+    scores, the wait for them (lgkmcnt(0), the kernel's own), the store of
+    the round counter, the poll of the partner's counter (a 4-byte read, its
+    value made scalar, s_sleep between polls), and only after that the four
+    16-byte reads of the partner's slot.  The emulator runs the kernel's
+    order; this checks that the compiler kept it."""
+    which, text = isa
+    if which != "split":
+        pytest.skip("the split candidate")
+    for name, blocks in _kernels_asm(text).items():
+        flat = [(i, a) for _lab, ins in blocks for i, a in ins]
+        # the publish: the kernel's lgkmcnt(0) followed by a 4-byte LDS store
+        pub = [k for k in range(1, len(flat))
+               if flat[k][0].startswith("ds_write_b32") and any(
+                   flat[j][1] is not None and flat[j][0] == "s_waitcnt lgkmcnt(0)"
+                   for j in range(max(0, k - 4), k))]
+        assert len(pub) == 1, (name, pub)
+        k = pub[0]
+        before = [i for i, _a in flat[:k]]
+        assert [i for i in before if i.startswith("ds_write_b128")][-4:] and all(
+            i.startswith("ds_write_b128") or not i.startswith("ds_")
+            for i in before[len(before) - 12:]), name
+        after = [i for i, _a in flat[k + 1:]]
+        first_read = next(n for n, i in enumerate(after) if i.startswith("ds_read_b128"))
+        poll = after[:first_read]
+        assert any(i.startswith("ds_read_b32") for i in poll), name
+        assert any(i.startswith("v_readfirstlane_b32") for i in poll), name
+        assert any(i.startswith("s_sleep") for i in poll), name
+        assert sum(i.startswith("ds_read_b128") for i in after[first_read:first_read + 24]) >= 4
+
+
 # The library's e4m3 16-key kernels load Q before the key loop without
 # forcing it resident there, so the compiler's wait-count pass, which does
 # not see the copies, keeps those loads pending into the loop and waits for
