@@ -24,6 +24,7 @@
 #include <cstring>
 #include <deque>
 #include <memory>
+#include <utility>
 #include <vector>
 
 thread_local EmuIdx threadIdx;
@@ -120,14 +121,36 @@ std::atomic<const unsigned char*> lds_base{nullptr};
 void apply(const Pending& p) { std::memcpy(p.dst, p.data, p.n); }
 
 // EMU_SCHED=drift runs each wave alone until it blocks at a workgroup barrier
-// (waves drift apart as far as the kernel's synchronisation allows); the
-// default interleaves the waves one wave operation at a time.
+// (waves drift apart as far as the kernel's synchronisation allows);
+// EMU_SCHED=random visits the waves in a shuffled order every sweep and lets
+// each take one to four wave operations (seeded by EMU_SEED), so waves get
+// ahead of one another by varying, reproducible amounts; the default
+// interleaves the waves one wave operation at a time.
 bool drift_schedule() {
   static const bool v = [] {
     const char* e = std::getenv("EMU_SCHED");
     return e && std::strcmp(e, "drift") == 0;
   }();
   return v;
+}
+bool random_schedule() {
+  static const bool v = [] {
+    const char* e = std::getenv("EMU_SCHED");
+    return e && std::strcmp(e, "random") == 0;
+  }();
+  return v;
+}
+// splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the schedule's random stream
+uint64_t next_random() {
+  static uint64_t state = [] {
+    const char* e = std::getenv("EMU_SEED");
+    return e ? std::strtoull(e, nullptr, 10) : 1ull;
+  }();
+  uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
 }
 
 void yield_to_scheduler(bool finishing) {
@@ -259,6 +282,15 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
               }
             }
             ++rot;
+          } else if (random_schedule()) {
+            std::vector<int> order(nw);
+            for (int w = 0; w < nw; ++w) order[w] = w;
+            for (int w = nw - 1; w > 0; --w) std::swap(order[w], order[next_random() % (w + 1)]);
+            for (int w : order) {
+              const int steps = 1 + int(next_random() % 4);
+              for (int k = 0; k < steps; ++k)
+                for (int t = 64 * w; t < 64 * w + 64; ++t) progressed |= resume(t);
+            }
           } else {
             for (int t = 0; t < nt; ++t) progressed |= resume(t);
           }

@@ -708,3 +708,50 @@ def test_split_random_shapes():
         jobs.append((case, nwg, 1, dict(env_extra={**MODES[modes[(trial // 2) % 3]], **SPLIT})))
     for (c, *_), (out, lse, _m) in zip(jobs, harness.run_many(jobs, workers=8)):
         _check(c, out, lse)
+
+
+# ---------------------------------------------------------------- random schedules
+# EMU_SCHED=random: every sweep visits the waves in a shuffled order and lets
+# each take one to four wave operations (seeded by EMU_SEED), so waves get
+# ahead of one another by varying amounts between their synchronisation
+# points, in both copy-landing modes.
+
+
+def test_random_schedules_every_decode_kernel():
+    # the library kernels (one and four phases), both two-waves-per-SIMD
+    # candidates and the Q-resident e4m3 rebuild, both cache types
+    jobs = []
+    # (workgroup counts divisible by 4, so that the planner takes four phases)
+    specs = [([700, 130, 5], [2, 2, 1], 8), ([1500, 65, 900], [1, 1, 2], 4)]
+    for kvd in ("bf16", "fp8_e4m3"):
+        for kv, ql, nwg in specs:
+            c = make_case(kv_lens=kv, q_lens=ql, seed=61, kv_dtype=kvd, max_q_len=2,
+                          sm_scale=1 / math.sqrt(192))
+            for kernel, phases in ((None, 1), (None, 4), ("w8", 1), ("split", 1), ("qres", 1)):
+                if kernel == "qres" and kvd == "bf16":
+                    continue
+                for seed in (1, 2):
+                    for land in ("wait", "issue"):
+                        env = {"EMU_SCHED": "random", "EMU_SEED": str(seed), "EMU_DMA_LAND": land}
+                        if kernel:
+                            env["MLA_DECODE_KERNEL"] = kernel
+                        jobs.append((c, nwg, phases, dict(env_extra=env)))
+    for (c, _n, ph, _kw), (out, lse, meta) in zip(jobs, harness.run_many(jobs, workers=8)):
+        assert meta["phases"] == ph
+        _check(c, out, lse)
+
+
+def test_random_schedules_catch_a_missing_partner_wait():
+    # the split candidate without its counter wait (planted on the CPU):
+    # every random schedule lets a wave read its partner's slot too early
+    from tests.simt_emu import build as _b
+    old, new, _mode, _kvd = SPLIT_PLANTS["partner_wait"]
+    binary = _b.build(tag="split_planted_partner_wait",
+                      patches={"decode_split_kernel.hip": [(old, new)]})
+    case = make_case(kv_lens=[700, 300, 130], q_lens=[2, 1, 2], seed=5, max_q_len=2,
+                     sm_scale=1 / math.sqrt(192))
+    for seed in (1, 2, 3):
+        out, lse, _ = harness.run(case, 3, 1, binary=binary, env_extra={
+            "EMU_SCHED": "random", "EMU_SEED": str(seed), "EMU_DMA_LAND": "wait", **SPLIT})
+        with pytest.raises(AssertionError):
+            _check(case, out, lse)
