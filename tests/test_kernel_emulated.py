@@ -730,12 +730,13 @@ def test_random_schedules_every_decode_kernel():
             for kernel, phases in ((None, 1), (None, 4), ("w8", 1), ("split", 1), ("qres", 1)):
                 if kernel == "qres" and kvd == "bf16":
                     continue
-                for seed in (1, 2):
-                    for land in ("wait", "issue"):
-                        env = {"EMU_SCHED": "random", "EMU_SEED": str(seed), "EMU_DMA_LAND": land}
-                        if kernel:
-                            env["MLA_DECODE_KERNEL"] = kernel
-                        jobs.append((c, nwg, phases, dict(env_extra=env)))
+                for land in ("wait", "issue"):
+                    # a schedule seed of its own for every run
+                    env = {"EMU_SCHED": "random", "EMU_SEED": str(100 + len(jobs)),
+                           "EMU_DMA_LAND": land}
+                    if kernel:
+                        env["MLA_DECODE_KERNEL"] = kernel
+                    jobs.append((c, nwg, phases, dict(env_extra=env)))
     for (c, _n, ph, _kw), (out, lse, meta) in zip(jobs, harness.run_many(jobs, workers=8)):
         assert meta["phases"] == ph
         _check(c, out, lse)

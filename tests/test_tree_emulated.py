@@ -39,7 +39,8 @@ def check_tree(case, mask, out_bits, lse):
         den += float((O[b, :q] ** 2).sum())
         # a row with no visible key at all: O = 0 and LSE = -inf on both sides
         same_inf = np.isinf(L[b, :q]) & (lse[b, :q] == L[b, :q])
-        assert float(np.where(same_inf, 0.0, np.abs(lse[b, :q] - L[b, :q])).max()) <= 1e-3
+        gap = np.abs(np.where(same_inf, 0.0, lse[b, :q]) - np.where(same_inf, 0.0, L[b, :q]))
+        assert float(gap.max()) <= 1e-3
         if q < case.max_q_len:
             assert np.all(out_bits[b, q:] == 0xC1C1)
     assert worst <= mabs, worst
