@@ -84,3 +84,12 @@ def test_split_full_size_workloads(name):
     assert pl.phases == 1
     worst, rel = check(case, out, lse)
     print(f"split: {name}: max-abs {worst:.3g} rel-L2 {rel:.3g}", flush=True)
+
+
+def test_split_graph_replay_with_new_lengths():
+    # fwd + combine captured once in a HIP graph over a fixed-shape plan and
+    # replayed for other lengths (the library's graph test, with the
+    # candidate selected): each replay equal, bit for bit, to the eager call
+    from tests import test_gpu_graph
+    print("split: graph replay", flush=True)
+    test_gpu_graph.test_graph_replay_with_new_lengths()

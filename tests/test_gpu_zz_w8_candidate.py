@@ -122,3 +122,12 @@ def test_w8_combine_of_bf16_partials_matches_combine_ref():
                 continue
             assert abs(l[b, t, h] - Lc[r]) <= 1e-4 * max(1.0, abs(Lc[r]))
             assert np.abs(o[b, t, h] - Oc[r]).max() <= 4e-3 * np.abs(Oc[r]).max()
+
+
+def test_w8_graph_replay_with_new_lengths():
+    # fwd + combine captured once in a HIP graph over a fixed-shape plan and
+    # replayed for other lengths (the library's graph test, with the
+    # candidate selected): each replay equal, bit for bit, to the eager call
+    from tests import test_gpu_graph
+    print("w8: graph replay", flush=True)
+    test_gpu_graph.test_graph_replay_with_new_lengths()
