@@ -4,7 +4,6 @@ and the counter summary lookup that goes stale when a kernel source changes."""
 import math
 import os
 
-import numpy as np
 
 import bench
 from workloads import make_case

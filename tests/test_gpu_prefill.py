@@ -3,13 +3,11 @@ through the C ABI): INT8 / e4m3 codes and scales bit-exact against the
 oracle's quantizers; O and LSE against the oracle's blocked online softmax
 at the e4m3 bar, on whole small cases and on sampled rows of a 64K-token
 prompt."""
-import math
 
 import numpy as np
 import pytest
 
-from oracle import prefill_ref
-from tests.prefill_cases import check_attention, check_quantized, natural_v_codes
+from tests.prefill_cases import check_attention, check_quantized
 from workloads.prefill import PrefillCase, make_prefill_case, prefill_workload
 
 pytestmark = pytest.mark.gpu

@@ -1,7 +1,6 @@
 """Quantized prefill on the CPU emulator (mla_prefill_quantize +
 mla_prefill_attn under AddressSanitizer): codes and scales bit-exact against
 the oracle's quantizers, O and LSE against the oracle's blocked softmax."""
-import numpy as np
 import pytest
 
 from oracle import prefill_ref
