@@ -134,21 +134,32 @@ struct Ring {
   int page_shift, k0, L, ntiles, lane;
 };
 
+// First key of tile t of round j: a tile past the item stands for the
+// round's first key (a harmless dummy copy of real cache rows).
+__device__ __forceinline__ int tile_key(const Ring& r, int t, int j) {
+  const int tile = kRoundTiles * j + t;
+  return tile < r.ntiles ? r.k0 + kTileTok * tile : r.k0 + kRoundTok * j;
+}
+
+// The cache page holding tile t of round j (a block-table read, issued a
+// round ahead of the copies that use it).
+__device__ __forceinline__ int tile_page(const Ring& r, int t, int j) {
+  return r.bt_row[tile_key(r, t, j) >> r.page_shift];
+}
+
 // This wave's share of round j: half HALF (copies 9*HALF .. 9*HALF + 8) of
-// tile `t` of the round, into its ring stage.  A tile past the item is a
-// harmless dummy copy of the round's first key (every wave issues exactly
-// nine copies per round, so each wave's vmcnt count is the same).  Copy ins
-// fills the stage's 1 KB block ins: rows 8(ins&1) .. +7, bytes 128(ins>>1) ..
-// +127 of each row, in the library's tile layout.
+// tile `t` of the round, which lies in page pg, into its ring stage (every
+// wave issues exactly nine copies per round, so each wave's vmcnt count is
+// the same).  Copy ins fills the stage's 1 KB block ins: rows 8(ins&1) .. +7,
+// bytes 128(ins>>1) .. +127 of each row, in the library's tile layout.
 template <int HALF>
-__device__ __forceinline__ void issue_half(const Ring& r, int t, int j) {
+__device__ __forceinline__ void issue_half(const Ring& r, int t, int j, int pg) {
   const int tile = kRoundTiles * j + t;
   const int stage = tile % Lds<0>::kStages;
-  const int kr = r.k0 + kRoundTok * j;          // first key of the round (< L)
   const bool real = tile < r.ntiles;
-  const int kt = real ? r.k0 + kTileTok * tile : kr;
+  const int kt = tile_key(r, t, j);
   const int pmask = (1 << r.page_shift) - 1;
-  const int row0 = (r.bt_row[kt >> r.page_shift] << r.page_shift) + (kt & pmask);
+  const int row0 = (pg << r.page_shift) + (kt & pmask);
   const uint8_t* base = uniform_ptr(r.kv + (int64_t)row0 * kRowBytes);
   const int nvalid = real ? min(kTileTok, r.L - kt) : 0;
   const uint32_t lds = r.lds + stage * kTileBytes;
@@ -170,9 +181,9 @@ __device__ __forceinline__ void issue_half(const Ring& r, int t, int j) {
   }
 }
 
-__device__ __forceinline__ void issue_round(const Ring& r, int t, int half, int j) {
-  if (half) issue_half<1>(r, t, j);
-  else issue_half<0>(r, t, j);
+__device__ __forceinline__ void issue_round(const Ring& r, int t, int half, int j, int pg) {
+  if (half) issue_half<1>(r, t, j, pg);
+  else issue_half<0>(r, t, j, pg);
 }
 
 // ---- e4m3 caches.  A round of 64 keys is one run of one page (pages hold a
@@ -187,17 +198,21 @@ struct RingF8 {
   int page_shift, k0, L, wave, lane;
 };
 
-// This wave's share of round r into ring slot r & 1: copies wave, wave + 8,
+__device__ __forceinline__ int round_page_f8(const RingF8& r, int j) {
+  return r.bt_row[(r.k0 + kRoundTok * j) >> r.page_shift];
+}
+
+// This wave's share of round j, which lies in page pg, into ring slot j & 1: copies wave, wave + 8,
 // ... (< 36) of the round's 36 KB (copy ins = bytes 1024 ins .. + 1023, lane
 // l taking 16 bytes at 16 l; a row is 36 such pieces, so a piece lies in one
 // row), and for wave 7 the round's 64 scales.  Lanes whose piece lies in a
 // row past the sequence's end are masked off, so no cache slot past the
 // sequence is read (the widening zeroes those rows; a scale lane past the end
 // copies the round's first scale).
-__device__ __forceinline__ void issue_round_f8(const RingF8& r, int j) {
+__device__ __forceinline__ void issue_round_f8(const RingF8& r, int j, int pg) {
   const int kr = r.k0 + kRoundTok * j;          // first key of the round (< L)
   const int pmask = (1 << r.page_shift) - 1;
-  const int row0 = (r.bt_row[kr >> r.page_shift] << r.page_shift) + (kr & pmask);
+  const int row0 = (pg << r.page_shift) + (kr & pmask);
   const uint8_t* base = uniform_ptr(r.kv + (int64_t)row0 * kF8RowBytes);
   const uint32_t lds = r.ring + (j & 1) * kF8RoundBytes;
   const int lane = opaque(r.lane);
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
 
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
-      if (nrounds > 0) issue_round(ring, tq, half, 0);
+      if (nrounds > 0) issue_round(ring, tq, half, 0, tile_page(ring, tq, 0));
       // Q must be resident before the key loop: otherwise the compiler,
       // which does not see the copies, keeps its loads pending into the loop
       // and waits for them there with vmcnt literals that, at run time, also
@@ -498,13 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       // round 0 anyway (the loop's first wait).
 #pragma unroll
       for (int c = 0; c < 18; ++c) require_vgpr(qf[c]);
+      int pg = nrounds > 1 ? tile_page(ring, tq, 1) : 0;   // page of the next round's tile
       // Round j opens by waiting for this wave's copies and the barrier (the
       // round's tiles come from all waves, and every wave is done with the
-      // stages round j + 1 refills); round j + 1 is then issued.
+      // stages round j + 1 refills); round j + 1, whose page was read in the
+      // previous round, is then issued.
       for (int j = 0; j < nrounds; ++j) {
         MLA_VM_WAIT(0);
         barrier();   // tiles of round j come from all waves
-        if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1);
+        if (j + 1 < nrounds) issue_round(ring, tq, half, j + 1, pg);
 #pragma unroll
         for (int pp = 0; pp < kRoundTiles / 2; ++pp) {
           const int tile = kRoundTiles * j + 2 * pp;   // first stage of the pair
@@ -513,6 +530,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
           const int so = (tile % Lds<0>::kStages) * kTileBytes;
           pair_step<0>(smem, fr, so, 0, kp, lim, lim_all, a.scale_log2, g4, qf, acc, m, l);
         }
+        // the page of round j + 2's tile, read under the round's last MFMAs
+        // and the barrier rather than between the barrier and the next pair
+        if (j + 2 < nrounds) pg = tile_page(ring, tq, j + 2);
       }
     } else {
       RingF8 ring;
@@ -536,15 +556,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
       // that round is in flight at the wait.
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) acc[cb] = f32x4{};
+      int pg = 0;   // page of the next round to issue
       if (npairs > 0) {
-        issue_round_f8(ring, 0);
+        issue_round_f8(ring, 0, round_page_f8(ring, 0));
         MLA_VM_WAIT(0);
-        // Q resident before the key loop (see the bf16 path)
+      }
+      // Q resident before the key loop (see the bf16 path), on every path
+      // into it
 #pragma unroll
-        for (int c = 0; c < 18; ++c) require_vgpr(qf[c]);
+      for (int c = 0; c < 18; ++c) require_vgpr(qf[c]);
+      if (npairs > 0) {
         barrier();   // round 0 comes from all waves
         widen_pair_f8(smem, 0, k0, L, wave, lane);
-        if (nrounds > 1) issue_round_f8(ring, 1);
+        if (nrounds > 1) issue_round_f8(ring, 1, round_page_f8(ring, 1));
+        if (nrounds > 2) pg = round_page_f8(ring, 2);
       }
       // Pair p opens with the barrier after which pair p is widened by all
       // waves (and, for odd p, round (p + 1) / 2 has landed).  The two pairs
@@ -557,11 +582,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel_w8(
           if (p >= npairs) break;
           if (pp == 1) MLA_VM_WAIT(0);
           barrier();   // pair p widened by all waves; for odd p, round j + 1 copied
-          if (pp == 1 && j + 2 < nrounds) issue_round_f8(ring, j + 2);
+          if (pp == 1 && j + 2 < nrounds) issue_round_f8(ring, j + 2, pg);
           if (p + 1 < npairs)
             widen_pair_f8(smem, p + 1, k0 + 2 * kTileTok * (p + 1), L, wave, lane);
           pair_step<1>(smem, fr, pp * 2 * kTileBytes, Lds<1>::kPairScale + pp * 2 * kTileTok * 4,
                        k0 + 2 * kTileTok * p, lim, lim_all, a.scale_log2, g4, qf, acc, m, l);
+          // the page of round j + 3, read a round ahead of its copies
+          if (pp == 1 && j + 3 < nrounds) pg = round_page_f8(ring, j + 3);
         }
       }
     }
