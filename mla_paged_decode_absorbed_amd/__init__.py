@@ -314,7 +314,13 @@ def _stream(stream):
 
 def decode_fwd(shape: Shape, pl: Plan, q, kv_cache, block_table, kv_lens, q_lens, sm_scale: float,
                out, lse, workspace, kv_scale=None, stream=None):
-    """Launch the main kernel (``mla_decode_fwd``) on torch device tensors."""
+    """Launch the main kernel (``mla_decode_fwd``) on torch device tensors.
+
+    The library reads ``MLA_DECODE_KERNEL`` at each call: ``w8`` or ``split``
+    run a two-waves-per-SIMD candidate for one-phase plans (bf16 partials,
+    merged by ``combine`` under the same setting), ``qres`` the Q-resident
+    rebuild of the e4m3 kernels; none of them has run on a GPU yet, and the
+    default (unset) runs the validated kernels."""
     lib = load_library()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.mla_decode_fwd(ctypes.byref(shape), ctypes.byref(pl.info), _ptr(pl.device), _ptr(q),
