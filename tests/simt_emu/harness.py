@@ -17,6 +17,14 @@ PREFILL_MAGIC = 0x4D4C5046
 
 
 def ensure_built() -> str:
+    """The emulator binary, built if missing or older than its sources.
+    EMU_BINARY names another build to run instead (the UndefinedBehavior-
+    Sanitizer one, say), used as it is."""
+    other = os.environ.get("EMU_BINARY")
+    if other:
+        if not os.path.exists(other):
+            raise RuntimeError(f"EMU_BINARY {other} does not exist")
+        return other
     from tests.simt_emu import build as _b  # noqa: WPS433
     if not os.path.exists(BIN) or _stale():
         _b.build()
