@@ -141,7 +141,9 @@ int32_t mla_device_num_cus(int32_t device);
  * divides num_workgroups) instead lets groups of 2 or 4 workgroups on one XCD
  * share a block (each takes 64 or 32 of its rows over the same keys, which then
  * come from HBM once); MLA_NUM_WORKGROUPS forces the workgroup count.  Both are
- * for tuning and tests.
+ * for tuning and tests.  MLA_LOG=1 prints one line per plan on stderr: the
+ * shape, the counts of info, and the largest and mean number of keys a
+ * workgroup takes (the hot path itself never logs).
  *
  *   kv_lens_host [B]  keys per sequence, including this step's q_b tokens.
  *   q_lens_host  [B]  query tokens per sequence (0..max_q_len); NULL means

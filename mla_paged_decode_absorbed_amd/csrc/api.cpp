@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
@@ -64,6 +65,32 @@ bool qres_selected(const mla_shape* shape) {
   return variant && std::strcmp(variant, "qres") == 0 && shape->kv_dtype == MLA_KV_FP8_E4M3;
 }
 
+// MLA_LOG=1: one line per host plan on stderr (shape, counts, and the keys
+// each workgroup takes: the balance the planner reached).  Plan time only.
+void log_plan(const mla_shape* shape, const int32_t* plan, const mla_plan_info* info,
+              bool fixed_shape) {
+  const char* e = std::getenv("MLA_LOG");
+  if (!e || std::strcmp(e, "1") != 0) return;
+  const int32_t* wg_start = plan + plan[kWOffWgStart];
+  const int32_t* items = plan + plan[kWOffItems];
+  int64_t total = 0, most = 0;
+  for (int g = 0; g < info->num_workgroups; ++g) {
+    int64_t keys = 0;
+    for (int it = wg_start[g]; it < wg_start[g + 1]; ++it)
+      keys += items[it * kItemWords + 3] - items[it * kItemWords + 2];
+    total += keys;
+    most = keys > most ? keys : most;
+  }
+  const double mean = info->num_workgroups > 0 ? double(total) / info->num_workgroups : 0.0;
+  std::fprintf(stderr,
+               "mla: plan%s B %d H %d q_max %d page %d %s: %d workgroups, %d items, %d partials, "
+               "%d merged blocks, %d phase(s); keys per workgroup max %lld, mean %.1f\n",
+               fixed_shape ? " (fixed shape)" : "", shape->batch, shape->num_heads,
+               shape->max_q_len, shape->page_size, shape->kv_dtype == MLA_KV_BF16 ? "bf16" : "e4m3",
+               info->num_workgroups, info->num_items, info->num_partials, info->num_combine,
+               info->phases, static_cast<long long>(most), mean);
+}
+
 mla_status host_plan(const mla_shape* shape, const int32_t* kv_lens_host,
                      const int32_t* q_lens_host, int32_t num_workgroups, void* plan_host,
                      uint64_t plan_bytes, mla_plan_info* info, bool fixed_shape) {
@@ -74,9 +101,11 @@ mla_status host_plan(const mla_shape* shape, const int32_t* kv_lens_host,
   if ((reinterpret_cast<uintptr_t>(plan_host) & 3u) != 0) return MLA_ERR_MISALIGNED;
   st = validate_lengths(shape, kv_lens_host, q_lens_host);
   if (st != MLA_OK) return st;
-  return build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
-                    static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info,
-                    fixed_shape);
+  st = build_plan(*shape, kv_lens_host, q_lens_host, num_workgroups,
+                  static_cast<int32_t*>(plan_host), plan_bytes / sizeof(int32_t), info,
+                  fixed_shape);
+  if (st == MLA_OK) log_plan(shape, static_cast<const int32_t*>(plan_host), info, fixed_shape);
+  return st;
 }
 
 }  // namespace

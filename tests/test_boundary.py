@@ -402,3 +402,35 @@ def test_prefill_validates_before_any_launch(lib):
                  vc=None, vs=None) == 0
     assert attn(empty, cu=None, qc=None, qs=None, kc=None, ks=None, vc=None, vs=None, o=None,
                 lse=None) == 0
+
+
+def test_plan_log_line():
+    # MLA_LOG=1: one stderr line per host plan with its counts and the keys
+    # per workgroup (checked against the plan image); unset: nothing
+    code = (
+        "import numpy as np, mla_paged_decode_absorbed_amd as mla\n"
+        "from tests.test_boundary import _shape\n"
+        "kv = np.array([5, 4000, 70, 1, 9000], np.int32)\n"
+        "pl = mla.plan(_shape(B=5, qmax=1, maxp=200), kv, None, num_workgroups=32, upload=False)\n"
+        "it = pl.items()\n"
+        "ws = pl.wg_start()\n"
+        "G = pl.info.num_workgroups\n"
+        "keys = [int(sum(int(i[3]) - int(i[2]) for i in it[ws[g]:ws[g + 1]])) for g in range(G)]\n"
+        "print(G, pl.info.num_items, pl.info.num_partials, pl.info.num_combine, max(keys),\n"
+        "      '%.1f' % (sum(keys) / G))\n")
+    import os
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for log in ("1", ""):
+        env = dict(os.environ, MLA_LOG=log)
+        res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                             env=env, cwd=root, timeout=300)
+        assert res.returncode == 0, res.stderr[-2000:]
+        lines = [l for l in res.stderr.splitlines() if l.startswith("mla: plan")]
+        if not log:
+            assert not lines
+            continue
+        G, n_items, n_part, n_comb, most, mean = res.stdout.split()
+        assert lines == [f"mla: plan B 5 H 128 q_max 1 page 64 bf16: {G} workgroups, {n_items} "
+                         f"items, {n_part} partials, {n_comb} merged blocks, 1 phase(s); keys per "
+                         f"workgroup max {most}, mean {mean}"], lines
