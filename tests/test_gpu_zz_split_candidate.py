@@ -93,3 +93,25 @@ def test_split_graph_replay_with_new_lengths():
     from tests import test_gpu_graph
     print("split: graph replay", flush=True)
     test_gpu_graph.test_graph_replay_with_new_lengths()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_split_page_relayout_is_bitwise_identical(kv_dtype):
+    # the library's relayout check with the candidate selected: pages moved
+    # in the pool, the same plan, the same bits
+    from tests import test_gpu_parity
+    print(f"split: page relayout {kv_dtype}", flush=True)
+    test_gpu_parity.test_page_relayout_is_bitwise_identical(kv_dtype, 1)
+
+
+def test_split_repeat_runs_bitwise_equal():
+    # 20 runs of one plan, bit for bit equal (a race canary)
+    from tests import test_gpu_parity
+    print("split: repeat runs", flush=True)
+    test_gpu_parity.test_repeat_runs_bitwise_equal(1)
+
+
+def test_split_unused_block_table_entries_never_read():
+    from tests import test_gpu_parity
+    print("split: unused block-table entries", flush=True)
+    test_gpu_parity.test_unused_block_table_entries_never_read()
