@@ -530,11 +530,10 @@ def main() -> int:
                          "(per-CU throughput against the number of CUs at work)")
     ap.add_argument("--decode-kernel", choices=("default", "w8", "qres", "split"),
                     default="default",
-                    help="w8: time the two-waves-per-SIMD candidate (one-phase plans, bf16 or "
-                         "e4m3 cache); qres: the library's e4m3 kernels with Q resident before "
-                         "the key loop (e4m3 caches); split: the candidate whose pairs of waves "
-                         "share 32 rows (one-phase plans, bf16 or e4m3 cache); none has run on a "
-                         "GPU yet")
+                    help="w8: time the two-waves-per-SIMD candidate with 16 rows per wave "
+                         "(one-phase plans, bf16 or e4m3 cache); split: the one whose pairs of "
+                         "waves share 32 rows (likewise); qres: the library's e4m3 kernels with Q "
+                         "resident before the key loop (e4m3 caches); none has run on a GPU yet")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times "
                          "(scales HBM byte counters against a kernel of known traffic)")
