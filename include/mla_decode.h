@@ -246,18 +246,19 @@ mla_status mla_decode_plan_device(const mla_shape* shape, int32_t num_workgroups
  *                [num_partials][128].
  *
  * Kernel choice: the environment variable MLA_DECODE_KERNEL=w8 selects, for
- * one-phase plans, a candidate kernel with two waves per SIMD (not yet run on
- * a GPU).  It writes the partial O as bf16 [num_partials][128][d_latent] in
- * the first half of the same area (the LSE where it always is), and
- * mla_combine, seeing the same setting, merges that layout: both calls of a
- * step must see the same value.  MLA_DECODE_KERNEL=split selects, for
- * one-phase plans, a second two-waves-per-SIMD candidate (bf16 or e4m3
- * cache) in which each pair of waves shares 32 query rows (half the
- * dimensions and half the output columns each); it writes and merges the
- * same bf16 partials, and is not yet run on a GPU either.  MLA_DECODE_KERNEL=qres
- * selects, for e4m3 caches, the library's e4m3 kernels rebuilt with the
- * query fragments resident before the key loop (same partials, same merge;
- * not yet run on a GPU either).
+ * one-phase plans, a candidate kernel with two waves per SIMD and 16 query
+ * rows per wave (not yet run on a GPU).  It writes the partial O as bf16
+ * [num_partials][128][d_latent] in the first half of the same area (the LSE
+ * where it always is), and mla_combine, seeing the same setting, merges that
+ * layout: both calls of a step must see the same value.
+ * MLA_DECODE_KERNEL=split selects, for one-phase plans, a second
+ * two-waves-per-SIMD candidate in which each pair of waves shares 32 query
+ * rows (half the dimensions and half the output columns each); it writes and
+ * merges the same bf16 partials, and is not yet run on a GPU either.  Both
+ * take bf16 and e4m3 caches.  MLA_DECODE_KERNEL=qres selects, for e4m3
+ * caches, the library's e4m3 kernels rebuilt with the query fragments
+ * resident before the key loop (same partials, same merge; not yet run on a
+ * GPU either).
  *
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, BAD_PLAN,
  * WORKSPACE_TOO_SMALL, HIP (launch failure).
