@@ -55,13 +55,15 @@ def compiler() -> str:
 
 
 def build(sanitize: bool = True, decode_source: str | None = None, tag: str = "",
-          patches: dict | None = None, ubsan: bool = False) -> str:
+          patches: dict | None = None, ubsan: bool = False, lds_trace: bool = False) -> str:
     """Build the emulator binary.  ``decode_source`` replaces the library's
     decode_kernel.hip (a candidate kernel); ``patches`` maps a copied source
     file to (old, new) text replacements, each of which must apply (a variant
     of the library, built on the CPU only); ``tag`` names that binary;
     ``ubsan`` adds UndefinedBehaviorSanitizer (every unit rebuilt, the run
-    stopping at the first report)."""
+    stopping at the first report); ``lds_trace`` makes the decode kernels'
+    LDS pointers log their accesses for the bank model (every unit rebuilt;
+    the counts are written where EMU_LDS_STATS names)."""
     out = os.path.join(OUT, tag) if tag else OUT
     src = os.path.join(out, "src")
     os.makedirs(src, exist_ok=True)
@@ -88,13 +90,15 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
         flags.append("-fsanitize=address")
     if ubsan:
         flags += ["-fsanitize=undefined", "-fno-sanitize-recover=undefined"]
+    if lds_trace:
+        flags.append("-DEMU_LDS_TRACE")
     units = [os.path.join(src, f) for f in UNITS]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     # A variant recompiles only the units that are, or include, a changed
     # file, and links the base build's other objects (brought up to date
     # first).
     changed = set(patches or {}) | ({"decode_kernel.hip"} if decode_source else set())
-    reuse = bool(tag) and sanitize and not ubsan
+    reuse = bool(tag) and sanitize and not ubsan and not lds_trace
     if reuse:
         from tests.simt_emu import harness as _h
         _h.ensure_built()

@@ -17,6 +17,7 @@
 #include <sanitizer/common_interface_defs.h>
 #include <sys/mman.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include <cstdio>
@@ -80,9 +81,16 @@ struct Barrier {
   unsigned gen = 0;
 };
 
+struct Access {
+  const unsigned char* addr;
+  int bytes;
+  bool write;
+};
+
 struct Wave {
   Barrier bar;
   alignas(64) unsigned char slot[64][128];
+  std::vector<Access> trace[64];   // LDS accesses per lane since the last analysis
 };
 
 struct Pending {
@@ -184,6 +192,117 @@ extern "C" void emu_fiber_entry() {
   fail("finished fiber resumed");
 }
 
+// ---- LDS bank model (EMU_LDS_TRACE builds).  An instruction's lanes are
+// served in groups that together move one row of the banks (banks x 4
+// bytes: 8 lanes of 16 bytes with 32 banks, 16 with 64, and so on); within a
+// group, every distinct dword maps to bank (address / 4) mod banks, and a
+// bank holding d distinct dwords costs d - 1 extra cycles (the same dword for
+// several lanes is a broadcast).  EMU_LDS_BANKS sets the bank count (64 by
+// default); EMU_LDS_STATS names a file the totals are written to at exit.
+struct LdsStat {
+  long long instructions = 0, groups = 0, extra = 0, worst = 0;
+};
+struct LdsStats {
+  LdsStat kind[2][5][2];   // [write][log2(bytes / 4) .. tr16 = 4][ignored]
+  long long unaligned = 0;
+} lds_stats;
+
+bool lds_tracing() {
+  static const bool v = std::getenv("EMU_LDS_STATS") != nullptr;
+  return v;
+}
+
+int lds_banks() {
+  static const int v = [] {
+    const char* e = std::getenv("EMU_LDS_BANKS");
+    return e ? std::atoi(e) : 64;
+  }();
+  return v;
+}
+
+void lds_write_stats() {
+  const char* path = std::getenv("EMU_LDS_STATS");
+  if (!path) return;
+  FILE* f = std::fopen(path, "w");
+  if (!f) return;
+  static const char* names[5] = {"b32", "b64", "b128", "b256", "tr16_b64"};
+  std::fprintf(f, "{\"banks\": %d, \"unaligned\": %lld", lds_banks(), lds_stats.unaligned);
+  for (int w = 0; w < 2; ++w)
+    for (int k = 0; k < 5; ++k) {
+      const LdsStat& st = lds_stats.kind[w][k][0];
+      if (!st.instructions) continue;
+      std::fprintf(f, ", \"%s_%s\": [%lld, %lld, %lld, %lld]", w ? "write" : "read", names[k],
+                   st.instructions, st.groups, st.extra, st.worst);
+    }
+  std::fprintf(f, "}\n");
+  std::fclose(f);
+}
+
+// Score one instruction: per-lane start addresses (nullptr: lane inactive).
+void lds_score(const unsigned char* const* addr, int bytes, bool write, int kind) {
+  const unsigned char* base = lds_base.load();
+  if (!base) return;
+  static bool registered = false;
+  if (!registered) {
+    registered = true;
+    std::atexit(lds_write_stats);
+  }
+  const int banks = lds_banks();
+  const int per_group = std::max(1, banks * 4 / bytes);
+  LdsStat& st = lds_stats.kind[write][kind][0];
+  ++st.instructions;
+  for (int g0 = 0; g0 < 64; g0 += per_group) {
+    std::vector<std::vector<long>> dwords(banks);
+    bool any = false;
+    for (int l = g0; l < g0 + per_group && l < 64; ++l) {
+      if (!addr[l]) continue;
+      any = true;
+      const long off = long(addr[l] - base);
+      for (int d = 0; d < bytes / 4; ++d) {
+        const long dw = off / 4 + d;
+        auto& v = dwords[dw % banks];
+        if (std::find(v.begin(), v.end(), dw) == v.end()) v.push_back(dw);
+      }
+    }
+    if (!any) continue;
+    ++st.groups;
+    long long degree = 1;
+    for (auto& v : dwords) degree = std::max<long long>(degree, (long long)v.size());
+    st.extra += degree - 1;
+    st.worst = std::max(st.worst, degree);
+  }
+}
+
+// Line up the lanes' traced accesses (the k-th of every lane is one
+// instruction) and score them; then clear the traces.
+void lds_analyze(Wave& w) {
+  size_t n = 0;
+  for (auto& t : w.trace) n = std::max(n, t.size());
+  for (size_t k = 0; k < n; ++k) {
+    const unsigned char* addr[64] = {};
+    int bytes = -1;
+    bool write = false, ok = true;
+    for (int l = 0; l < 64; ++l) {
+      if (k >= w.trace[l].size()) continue;
+      const Access& a = w.trace[l][k];
+      if (bytes < 0) {
+        bytes = a.bytes;
+        write = a.write;
+      } else if (a.bytes != bytes || a.write != write) {
+        ok = false;
+      }
+      addr[l] = a.addr;
+    }
+    if (!ok || (bytes != 4 && bytes != 8 && bytes != 16 && bytes != 32)) {
+      ++lds_stats.unaligned;
+      continue;
+    }
+    const int kind = bytes == 4 ? 0 : bytes == 8 ? 1 : bytes == 16 ? 2 : 3;
+    lds_score(addr, bytes, write, kind);
+  }
+  for (auto& t : w.trace) t.clear();
+}
+
 template <typename T, typename F>
 auto wave_op(const T& in, F&& f) {
   static_assert(sizeof(T) <= sizeof(Wave::slot[0]), "slot");
@@ -191,6 +310,8 @@ auto wave_op(const T& in, F&& f) {
   Wave& w = *me.wave;
   std::memcpy(w.slot[me.lane], &in, sizeof(T));
   wait_on(w.bar);
+  // between the two rendezvous no lane of the wave touches the LDS
+  if (me.lane == 0 && lds_tracing()) lds_analyze(w);
   auto get = [&](int l) {
     T x;
     std::memcpy(&x, w.slot[l], sizeof(T));
@@ -298,6 +419,8 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
             fail("deadlock: every live lane waits at a barrier no lane can complete, or for an "
                  "LDS word no lane raises");
         }
+        if (lds_tracing())
+          for (auto& w : S.waves) lds_analyze(*w);
       }
   for (Fiber& f : fib) munmap(f.stack, kStackBytes + page);
 }
@@ -347,6 +470,13 @@ void vm_wait(int n) {
 }
 
 void block_barrier() { wait_on(S.block_bar); }
+
+void lds_trace_access(const void* p, int bytes, bool write) {
+  const unsigned char* b = lds_base.load();
+  const unsigned char* c = static_cast<const unsigned char*>(p);
+  if (!b || c < b || c + bytes > b + kLdsLimit) fail("LDS access outside the LDS");
+  S.cur->wave->trace[S.cur->lane].push_back(Access{c, bytes, write});
+}
 
 // Publishing an LDS word is a wave operation: every lane of the wave has
 // made its earlier LDS writes before any lane stores the word.
@@ -451,6 +581,11 @@ emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c) {
 
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
   return wave_op(p, [](int l, auto get) {
+    if (l == 0 && lds_tracing()) {
+      const unsigned char* addr[64];
+      for (int k = 0; k < 64; ++k) addr[k] = reinterpret_cast<const unsigned char*>(get(k));
+      lds_score(addr, 8, false, 4);
+    }
     const int g = l >> 4, i = l & 15;
     emu_bf16x4 r;
     for (int row = 0; row < 4; ++row) {

@@ -6,7 +6,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifdef EMU_LDS_TRACE
+#include "lds_trace.h"
+#define LDS_PTR(T) emu::LdsP<T>
+#else
 #define LDS_PTR(T) T*
+#endif
 
 namespace emu {
 uint32_t lds_address(const void* p);

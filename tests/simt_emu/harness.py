@@ -35,7 +35,8 @@ def _stale() -> bool:
     from tests.simt_emu import build as _b
     t = os.path.getmtime(BIN)
     srcs = [os.path.join(_b.CSRC, f) for f in _b.KERNEL_FILES]
-    srcs += [os.path.join(HERE, f) for f in ("gfx950_asm.h", "emu_runtime.cpp", "run_case.cpp",
+    srcs += [os.path.join(HERE, f) for f in ("gfx950_asm.h", "lds_trace.h", "emu_runtime.cpp",
+                                              "run_case.cpp",
                                               os.path.join("hip", "hip_runtime.h"), "build.py")]
     return any(os.path.getmtime(s) > t for s in srcs)
 
