@@ -14,7 +14,9 @@ cross-compiles; nothing runs on a GPU).
   MFMAs and LDS reads per 16-key tile.
 
 The default plan runs mla_decode_kernel_pairs (32 keys per step); the
-checks cover it and every instantiation of the 16-key kernel.
+checks cover it, every instantiation of the 16-key kernel, the Q-resident
+e4m3 rebuild and both two-waves-per-SIMD candidates (their register budgets,
+copy runs and wait literals, and the split candidate's exchange order).
 """
 import os
 import re
