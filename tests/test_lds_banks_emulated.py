@@ -81,3 +81,23 @@ def test_transposed_v_reads_would_conflict_at_32_banks(binary):
     st = _stats(binary, None, "bf16", 32)
     assert st["read_tr16_b64"][3] == 2 and st["read_tr16_b64"][2] > 0
     assert st["read_b128"][2] == 0
+
+
+def test_lds_bytes_per_32_keys_match_the_cost_model(binary):
+    # The LDS bytes a CU moves per 32 keys of a 128-row block, counted from
+    # the traced instructions (64 lanes each): 272 KB for the default bf16
+    # kernel (four waves: 36 K-fragment reads of 1 KB and 64 transposing
+    # reads of 512 bytes each), 544 KB for the 16-rows-per-wave candidate
+    # (eight waves reading all of K and V) and 336 KB for the split
+    # candidate (18 K reads and 32 transposing reads per wave, plus 4 KB of
+    # scores written and read per wave): the figures the design's LDS bound
+    # rests on.  The case's 128-row blocks take 2 x 22 + 2 x 5 + 1 = 55
+    # steps of 32 keys.
+    size = {"b32": 4, "b64": 8, "b128": 16, "tr16_b64": 8}
+    want = {None: 272, "w8": 544, "split": 336}
+    for kernel, kb in want.items():
+        st = _stats(binary, kernel, "bf16", 64)
+        moved = sum(v[0] * 64 * size[k.split("_", 1)[1]] for k, v in st.items()
+                    if k not in ("banks", "unaligned"))
+        per_step_kb = moved / 55 / 1024
+        assert abs(per_step_kb - kb) <= 0.02 * kb, (kernel, per_step_kb, st)
