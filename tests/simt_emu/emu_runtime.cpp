@@ -25,6 +25,7 @@
 #include <cstring>
 #include <deque>
 #include <memory>
+#include <unordered_set>
 #include <utility>
 #include <vector>
 
@@ -205,6 +206,8 @@ struct LdsStat {
 struct LdsStats {
   LdsStat kind[2][5][2];   // [write][log2(bytes / 4) .. tr16 = 4][ignored]
   long long unaligned = 0;
+  long long dma_lane_bytes = 0;            // bytes the HBM -> LDS copies read, lane by lane
+  std::unordered_set<uintptr_t> dma_lines; // distinct 128-byte lines they read
 } lds_stats;
 
 bool lds_tracing() {
@@ -226,7 +229,9 @@ void lds_write_stats() {
   FILE* f = std::fopen(path, "w");
   if (!f) return;
   static const char* names[5] = {"b32", "b64", "b128", "b256", "tr16_b64"};
-  std::fprintf(f, "{\"banks\": %d, \"unaligned\": %lld", lds_banks(), lds_stats.unaligned);
+  std::fprintf(f, "{\"banks\": %d, \"unaligned\": %lld, \"dma_lane_bytes\": %lld, "
+               "\"dma_lines\": %zu", lds_banks(), lds_stats.unaligned, lds_stats.dma_lane_bytes,
+               lds_stats.dma_lines.size());
   for (int w = 0; w < 2; ++w)
     for (int k = 0; k < 5; ++k) {
       const LdsStat& st = lds_stats.kind[w][k][0];
@@ -238,15 +243,19 @@ void lds_write_stats() {
   std::fclose(f);
 }
 
-// Score one instruction: per-lane start addresses (nullptr: lane inactive).
-void lds_score(const unsigned char* const* addr, int bytes, bool write, int kind) {
-  const unsigned char* base = lds_base.load();
-  if (!base) return;
+void lds_stats_at_exit() {
   static bool registered = false;
   if (!registered) {
     registered = true;
     std::atexit(lds_write_stats);
   }
+}
+
+// Score one instruction: per-lane start addresses (nullptr: lane inactive).
+void lds_score(const unsigned char* const* addr, int bytes, bool write, int kind) {
+  const unsigned char* base = lds_base.load();
+  if (!base) return;
+  lds_stats_at_exit();
   const int banks = lds_banks();
   const int per_group = std::max(1, banks * 4 / bytes);
   LdsStat& st = lds_stats.kind[write][kind][0];
@@ -455,6 +464,13 @@ void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
   p.dst = const_cast<unsigned char*>(b) + off;
   p.n = bytes;
   std::memcpy(p.data, static_cast<const unsigned char*>(sbase) + voff, bytes);   // checked read
+  if (lds_tracing()) {
+    lds_stats_at_exit();
+    const uintptr_t a = reinterpret_cast<uintptr_t>(sbase) + uintptr_t(voff);
+    lds_stats.dma_lane_bytes += bytes;
+    for (uintptr_t line = a / 128; line <= (a + bytes - 1) / 128; ++line)
+      lds_stats.dma_lines.insert(line);
+  }
   if (land_at_issue()) apply(p);
   else S.cur->dma.push_back(p);
 }

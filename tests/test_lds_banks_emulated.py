@@ -52,18 +52,29 @@ def _stats(binary, kernel, kvd, banks):
         return json.load(open(path))
 
 
+def _kinds(st):
+    """The per-instruction-kind entries of a stats record: read_* / write_*."""
+    return {k: v for k, v in st.items() if k.startswith(("read_", "write_"))}
+
+
 @pytest.fixture(scope="module")
 def binary():
     from tests.simt_emu import build as _b
     return _b.build(tag="ldstrace", lds_trace=True)
 
 
-def test_decode_kernels_are_bank_conflict_free_at_64_banks(binary):
+@pytest.fixture(scope="module")
+def stats64(binary):
+    """{(kernel, cache type): stats at 64 banks}, all runs at once."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(max_workers=7) as ex:
+    with ThreadPoolExecutor(max_workers=len(KERNELS)) as ex:
         runs = list(ex.map(lambda kk: _stats(binary, kk[0], kk[1], 64), KERNELS))
-    for (kernel, kvd), st in zip(KERNELS, runs):
-        kinds = {k: v for k, v in st.items() if k not in ("banks", "unaligned")}
+    return dict(zip(KERNELS, runs))
+
+
+def test_decode_kernels_are_bank_conflict_free_at_64_banks(stats64):
+    for (kernel, kvd), st in stats64.items():
+        kinds = _kinds(st)
         total = sum(v[0] for v in kinds.values())
         assert total > 1000, (kernel, kvd, st)
         # [instructions, lane groups, extra cycles, worst degree]
@@ -83,7 +94,7 @@ def test_transposed_v_reads_would_conflict_at_32_banks(binary):
     assert st["read_b128"][2] == 0
 
 
-def test_lds_bytes_per_32_keys_match_the_cost_model(binary):
+def test_lds_bytes_per_32_keys_match_the_cost_model(stats64):
     # The LDS bytes a CU moves per 32 keys of a 128-row block, counted from
     # the traced instructions (64 lanes each): 272 KB for the default bf16
     # kernel (four waves: 36 K-fragment reads of 1 KB and 64 transposing
@@ -96,8 +107,32 @@ def test_lds_bytes_per_32_keys_match_the_cost_model(binary):
     size = {"b32": 4, "b64": 8, "b128": 16, "tr16_b64": 8}
     want = {None: 272, "w8": 544, "split": 336}
     for kernel, kb in want.items():
-        st = _stats(binary, kernel, "bf16", 64)
-        moved = sum(v[0] * 64 * size[k.split("_", 1)[1]] for k, v in st.items()
-                    if k not in ("banks", "unaligned"))
+        st = stats64[(kernel, "bf16")]
+        moved = sum(v[0] * 64 * size[k.split("_", 1)[1]] for k, v in _kinds(st).items())
         per_step_kb = moved / 55 / 1024
         assert abs(per_step_kb - kb) <= 0.02 * kb, (kernel, per_step_kb, st)
+
+
+def test_copies_read_each_cached_row_once_per_row_block(stats64):
+    # The HBM -> LDS copies, counted in the same trace: the distinct bytes
+    # they read are exactly the sequences' cached rows (none outside a
+    # sequence, none missed; for e4m3 also the rows' scales), and per 128-row
+    # block every key is copied once, up to the kernel's round: 64 keys for
+    # the default kernel and the 16-rows-per-wave candidate (a round's
+    # stages past the item copy its first row again), 32 for the split
+    # candidate.  Two of the case's sequences carry two draft tokens, i.e.
+    # two row blocks each.
+    import numpy as np
+    blocks = np.array([2, 2, 1])
+    for kvd, row in (("bf16", 1152), ("fp8_e4m3", 576)):
+        for kernel, rnd in ((None, 64), ("w8", 64), ("split", 32)):
+            st = stats64[(kernel, kvd)]
+            lens = np.array([700, 130, 5])
+            rows = int(lens.sum()) * row
+            if kvd == "bf16":
+                assert st["dma_lines"] * 128 == rows, (kernel, st["dma_lines"])
+                copied = int((blocks * ((lens + rnd - 1) // rnd * rnd)).sum()) * row
+                assert st["dma_lane_bytes"] == copied, (kernel, st["dma_lane_bytes"], copied)
+            else:
+                scales = int(lens.sum()) * 4
+                assert rows <= st["dma_lines"] * 128 <= rows + scales + 128 * 8, (kernel, st)
