@@ -6,8 +6,8 @@ planner or the C-ABI layer, stop the run.
 
 A selection of the emulated suites runs against that build (EMU_BINARY names
 it to the harness): every decode kernel under random schedules in both
-copy-landing modes, the split candidate's parity cases, a cache append,
-tree drafts, the device planner, the input check and the quantized prefill.
+copy-landing modes, a cache append, tree drafts, the device planner, the
+input check and the quantized prefill.
 The whole emulated suite passed against it in a one-off run."""
 import os
 import subprocess
@@ -23,7 +23,6 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 SELECTION = [
     "tests/test_kernel_emulated.py::test_random_schedules_every_decode_kernel",
-    "tests/test_kernel_emulated.py::test_split_kernel_matches_oracle",
     "tests/test_append_emulated.py::test_decode_step_append",
     "tests/test_tree_emulated.py::test_tree_drafts_through_the_split_decode_kernel",
     "tests/test_plan_device_emulated.py::test_device_plan_without_q_lens_and_non_causal",
