@@ -756,3 +756,22 @@ def test_random_schedules_catch_a_missing_partner_wait():
             "EMU_SCHED": "random", "EMU_SEED": str(seed), "EMU_DMA_LAND": "wait", **SPLIT})
         with pytest.raises(AssertionError):
             _check(case, out, lse)
+
+
+def test_candidate_switches_leave_other_plans_to_the_library():
+    # MLA_DECODE_KERNEL=w8 / split apply to one-phase plans only, qres to
+    # e4m3 caches only: a four-phase plan, or a bf16 cache under qres, runs
+    # (and merges with) the library's kernels and still matches the oracle
+    jobs = []
+    for kvd in ("bf16", "fp8_e4m3"):
+        case = make_case(kv_lens=[900, 70], q_lens=[1, 2], seed=29, kv_dtype=kvd, max_q_len=2,
+                         sm_scale=1 / math.sqrt(192))
+        for kernel in ("w8", "split"):
+            jobs.append((case, 16, 4, dict(env_extra={**MODES["wait-lockstep"],
+                                                      "MLA_DECODE_KERNEL": kernel})))
+        if kvd == "bf16":
+            jobs.append((case, 8, 1, dict(env_extra={**MODES["wait-lockstep"],
+                                                     "MLA_DECODE_KERNEL": "qres"})))
+    for (c, _n, ph, _kw), (out, lse, meta) in zip(jobs, harness.run_many(jobs)):
+        assert meta["phases"] == ph
+        _check(c, out, lse)
