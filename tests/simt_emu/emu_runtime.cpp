@@ -77,9 +77,11 @@ constexpr size_t kStackBytes = 512 * 1024;  // per lane fiber
   std::abort();
 }
 
+struct Wave;
 struct Barrier {
   int n = 0, count = 0;
   unsigned gen = 0;
+  Wave* owner = nullptr;   // the wave of a wave rendezvous (null: the workgroup barrier)
 };
 
 struct Access {
@@ -90,7 +92,11 @@ struct Access {
 
 struct Wave {
   Barrier bar;
-  alignas(64) unsigned char slot[64][128];
+  // operands of a wave operation, lane by lane; two sets used in turn, so a
+  // lane may write the next operation's operands while others still read
+  // this one's (it can reach the next operation only after every lane has
+  // arrived at, and so finished reading, this one)
+  alignas(64) unsigned char slot[2][64][128];
   std::vector<Access> trace[64];   // LDS accesses per lane since the last analysis
 };
 
@@ -109,6 +115,7 @@ struct Fiber {
   unsigned wait_gen = 0;
   const int* wait_flag = nullptr;   // blocked until *wait_flag >= wait_target
   int wait_target = 0;
+  unsigned ops = 0;                 // wave operations so far (selects the slot set)
   bool done = false;
   std::deque<Pending> dma;
 };
@@ -170,9 +177,15 @@ void yield_to_scheduler(bool finishing) {
   __sanitizer_finish_switch_fiber(fake, &S.bottom, &S.size);
 }
 
+bool lds_tracing();
+void lds_analyze(Wave& w);
+
 void wait_on(Barrier& b) {
   const unsigned g = b.gen;
   if (++b.count == b.n) {
+    // every lane of the wave (or workgroup) is here: none touches the LDS
+    // until the rendezvous opens, so a wave's traced accesses line up
+    if (b.owner && lds_tracing()) lds_analyze(*b.owner);
     b.count = 0;
     ++b.gen;
     return;
@@ -314,21 +327,18 @@ void lds_analyze(Wave& w) {
 
 template <typename T, typename F>
 auto wave_op(const T& in, F&& f) {
-  static_assert(sizeof(T) <= sizeof(Wave::slot[0]), "slot");
+  static_assert(sizeof(T) <= sizeof(Wave::slot[0][0]), "slot");
   Fiber& me = *S.cur;
   Wave& w = *me.wave;
-  std::memcpy(w.slot[me.lane], &in, sizeof(T));
+  const int set = int(me.ops++ & 1u);
+  std::memcpy(w.slot[set][me.lane], &in, sizeof(T));
   wait_on(w.bar);
-  // between the two rendezvous no lane of the wave touches the LDS
-  if (me.lane == 0 && lds_tracing()) lds_analyze(w);
   auto get = [&](int l) {
     T x;
-    std::memcpy(&x, w.slot[l], sizeof(T));
+    std::memcpy(&x, w.slot[set][l], sizeof(T));
     return x;
   };
-  auto r = f(me.lane, get);
-  wait_on(w.bar);
-  return r;
+  return f(me.lane, get);
 }
 
 
@@ -356,6 +366,7 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
         for (int w = 0; w < nt / 64; ++w) {
           S.waves.push_back(std::make_unique<Wave>());
           S.waves.back()->bar.n = 64;
+          S.waves.back()->bar.owner = S.waves.back().get();
         }
         for (int t = 0; t < nt; ++t) {
           Fiber& f = fib[t];
@@ -364,6 +375,7 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           f.wave = S.waves[t >> 6].get();
           f.wait_bar = nullptr;
           f.wait_flag = nullptr;
+          f.ops = 0;
           f.done = false;
           f.dma.clear();
           // initial frame: six zeroed callee-saved registers, then the entry
@@ -564,13 +576,18 @@ emu_u32x2 permlane32_swap(uint32_t a, uint32_t b) {
 emu_f32x4 mfma16x16x32(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c) {
   struct In { emu_bf16x8 a, b; };
   const emu_f32x4 out = wave_op(In{a, b}, [](int l, auto get) {
+    // the operands this lane's outputs use, each fetched once; the products
+    // are summed in k order as before
     emu_f32x4 d;
     const int j = l & 15;
+    emu_bf16x8 bq[4];
+    for (int q = 0; q < 4; ++q) bq[q] = get(j + 16 * q).b;
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * (l >> 4) + r;
+      emu_bf16x8 aq[4];
+      for (int q = 0; q < 4; ++q) aq[q] = get(i + 16 * q).a;
       float s = 0.f;
-      for (int k = 0; k < 32; ++k)
-        s += float(get(i + 16 * (k >> 3)).a[k & 7]) * float(get(j + 16 * (k >> 3)).b[k & 7]);
+      for (int k = 0; k < 32; ++k) s += float(aq[k >> 3][k & 7]) * float(bq[k >> 3][k & 7]);
       d[r] = s;
     }
     return d;
@@ -581,13 +598,17 @@ emu_f32x4 mfma16x16x32(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c) {
 emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c) {
   struct In { emu_bf16x8 a, b; };
   const emu_f32x16 out = wave_op(In{a, b}, [](int l, auto get) {
+    // the operands this lane's outputs use, each fetched once; the products
+    // are summed in k order as before
     emu_f32x16 d;
     const int j = l & 31;
+    const emu_bf16x8 b0 = get(j).b, b1 = get(j + 32).b;
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      const emu_bf16x8 a0 = get(i).a, a1 = get(i + 32).a;
       float s = 0.f;
-      for (int k = 0; k < 16; ++k)
-        s += float(get(i + 32 * (k >> 3)).a[k & 7]) * float(get(j + 32 * (k >> 3)).b[k & 7]);
+      for (int k = 0; k < 8; ++k) s += float(a0[k]) * float(b0[k]);
+      for (int k = 0; k < 8; ++k) s += float(a1[k]) * float(b1[k]);
       d[r] = s;
     }
     return d;
