@@ -2,7 +2,7 @@
 stubbed as available (tests/bench_stub_run.py), ``pytest --collect-only -m
 gpu`` imports every test_gpu_* module past its GPU guard, resolves their
 imports and expands their parameters, so a broken import or parametrization
-shows here rather than on the GPU machine.  Nothing is run."""
+shows here rather than in a GPU run.  Nothing is run."""
 import os
 import subprocess
 import sys
