@@ -63,7 +63,8 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
     ``ubsan`` adds UndefinedBehaviorSanitizer (every unit rebuilt, the run
     stopping at the first report); ``lds_trace`` makes the decode kernels'
     LDS pointers log their accesses for the bank model (every unit rebuilt;
-    the counts are written where EMU_LDS_STATS names)."""
+    the counts are written where EMU_LDS_STATS names) and for the race
+    detector (run with EMU_LDS_RACE set)."""
     out = os.path.join(OUT, tag) if tag else OUT
     src = os.path.join(out, "src")
     os.makedirs(src, exist_ok=True)

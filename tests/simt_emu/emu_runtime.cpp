@@ -69,6 +69,7 @@ namespace emu {
 namespace {
 
 constexpr int kLdsLimit = 160 * 1024;      // LDS bytes of one CU
+constexpr int kMaxWaves = 16;              // waves of a 1024-thread workgroup
 constexpr size_t kStackBytes = 512 * 1024;  // per lane fiber
 
 [[noreturn]] void fail(const char* what) {
@@ -118,6 +119,10 @@ struct Fiber {
   unsigned ops = 0;                 // wave operations so far (selects the slot set)
   bool done = false;
   std::deque<Pending> dma;
+  // race detector (EMU_LDS_RACE): this lane's vector clock over the waves of
+  // the workgroup, and its copies not yet waited for (LDS byte, size)
+  uint32_t vc[kMaxWaves] = {};
+  std::deque<std::pair<uint32_t, int>> race_dma;
 };
 
 struct Sched {
@@ -127,6 +132,8 @@ struct Sched {
   Fiber* cur = nullptr;
   Barrier block_bar;
   std::vector<std::unique_ptr<Wave>> waves;
+  Fiber* fibers = nullptr;   // the workgroup's lanes
+  int nfib = 0;
   void (*body)(void*) = nullptr;
   void* arg = nullptr;
 };
@@ -180,12 +187,148 @@ void yield_to_scheduler(bool finishing) {
 bool lds_tracing();
 void lds_analyze(Wave& w);
 
+// ---- LDS race detector (EMU_LDS_RACE set, in LDS-trace builds).  Each wave
+// is one thread of a happens-before model (its lanes run in program order on
+// the GPU): a lane carries a vector clock over the workgroup's waves, which
+// the workgroup barrier joins over all lanes, a published LDS word hands
+// over (release at lds_publish, acquire when a wait sees the value) and a
+// wave's own entry advances at each of those points.  Every traced LDS load
+// and store, transposing read and HBM -> LDS copy is checked per dword
+// against the last write and the reads since it: an access of another wave
+// that the accessing lane's clock does not order before it is a race (read
+// after write, write after write, write after read), whatever the schedule
+// happened to do.  A copy counts as written when the issuing wave waits for
+// it (vmcnt), and any access to its destination while it is in flight is a
+// race, also by the issuing wave.  The first race stops the run.
+bool race_checking() {
+  static const bool v = [] {
+    if (!std::getenv("EMU_LDS_RACE")) return false;
+#ifndef EMU_LDS_TRACE
+    fail("EMU_LDS_RACE needs the LDS-trace build");
+#endif
+    return true;
+  }();
+  return v;
+}
+
+struct RaceCell {
+  uint32_t gen = 0;        // workgroup the state belongs to (else: untouched)
+  int writer = -1;         // wave of the last write, -1 if none
+  int in_flight = 0;       // copies into the dword not yet waited for
+  uint32_t wepoch = 0;     // the writer's epoch at that write (or at the wait)
+  uint32_t reads[kMaxWaves] = {};   // each wave's latest read epoch since it
+};
+std::vector<RaceCell> race_cells(kLdsLimit / 4);
+uint32_t race_gen = 0;
+struct FlagRelease {
+  const int* p;
+  int value;
+  uint32_t vc[kMaxWaves];
+};
+std::vector<FlagRelease> race_flags;   // this workgroup's publishes, in order
+
+int race_waves() { return int(S.waves.size()); }
+
+RaceCell& race_cell(uint32_t dword) {
+  RaceCell& c = race_cells[dword];
+  if (c.gen != race_gen) c = RaceCell{race_gen};
+  return c;
+}
+
+[[noreturn]] void race_report(const char* kind, uint32_t dword, int other, uint32_t epoch) {
+  const Fiber& f = *S.cur;
+  std::fprintf(stderr,
+               "simt-emu: LDS race (%s) at LDS byte %u: wave %d lane %d has seen wave %d up to "
+               "epoch %u, which accessed the dword at epoch %u\n",
+               kind, 4 * dword, f.tid >> 6, f.lane, other, other >= 0 ? f.vc[other] : 0u, epoch);
+  fail("LDS race");
+}
+
+uint32_t race_offset(const void* p, int bytes) {
+  const unsigned char* b = lds_base.load();
+  const unsigned char* c = static_cast<const unsigned char*>(p);
+  if (!b || c < b || c + bytes > b + kLdsLimit) fail("LDS access outside the LDS");
+  return uint32_t(c - b);
+}
+
+// kind: 0 load, 1 store, 2 copy issued
+void race_access(uint32_t off, int bytes, int kind) {
+  Fiber& f = *S.cur;
+  const int u = f.tid >> 6;
+  for (uint32_t d = off / 4; d <= (off + uint32_t(bytes) - 1) / 4; ++d) {
+    RaceCell& c = race_cell(d);
+    if (c.in_flight)
+      race_report(kind == 0 ? "read of a copy in flight" : "write over a copy in flight", d,
+                  c.writer, c.wepoch);
+    if (c.writer >= 0 && c.writer != u && f.vc[c.writer] < c.wepoch)
+      race_report(kind == 0 ? "read after write" : "write after write", d, c.writer, c.wepoch);
+    if (kind == 0) {
+      c.reads[u] = std::max(c.reads[u], f.vc[u]);
+      continue;
+    }
+    for (int x = 0; x < race_waves(); ++x)
+      if (x != u && c.reads[x] > f.vc[x]) race_report("write after read", d, x, c.reads[x]);
+    c.writer = u;
+    c.wepoch = f.vc[u];
+    c.in_flight = kind == 2;
+    std::fill(std::begin(c.reads), std::end(c.reads), 0u);
+  }
+}
+
+// the issuing lane's wait for a copy: from here on it counts as written
+void race_copy_landed(uint32_t off, int bytes) {
+  Fiber& f = *S.cur;
+  for (uint32_t d = off / 4; d <= (off + uint32_t(bytes) - 1) / 4; ++d) {
+    RaceCell& c = race_cell(d);
+    c.in_flight = 0;
+    c.wepoch = f.vc[f.tid >> 6];
+  }
+}
+
+// the workgroup barrier opens: every lane leaves with the join of all
+// lanes' clocks, its own wave's entry advanced
+void race_barrier() {
+  uint32_t j[kMaxWaves] = {};
+  for (int t = 0; t < S.nfib; ++t)
+    for (int w = 0; w < kMaxWaves; ++w) j[w] = std::max(j[w], S.fibers[t].vc[w]);
+  for (int t = 0; t < S.nfib; ++t) {
+    std::memcpy(S.fibers[t].vc, j, sizeof j);
+    ++S.fibers[t].vc[t >> 6];
+  }
+}
+
+// a wave publishes `value` at p (every lane is at the publish): the first
+// lane to store it records the join of the wave's clocks
+void race_release(const int* p, int value) {
+  for (auto it = race_flags.rbegin(); it != race_flags.rend(); ++it)
+    if (it->p == p) {
+      if (it->value == value) return;
+      break;
+    }
+  FlagRelease r{p, value, {}};
+  const int w0 = 64 * (S.cur->tid >> 6);
+  for (int t = w0; t < w0 + 64; ++t)
+    for (int w = 0; w < kMaxWaves; ++w) r.vc[w] = std::max(r.vc[w], S.fibers[t].vc[w]);
+  race_flags.push_back(r);
+}
+
+// a lane's wait saw the word at p: it acquires the publish that stored it
+void race_acquire(const int* p) {
+  const int v = *static_cast<const volatile int*>(p);
+  for (auto it = race_flags.rbegin(); it != race_flags.rend(); ++it)
+    if (it->p == p && it->value == v) {
+      for (int w = 0; w < kMaxWaves; ++w) S.cur->vc[w] = std::max(S.cur->vc[w], it->vc[w]);
+      return;
+    }
+}
+
 void wait_on(Barrier& b) {
   const unsigned g = b.gen;
   if (++b.count == b.n) {
     // every lane of the wave (or workgroup) is here: none touches the LDS
     // until the rendezvous opens, so a wave's traced accesses line up
     if (b.owner && lds_tracing()) lds_analyze(*b.owner);
+    if (!b.owner && race_checking()) race_barrier();
     b.count = 0;
     ++b.gen;
     return;
@@ -358,10 +501,15 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
   }
   S.body = body;
   S.arg = arg;
+  S.fibers = fib.data();
+  S.nfib = nt;
+  if (race_checking() && nt / 64 > kMaxWaves) fail("race detector: more waves than it tracks");
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
         S.block_bar = Barrier{nt, 0, 0};
+        ++race_gen;
+        race_flags.clear();
         S.waves.clear();
         for (int w = 0; w < nt / 64; ++w) {
           S.waves.push_back(std::make_unique<Wave>());
@@ -378,6 +526,9 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* arg) {
           f.ops = 0;
           f.done = false;
           f.dma.clear();
+          std::fill(std::begin(f.vc), std::end(f.vc), 0u);
+          f.vc[t >> 6] = 1;
+          f.race_dma.clear();
           // initial frame: six zeroed callee-saved registers, then the entry
           uint64_t* top = reinterpret_cast<uint64_t*>(f.stack + page + kStackBytes);
           top -= 2;
@@ -483,6 +634,10 @@ void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
     for (uintptr_t line = a / 128; line <= (a + bytes - 1) / 128; ++line)
       lds_stats.dma_lines.insert(line);
   }
+  if (race_checking()) {
+    race_access(uint32_t(off), bytes, 2);
+    S.cur->race_dma.emplace_back(uint32_t(off), bytes);
+  }
   if (land_at_issue()) apply(p);
   else S.cur->dma.push_back(p);
 }
@@ -494,16 +649,22 @@ void vm_wait(int n) {
     apply(q.front());
     q.pop_front();
   }
+  auto& r = S.cur->race_dma;
+  while (int(r.size()) > n) {
+    race_copy_landed(r.front().first, r.front().second);
+    r.pop_front();
+  }
   wait_on(S.cur->wave->bar);
 }
 
 void block_barrier() { wait_on(S.block_bar); }
 
 void lds_trace_access(const void* p, int bytes, bool write) {
-  const unsigned char* b = lds_base.load();
-  const unsigned char* c = static_cast<const unsigned char*>(p);
-  if (!b || c < b || c + bytes > b + kLdsLimit) fail("LDS access outside the LDS");
-  S.cur->wave->trace[S.cur->lane].push_back(Access{c, bytes, write});
+  const uint32_t off = race_offset(p, bytes);
+  if (lds_tracing())
+    S.cur->wave->trace[S.cur->lane].push_back(
+        Access{static_cast<const unsigned char*>(p), bytes, write});
+  if (race_checking()) race_access(off, bytes, write ? 1 : 0);
 }
 
 // Publishing an LDS word is a wave operation: every lane of the wave has
@@ -513,7 +674,9 @@ void flag_publish(int* p, int value) {
   const unsigned char* c = reinterpret_cast<const unsigned char*>(p);
   if (!b || c < b || c + sizeof(int) > b + kLdsLimit) fail("flag store outside the LDS");
   wait_on(S.cur->wave->bar);
+  if (race_checking()) race_release(p, value);
   *static_cast<volatile int*>(p) = value;
+  if (race_checking()) ++S.cur->vc[S.cur->tid >> 6];
 }
 
 // A lane waiting for an LDS word another wave publishes is not resumed until
@@ -523,10 +686,12 @@ void flag_wait(const int* p, int target) {
   const unsigned char* b = lds_base.load();
   const unsigned char* c = reinterpret_cast<const unsigned char*>(p);
   if (!b || c < b || c + sizeof(int) > b + kLdsLimit) fail("flag wait outside the LDS");
-  if (*static_cast<const volatile int*>(p) >= target) return;
-  S.cur->wait_flag = p;
-  S.cur->wait_target = target;
-  yield_to_scheduler(false);
+  if (*static_cast<const volatile int*>(p) < target) {
+    S.cur->wait_flag = p;
+    S.cur->wait_target = target;
+    yield_to_scheduler(false);
+  }
+  if (race_checking()) race_acquire(p);
 }
 
 uint32_t readfirstlane(uint32_t v) {
@@ -617,6 +782,7 @@ emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c) {
 }
 
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
+  if (race_checking()) race_access(race_offset(p, 8), 8, 0);
   return wave_op(p, [](int l, auto get) {
     if (l == 0 && lds_tracing()) {
       const unsigned char* addr[64];
@@ -635,6 +801,7 @@ emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
 }
 
 emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p) {
+  if (race_checking()) race_access(race_offset(p, 8), 8, 0);
   return wave_op(p, [](int l, auto get) {
     const int g = l >> 4, i = l & 15;
     unsigned char out[8];

@@ -1,0 +1,166 @@
+"""LDS races in the decode kernels, found by a happens-before detector in the
+lane-fiber emulator (CPU only).
+
+With EMU_LDS_RACE set, the LDS-trace build of the emulator
+(tests/simt_emu/emu_runtime.cpp) treats each wave as one thread: a lane
+carries a vector clock over the workgroup's waves, joined at every workgroup
+barrier and handed over from lds_publish to the wait that sees the
+published value.  Every traced LDS load and store, transposing read and
+HBM -> LDS copy is checked per dword against the last write and the reads
+since it, and a copy counts as written only once its wave has waited for it.
+Two accesses of different waves that no barrier or counter orders are a
+race even where the schedule that ran happened to put them in a harmless
+order, so the check does not depend on the lockstep, drift or random
+schedule finding the bad interleaving.
+
+The checks: no decode kernel races on a case with several items per
+workgroup, in any schedule; each synchronisation step taken out of a kernel
+(planted in a copy of the source, on the CPU only) is reported, in the
+lockstep schedule, as the kind of race it opens; and the library kernels'
+known restart-flag race (a wave sets the flag while another still reads it
+in the same barrier interval) is reported whenever an item restarts."""
+import math
+import os
+import re
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from tests.test_kernel_emulated import _available, _check, _rising_scores_case
+from workloads import make_case
+
+pytestmark = pytest.mark.skipif(not _available(), reason="host clang++ not available")
+
+RACE = {"EMU_LDS_RACE": "1"}
+
+# (MLA_DECODE_KERNEL, cache type, phases): the library's kernels (the 32-key
+# pairs kernel is the bf16 one-phase default, the 16-key kernel serves e4m3
+# and the phased plans) and the three candidates
+KERNELS = [(None, "bf16", 1), (None, "bf16", 2), (None, "bf16", 4), (None, "fp8_e4m3", 1),
+           (None, "fp8_e4m3", 4), ("qres", "fp8_e4m3", 1), ("w8", "bf16", 1),
+           ("w8", "fp8_e4m3", 1), ("split", "bf16", 1), ("split", "fp8_e4m3", 1)]
+
+SCHEDULES = {"lockstep": {}, "drift": {"EMU_SCHED": "drift"},
+             "random": {"EMU_SCHED": "random", "EMU_SEED": "3"}}
+
+
+@pytest.fixture(scope="module")
+def binary():
+    from tests.simt_emu import build as _b
+    return _b.build(tag="ldstrace", lds_trace=True)
+
+
+def _case(kv_dtype):
+    # several items per workgroup at 4 workgroups, two draft tokens, a
+    # sequence shorter than a round and one spanning many pages
+    return make_case(kv_lens=[700, 300, 130, 5], q_lens=[2, 1, 2, 1], seed=5, max_q_len=2,
+                     kv_dtype=kv_dtype, sm_scale=1 / math.sqrt(192))
+
+
+def _run(binary, kernel, kv_dtype, phases, env, nwg=4):
+    from tests.simt_emu import harness
+    extra = {**RACE, **env}
+    if kernel:
+        extra["MLA_DECODE_KERNEL"] = kernel
+    case = _case(kv_dtype)
+    out, lse, _ = harness.run(case, nwg, phases, env_extra=extra, binary=binary)
+    _check(case, out, lse)
+
+
+def test_decode_kernels_have_no_lds_race(binary):
+    jobs = [(k, s) for k in KERNELS for s in SCHEDULES]
+
+    def one(job):
+        (kernel, kvd, phases), sched = job
+        try:
+            _run(binary, kernel, kvd, phases, SCHEDULES[sched])
+            return None
+        except (RuntimeError, AssertionError) as e:
+            return job, str(e)[-600:]
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        failures = [r for r in ex.map(one, jobs) if r]
+    assert not failures, failures
+
+
+# Synchronisation steps taken out, one at a time: (source file, text, its
+# replacement, cache type, the race the detector must report).
+PLANTS = {
+    # the default bf16 kernel's per-round barrier: waves read a round other
+    # waves' copies have not been waited for by a barrier
+    "pairs_barrier": ("decode_kernel.hip",
+                      "vm_wait_rounds<KVD>(ahead);\n"
+                      "        barrier();   // tiles of round j come from all waves",
+                      "vm_wait_rounds<KVD>(ahead);", "bf16", "read after write"),
+    # the 16-key kernel's (the e4m3 default)
+    "e4m3_barrier": ("decode_kernel.hip",
+                     "{\n          barrier();   // tiles of round j come from all waves", "{",
+                     "fp8_e4m3", "read after write"),
+    "w8_barrier": ("decode_w8_kernel.hip", "barrier();   // tiles of round j come from all waves",
+                   "/* removed */", "bf16", "read after write"),
+    # the split candidate: its round barrier, its wait for a round's copies,
+    # its partner's round counter and the barrier that closes an item
+    "split_barrier": ("decode_split_kernel.hip",
+                      "barrier();   // round j from all waves; round j - 1 and its exchange done",
+                      "/* removed */", "bf16", "read after write"),
+    "split_copy_wait": ("decode_split_kernel.hip", "if (j + 1 < nrounds) MLA_VM_WAIT(4);",
+                        "if (j + 1 < nrounds) MLA_VM_WAIT(8);", "bf16", "read of a copy in flight"),
+    "split_partner_wait": ("decode_split_kernel.hip", "lds_wait_at_least(flag_par, seq);",
+                           "/* removed */", "bf16", "read after write"),
+    "split_item_barrier": ("decode_split_kernel.hip",
+                           "    // item's prologue refills them\n    barrier();",
+                           "    // item's prologue refills them", "bf16", "write after read"),
+    # its e4m3 pipeline: the round barrier, the wait for the round about to
+    # be widened, and the prologue's wait for round 0
+    "split_f8_barrier": ("decode_split_kernel.hip",
+                         "barrier();   // round p widened and round p + 1 copied by all waves; "
+                         "round p - 1 done", "/* removed */", "fp8_e4m3", "write after read"),
+    "split_f8_copy_wait": ("decode_split_kernel.hip", "if (p + 2 < nrounds) MLA_VM_WAIT(2);",
+                           "if (p + 2 < nrounds) MLA_VM_WAIT(5);", "fp8_e4m3",
+                           "read of a copy in flight"),
+    "split_f8_first_wait": ("decode_split_kernel.hip",
+                            "MLA_VM_WAIT(0);   // this wave's copies of round 0 (and its Q loads)",
+                            "/* removed */", "fp8_e4m3", "read of a copy in flight"),
+}
+
+
+@pytest.fixture(scope="module")
+def planted():
+    """{plant: emulator binary}, built three at a time."""
+    from tests.simt_emu import build as _b
+
+    def one(name):
+        fname, old, new, _kvd, _kind = PLANTS[name]
+        src = open(os.path.join(_b.CSRC, fname)).read()
+        assert src.count(old) == 1, name
+        return _b.build(tag="race_" + name, lds_trace=True, patches={fname: [(old, new)]})
+
+    names = sorted(PLANTS)
+    with ThreadPoolExecutor(max_workers=3) as ex:
+        return dict(zip(names, ex.map(one, names)))
+
+
+@pytest.mark.parametrize("plant", sorted(PLANTS))
+def test_detector_reports_each_planted_mistake(planted, plant):
+    fname, _old, _new, kvd, kind = PLANTS[plant]
+    kernel = {"decode_w8_kernel.hip": "w8", "decode_split_kernel.hip": "split"}.get(fname)
+    with pytest.raises(RuntimeError, match=re.escape(f"LDS race ({kind})")):
+        _run(planted[plant], kernel, kvd, 1, {})
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_detector_reports_the_library_restart_flag_race(binary, kv_dtype):
+    # Scores that restart the item every 32 keys: a wave that overshoots sets
+    # the library kernels' single restart flag while other waves of the same
+    # barrier interval still read it (the race the drift schedule turns into
+    # a barrier deadlock); the detector names the flag's word in any
+    # schedule (152576 is that word's offset, kFlagOff in decode_kernel.hip).
+    # The candidates rescale instead and stay race-free.
+    from tests.simt_emu import harness
+    case = _rising_scores_case(kv_dtype, L=160)
+    with pytest.raises(RuntimeError, match=r"LDS race \(write after read\) at LDS byte 152576"):
+        harness.run(case, 1, 1, env_extra=RACE, binary=binary)
+    for kernel in ("w8", "split"):
+        out, lse, _ = harness.run(case, 1, 1, env_extra={**RACE, "MLA_DECODE_KERNEL": kernel},
+                                  binary=binary)
+        _check(case, out, lse)
