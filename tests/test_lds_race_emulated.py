@@ -84,10 +84,11 @@ def test_decode_kernels_have_no_lds_race(binary):
 
 
 # Synchronisation steps taken out, one at a time: (source file, text, its
-# replacement, cache type, the race the detector must report).
+# replacement, cache type, the race the detector must report, and the
+# MLA_DECODE_KERNEL value that runs it where the library's default does not).
 PLANTS = {
-    # the default bf16 kernel's per-round barrier: waves read a round other
-    # waves' copies have not been waited for by a barrier
+    # the default bf16 kernel's per-round barrier: a wave reads tiles that
+    # other waves copied, with no barrier after their waits for the copies
     "pairs_barrier": ("decode_kernel.hip",
                       "vm_wait_rounds<KVD>(ahead);\n"
                       "        barrier();   // tiles of round j come from all waves",
@@ -96,8 +97,20 @@ PLANTS = {
     "e4m3_barrier": ("decode_kernel.hip",
                      "{\n          barrier();   // tiles of round j come from all waves", "{",
                      "fp8_e4m3", "read after write"),
+    # the same step in the Q-resident rebuild, which is that source compiled
+    # with Q forced resident
+    "qres_barrier": ("decode_kernel.hip",
+                     "{\n          barrier();   // tiles of round j come from all waves", "{",
+                     "fp8_e4m3", "read after write", "qres"),
     "w8_barrier": ("decode_w8_kernel.hip", "barrier();   // tiles of round j come from all waves",
-                   "/* removed */", "bf16", "read after write"),
+                   "/* removed */", "bf16", "read after write", "w8"),
+    # the 16-rows-per-wave candidate's e4m3 pipeline: the barrier after a
+    # pair's widening, and the wait for the next round's copies
+    "w8_f8_barrier": ("decode_w8_kernel.hip",
+                      "barrier();   // pair p widened by all waves; for odd p, round j + 1 copied",
+                      "/* removed */", "fp8_e4m3", "read after write", "w8"),
+    "w8_f8_wait": ("decode_w8_kernel.hip", "if (pp == 1) MLA_VM_WAIT(0);", "/* removed */",
+                   "fp8_e4m3", "read of a copy in flight", "w8"),
     # the split candidate: its round barrier, its wait for a round's copies,
     # its partner's round counter and the barrier that closes an item
     "split_barrier": ("decode_split_kernel.hip",
@@ -130,7 +143,7 @@ def planted():
     from tests.simt_emu import build as _b
 
     def one(name):
-        fname, old, new, _kvd, _kind = PLANTS[name]
+        fname, old, new = PLANTS[name][:3]
         src = open(os.path.join(_b.CSRC, fname)).read()
         assert src.count(old) == 1, name
         return _b.build(tag="race_" + name, lds_trace=True, patches={fname: [(old, new)]})
@@ -142,8 +155,8 @@ def planted():
 
 @pytest.mark.parametrize("plant", sorted(PLANTS))
 def test_detector_reports_each_planted_mistake(planted, plant):
-    fname, _old, _new, kvd, kind = PLANTS[plant]
-    kernel = {"decode_w8_kernel.hip": "w8", "decode_split_kernel.hip": "split"}.get(fname)
+    fname, _old, _new, kvd, kind, *kernel = PLANTS[plant]
+    kernel = kernel[0] if kernel else {"decode_split_kernel.hip": "split"}.get(fname)
     with pytest.raises(RuntimeError, match=re.escape(f"LDS race ({kind})")):
         _run(planted[plant], kernel, kvd, 1, {})
 
