@@ -732,6 +732,32 @@ def test_split_exchange_order(isa):
 KNOWN_LOOP_VMCNT = {"mla_decode_kernelILi1E", "mla_decode_kernel_qresILi1ELi4E"}
 
 
+def test_every_barrier_follows_the_waves_lds_operations(isa):
+    """Each s_barrier of every decode kernel comes after an s_waitcnt that
+    includes lgkmcnt(0), with no LDS instruction between the two, on the one
+    path into it (a barrier is never a branch target here): a wave's LDS
+    stores and reads are complete before other waves pass the barrier.  The
+    CPU emulator's race detector takes LDS operations as complete in program
+    order at barriers and publishes, which this makes true of the machine
+    code (the publish's own wait is checked with the exchange above)."""
+    _which, text = isa
+    for name, blocks in _kernels_asm(text).items():
+        n = 0
+        for _lab, ins in blocks:
+            for k, (i, _a) in enumerate(ins):
+                if not i.startswith("s_barrier"):
+                    continue
+                n += 1
+                # the wait is in the same block (it shares the barrier's asm)
+                prior = [x for x, _ in ins[:k]]
+                w = next((j for j in range(len(prior) - 1, -1, -1)
+                          if prior[j].startswith("s_waitcnt") and "lgkmcnt(0)" in prior[j]), None)
+                assert w is not None, (name, _lab, k)
+                between = prior[w + 1:]
+                assert not any(x.startswith("ds_") for x in between), (name, _lab, between)
+        assert n >= 2, (name, n)
+
+
 def test_no_compiler_vmcnt_wait_in_key_loop(isa):
     """In every block that issues MFMAs, a vmcnt wait comes from the kernel's
     own inline assembly (which counts the copies), never from the compiler."""
