@@ -14,7 +14,7 @@ order, so the check does not depend on the lockstep, drift or random
 schedule finding the bad interleaving.
 
 The checks: no decode kernel races on a case with several items per
-workgroup, in any schedule; each synchronisation step taken out of a kernel
+workgroup, in any schedule, or on seeded random shapes; each synchronisation step taken out of a kernel
 (planted in a copy of the source, on the CPU only) is reported, in the
 lockstep schedule, as the kind of race it opens; and the library kernels'
 known restart-flag race (a wave sets the flag while another still reads it
@@ -81,6 +81,33 @@ def test_decode_kernels_have_no_lds_race(binary):
     with ThreadPoolExecutor(max_workers=8) as ex:
         failures = [r for r in ex.map(one, jobs) if r]
     assert not failures, failures
+
+
+def test_random_shapes_have_no_lds_race(binary):
+    """Seeded random shapes through every decode kernel, race-checked: batch,
+    heads, draft tokens, page size, lengths (at least the draft count),
+    phase count, workgroup count and schedule drawn at random."""
+    import numpy as np
+    from tests.simt_emu import harness
+    rng = np.random.default_rng(83)
+    jobs = []
+    for trial in range(40):
+        kernel, kvd, phases = KERNELS[trial % len(KERNELS)]
+        B, H, qmax = int(rng.integers(1, 5)), int(rng.choice([16, 32, 128])), int(rng.integers(1, 4))
+        P = int(rng.choice([64, 256] if kvd == "fp8_e4m3" else [16, 64, 256]))
+        ql = [int(x) for x in rng.integers(1, qmax + 1, B)]
+        lens = [max(q, int(x)) for q, x in zip(ql, rng.integers(0, 900, B))]
+        nwg = int(rng.integers(1, 12))
+        nwg = max(phases, nwg - nwg % phases)
+        sched = sorted(SCHEDULES)[trial % 3]
+        case = make_case(kv_lens=lens, q_lens=ql, seed=trial, kv_dtype=kvd, max_q_len=qmax,
+                         num_heads=H, page_size=P, sm_scale=1 / math.sqrt(192))
+        env = {**RACE, **SCHEDULES[sched]}
+        if kernel:
+            env["MLA_DECODE_KERNEL"] = kernel
+        jobs.append((case, nwg, phases, dict(env_extra=env, binary=binary)))
+    for (case, *_), (out, lse, _meta) in zip(jobs, harness.run_many(jobs, workers=8)):
+        _check(case, out, lse)
 
 
 # Synchronisation steps taken out, one at a time: (source file, text, its
