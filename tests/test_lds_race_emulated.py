@@ -204,3 +204,26 @@ def test_detector_reports_the_library_restart_flag_race(binary, kv_dtype):
         out, lse, _ = harness.run(case, 1, 1, env_extra={**RACE, "MLA_DECODE_KERNEL": kernel},
                                   binary=binary)
         _check(case, out, lse)
+
+
+def test_fifth_fault_plan_is_race_free():
+    # The plan of the fifth faulting GPU run (the library's planner with a
+    # per-piece charge of one round and one-round pieces: one workgroup takes
+    # two one-round items back to back), built for the emulator only, in the
+    # e4m3 case and page relayout it faulted on: no LDS race in any schedule
+    # or copy-landing mode, so the kernel's LDS protocol does not explain it.
+    from tests.simt_emu import build as _b, harness
+    from tests.test_kernel_emulated import _plan_items, _relayout
+    binary = _b.build(tag="race_min_piece_1", lds_trace=True, patches={"plan_core.h": [
+        ("constexpr int kMinPieceRounds = 2;", "constexpr int kMinPieceRounds = 1;")]})
+    case = make_case(kv_lens=[700, 64, 1234], q_lens=[2, 1, 1], kv_dtype="fp8_e4m3", seed=22,
+                     sm_scale=1 / math.sqrt(192))
+    jobs = []
+    for c in (case, _relayout(case, 5)):
+        for sched in SCHEDULES.values():
+            for land in ("wait", "issue"):
+                env = {**RACE, **sched, "MLA_ITEM_COST_ROUNDS": "1", "EMU_DMA_LAND": land}
+                jobs.append((c, 16, 1, dict(binary=binary, env_extra=env, want_plan=True)))
+    for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs, workers=8)):
+        assert sum(len(w) == 2 for w in _plan_items(meta["plan"])) == 1
+        _check(c, out, lse)
