@@ -96,18 +96,21 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
     units = [os.path.join(src, f) for f in UNITS]
     units += [os.path.join(HERE, "emu_runtime.cpp"), os.path.join(HERE, "run_case.cpp")]
     # A variant recompiles only the units that are, or include, a changed
-    # file, and links the base build's other objects (brought up to date
-    # first).
+    # file, and links the other objects of its base build (the default one,
+    # or the LDS-trace one for a traced variant), brought up to date first.
     changed = set(patches or {}) | ({"decode_kernel.hip"} if decode_source else set())
-    reuse = bool(tag) and sanitize and not ubsan and not lds_trace
-    if reuse:
+    reuse = bool(tag) and sanitize and not ubsan and tag != TRACE_TAG
+    base = os.path.join(OUT, TRACE_TAG) if lds_trace else OUT
+    if reuse and lds_trace:
+        trace_binary()
+    elif reuse:
         from tests.simt_emu import harness as _h
         _h.ensure_built()
 
     def compile_unit(u):
         name = os.path.basename(u)
         if reuse and not (_includes(u, src) & changed) and name not in changed:
-            return os.path.join(OUT, name + ".o")
+            return os.path.join(base, name + ".o")
         obj = os.path.join(out, name + ".o")
         cmd = [compiler(), *flags, "-x", "c++", "-c", u, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
@@ -123,6 +126,28 @@ def build(sanitize: bool = True, decode_source: str | None = None, tag: str = ""
     if res.returncode != 0:
         raise RuntimeError(f"emulator link failed:\n{res.stderr[-4000:]}")
     return binary
+
+
+TRACE_TAG = "ldstrace"
+
+
+def fresh_build(tag: str, **kw) -> str:
+    """build(tag=tag, **kw) unless that binary exists and is newer than every
+    source (for builds without patches: their options are fixed by the tag).
+    Not safe to call from several threads while the binary is stale."""
+    from tests.simt_emu import harness as _h
+    if kw.get("patches") or kw.get("decode_source"):
+        raise ValueError("fresh_build is for builds without patches")
+    path = os.path.join(OUT, tag, "run_case")
+    if not os.path.exists(path) or _h._stale(path):
+        build(tag=tag, **kw)
+    return path
+
+
+def trace_binary() -> str:
+    """The LDS-trace build (bank model and race detector), the base that
+    traced variants link against."""
+    return fresh_build(TRACE_TAG, lds_trace=True)
 
 
 def build_exhaustive() -> str:

@@ -31,9 +31,9 @@ def ensure_built() -> str:
     return BIN
 
 
-def _stale() -> bool:
+def _stale(binary: str = BIN) -> bool:
     from tests.simt_emu import build as _b
-    t = os.path.getmtime(BIN)
+    t = os.path.getmtime(binary)
     srcs = [os.path.join(_b.CSRC, f) for f in _b.KERNEL_FILES]
     srcs += [os.path.join(HERE, f) for f in ("gfx950_asm.h", "lds_trace.h", "emu_runtime.cpp",
                                               "run_case.cpp",

@@ -60,7 +60,7 @@ def _kinds(st):
 @pytest.fixture(scope="module")
 def binary():
     from tests.simt_emu import build as _b
-    return _b.build(tag="ldstrace", lds_trace=True)
+    return _b.trace_binary()
 
 
 @pytest.fixture(scope="module")

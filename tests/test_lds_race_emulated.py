@@ -47,7 +47,7 @@ SCHEDULES = {"lockstep": {}, "drift": {"EMU_SCHED": "drift"},
 @pytest.fixture(scope="module")
 def binary():
     from tests.simt_emu import build as _b
-    return _b.build(tag="ldstrace", lds_trace=True)
+    return _b.trace_binary()
 
 
 def _case(kv_dtype):
@@ -166,7 +166,8 @@ PLANTS = {
 
 @pytest.fixture(scope="module")
 def planted():
-    """{plant: emulator binary}, built three at a time."""
+    """{plant: emulator binary}, built four at a time (each recompiles only
+    the units its patched file enters)."""
     from tests.simt_emu import build as _b
 
     def one(name):
@@ -176,7 +177,8 @@ def planted():
         return _b.build(tag="race_" + name, lds_trace=True, patches={fname: [(old, new)]})
 
     names = sorted(PLANTS)
-    with ThreadPoolExecutor(max_workers=3) as ex:
+    _b.trace_binary()   # the base the variants link against, brought up to date once
+    with ThreadPoolExecutor(max_workers=4) as ex:
         return dict(zip(names, ex.map(one, names)))
 
 

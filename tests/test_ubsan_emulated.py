@@ -33,7 +33,7 @@ SELECTION = [
 
 def test_emulated_suites_under_ubsan():
     from tests.simt_emu import build as _b
-    binary = _b.build(tag="ubsan", ubsan=True)
+    binary = _b.fresh_build("ubsan", ubsan=True)
     env = dict(os.environ, EMU_BINARY=binary, UBSAN_OPTIONS="print_stacktrace=1")
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                           *SELECTION], env=env, cwd=ROOT, capture_output=True, text=True,
