@@ -32,6 +32,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "gfx950_asm.h"
 #include "plan_layout.h"
 #include "tree.h"
 
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kWaves * 64) void mla_tree_kernel(const TreeArgs a)
       v0 = f32x4{p0[0] * s, p0[1] * s, p1[0] * s, p1[1] * s};
       v1 = f32x4{p2[0] * s, p2[1] * s, p3[0] * s, p3[1] * s};
     }
-    f32x4* dst = reinterpret_cast<f32x4*>(&keys[k][8 * c]);
+    LDS_PTR(f32x4) dst = (LDS_PTR(f32x4))(&keys[k][8 * c]);
     dst[0] = v0;
     dst[1] = v1;
   }
@@ -178,11 +179,11 @@ __global__ __launch_bounds__(kWaves * 64) void mla_tree_kernel(const TreeArgs a)
 #pragma unroll
     for (int i = 0; i < kHeadsPerWave; ++i) part[i][k] = 0.f;
     if (!((vis >> k) & 1u)) continue;
-    const f32x4* kr = reinterpret_cast<const f32x4*>(&keys[k][8 * lane]);
+    const LDS_PTR(f32x4) kr = (const LDS_PTR(f32x4))(&keys[k][8 * lane]);
     const f32x4 k0 = kr[0], k1 = kr[1];
     f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
     if (lane < kTail) {
-      const f32x4* tr = reinterpret_cast<const f32x4*>(&keys[k][kDLatent + 8 * lane]);
+      const LDS_PTR(f32x4) tr = (const LDS_PTR(f32x4))(&keys[k][kDLatent + 8 * lane]);
       t0 = tr[0];
       t1 = tr[1];
     }
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kWaves * 64) void mla_tree_kernel(const TreeArgs a)
 #pragma unroll
   for (int k = 0; k < kMaxDrafts; ++k) {
     if (!((vis >> k) & 1u)) continue;
-    const f32x4* kr = reinterpret_cast<const f32x4*>(&keys[k][8 * lane]);
+    const LDS_PTR(f32x4) kr = (const LDS_PTR(f32x4))(&keys[k][8 * lane]);
     const f32x4 k0 = kr[0], k1 = kr[1];
 #pragma unroll
     for (int i = 0; i < kHeadsPerWave; ++i) {

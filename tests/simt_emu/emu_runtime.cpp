@@ -25,6 +25,7 @@
 #include <cstring>
 #include <deque>
 #include <memory>
+#include <unordered_map>
 #include <unordered_set>
 #include <utility>
 #include <vector>
@@ -120,9 +121,9 @@ struct Fiber {
   bool done = false;
   std::deque<Pending> dma;
   // race detector (EMU_LDS_RACE): this lane's vector clock over the waves of
-  // the workgroup, and its copies not yet waited for (LDS byte, size)
+  // the workgroup, and its copies not yet waited for (address, size)
   uint32_t vc[kMaxWaves] = {};
-  std::deque<std::pair<uint32_t, int>> race_dma;
+  std::deque<std::pair<uintptr_t, int>> race_dma;
 };
 
 struct Sched {
@@ -199,7 +200,9 @@ void lds_analyze(Wave& w);
 // after write, write after write, write after read), whatever the schedule
 // happened to do.  A copy counts as written when the issuing wave waits for
 // it (vmcnt), and any access to its destination while it is in flight is a
-// race, also by the issuing wave.  The first race stops the run.
+// race, also by the issuing wave.  The first race stops the run.  Accesses
+// outside the decode kernels' LDS array (the tree merge kernel's shared
+// array) are tracked by address.
 bool race_checking() {
   static const bool v = [] {
     if (!std::getenv("EMU_LDS_RACE")) return false;
@@ -218,7 +221,8 @@ struct RaceCell {
   uint32_t wepoch = 0;     // the writer's epoch at that write (or at the wait)
   uint32_t reads[kMaxWaves] = {};   // each wave's latest read epoch since it
 };
-std::vector<RaceCell> race_cells(kLdsLimit / 4);
+std::vector<RaceCell> race_cells(kLdsLimit / 4);    // the decode kernels' LDS array
+std::unordered_map<uintptr_t, RaceCell> race_other;  // other kernels' shared arrays
 uint32_t race_gen = 0;
 struct FlagRelease {
   const int* p;
@@ -229,33 +233,39 @@ std::vector<FlagRelease> race_flags;   // this workgroup's publishes, in order
 
 int race_waves() { return int(S.waves.size()); }
 
-RaceCell& race_cell(uint32_t dword) {
-  RaceCell& c = race_cells[dword];
+// the LDS byte offset of an address in the decode kernels' LDS array, or -1
+long lds_offset_of(uintptr_t a) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(lds_base.load());
+  return (b && a >= b && a < b + kLdsLimit) ? long(a - b) : -1;
+}
+
+// the state of the dword at address 4 * dword
+RaceCell& race_cell(uintptr_t dword) {
+  const long off = lds_offset_of(4 * dword);
+  RaceCell& c = off >= 0 ? race_cells[off / 4] : race_other[dword];
   if (c.gen != race_gen) c = RaceCell{race_gen};
   return c;
 }
 
-[[noreturn]] void race_report(const char* kind, uint32_t dword, int other, uint32_t epoch) {
+[[noreturn]] void race_report(const char* kind, uintptr_t dword, int other, uint32_t epoch) {
   const Fiber& f = *S.cur;
+  char where[64];
+  const long off = lds_offset_of(4 * dword);
+  if (off >= 0) std::snprintf(where, sizeof where, "LDS byte %ld", off);
+  else std::snprintf(where, sizeof where, "shared address %#lx", (unsigned long)(4 * dword));
   std::fprintf(stderr,
-               "simt-emu: LDS race (%s) at LDS byte %u: wave %d lane %d has seen wave %d up to "
-               "epoch %u, which accessed the dword at epoch %u\n",
-               kind, 4 * dword, f.tid >> 6, f.lane, other, other >= 0 ? f.vc[other] : 0u, epoch);
+               "simt-emu: LDS race (%s) at %s: wave %d lane %d has seen wave %d up to epoch %u, "
+               "which accessed the dword at epoch %u\n",
+               kind, where, f.tid >> 6, f.lane, other, other >= 0 ? f.vc[other] : 0u, epoch);
   fail("LDS race");
 }
 
-uint32_t race_offset(const void* p, int bytes) {
-  const unsigned char* b = lds_base.load();
-  const unsigned char* c = static_cast<const unsigned char*>(p);
-  if (!b || c < b || c + bytes > b + kLdsLimit) fail("LDS access outside the LDS");
-  return uint32_t(c - b);
-}
-
 // kind: 0 load, 1 store, 2 copy issued
-void race_access(uint32_t off, int bytes, int kind) {
+void race_access(const void* p, int bytes, int kind) {
   Fiber& f = *S.cur;
   const int u = f.tid >> 6;
-  for (uint32_t d = off / 4; d <= (off + uint32_t(bytes) - 1) / 4; ++d) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  for (uintptr_t d = a / 4; d <= (a + uintptr_t(bytes) - 1) / 4; ++d) {
     RaceCell& c = race_cell(d);
     if (c.in_flight)
       race_report(kind == 0 ? "read of a copy in flight" : "write over a copy in flight", d,
@@ -276,9 +286,9 @@ void race_access(uint32_t off, int bytes, int kind) {
 }
 
 // the issuing lane's wait for a copy: from here on it counts as written
-void race_copy_landed(uint32_t off, int bytes) {
+void race_copy_landed(uintptr_t a, int bytes) {
   Fiber& f = *S.cur;
-  for (uint32_t d = off / 4; d <= (off + uint32_t(bytes) - 1) / 4; ++d) {
+  for (uintptr_t d = a / 4; d <= (a + uintptr_t(bytes) - 1) / 4; ++d) {
     RaceCell& c = race_cell(d);
     c.in_flight = 0;
     c.wepoch = f.vc[f.tid >> 6];
@@ -635,8 +645,8 @@ void lds_dma(uint32_t lds, int voff, const void* sbase, int bytes) {
       lds_stats.dma_lines.insert(line);
   }
   if (race_checking()) {
-    race_access(uint32_t(off), bytes, 2);
-    S.cur->race_dma.emplace_back(uint32_t(off), bytes);
+    race_access(p.dst, bytes, 2);
+    S.cur->race_dma.emplace_back(reinterpret_cast<uintptr_t>(p.dst), bytes);
   }
   if (land_at_issue()) apply(p);
   else S.cur->dma.push_back(p);
@@ -660,11 +670,14 @@ void vm_wait(int n) {
 void block_barrier() { wait_on(S.block_bar); }
 
 void lds_trace_access(const void* p, int bytes, bool write) {
-  const uint32_t off = race_offset(p, bytes);
-  if (lds_tracing())
+  if (lds_tracing()) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (lds_offset_of(a) < 0 || lds_offset_of(a + bytes - 1) < 0)
+      fail("LDS access outside the LDS");
     S.cur->wave->trace[S.cur->lane].push_back(
         Access{static_cast<const unsigned char*>(p), bytes, write});
-  if (race_checking()) race_access(off, bytes, write ? 1 : 0);
+  }
+  if (race_checking()) race_access(p, bytes, write ? 1 : 0);
 }
 
 // Publishing an LDS word is a wave operation: every lane of the wave has
@@ -782,7 +795,7 @@ emu_f32x16 mfma32x32x16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x16 c) {
 }
 
 emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
-  if (race_checking()) race_access(race_offset(p, 8), 8, 0);
+  if (race_checking()) race_access(p, 8, 0);
   return wave_op(p, [](int l, auto get) {
     if (l == 0 && lds_tracing()) {
       const unsigned char* addr[64];
@@ -801,7 +814,7 @@ emu_bf16x4 ds_read_tr16_b64(const emu_bf16x4* p) {
 }
 
 emu_i32x2 ds_read_tr8_b64(const emu_i32x2* p) {
-  if (race_checking()) race_access(race_offset(p, 8), 8, 0);
+  if (race_checking()) race_access(p, 8, 0);
   return wave_op(p, [](int l, auto get) {
     const int g = l >> 4, i = l & 15;
     unsigned char out[8];

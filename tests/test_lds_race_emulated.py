@@ -14,7 +14,8 @@ order, so the check does not depend on the lockstep, drift or random
 schedule finding the bad interleaving.
 
 The checks: no decode kernel races on a case with several items per
-workgroup, in any schedule, or on seeded random shapes; each synchronisation step taken out of a kernel
+workgroup, in any schedule, on seeded random shapes, or with tree-shaped
+drafts (whose merge kernel shares the drafts' keys through LDS); each synchronisation step taken out of a kernel
 (planted in a copy of the source, on the CPU only) is reported, in the
 lockstep schedule, as the kind of race it opens; and the library kernels'
 known restart-flag race (a wave sets the flag while another still reads it
@@ -229,3 +230,43 @@ def test_fifth_fault_plan_is_race_free():
     for (c, *_), (out, lse, meta) in zip(jobs, harness.run_many(jobs, workers=8)):
         assert sum(len(w) == 2 for w in _plan_items(meta["plan"])) == 1
         _check(c, out, lse)
+
+
+def test_tree_drafts_have_no_lds_race(binary):
+    # the tree-draft path (a non-causal decode of the prefix, then
+    # mla_tree_attend, whose workgroups share the drafts' keys through LDS)
+    # with every mask kind, both cache types and each decode kernel that
+    # takes it, race-checked
+    from tests.simt_emu import harness
+    from tests.test_tree_emulated import check_tree
+    from tests.tree_cases import tree_masks
+    jobs = []
+    for n, kind in enumerate(("causal", "diag", "branch", "random", "none")):
+        kvd = ("bf16", "fp8_e4m3")[n % 2]
+        case = make_case(kv_lens=[300, 8, 70, 4, 1000], q_lens=[4, 8, 3, 4, 0], seed=51,
+                         num_heads=16, page_size=64, kv_dtype=kvd, sm_scale=1 / math.sqrt(192),
+                         max_q_len=8)
+        mask = tree_masks(case.q_lens, case.max_q_len, kind, seed=2)
+        for kernel in (None, "w8", "split"):
+            env = dict(RACE, **({"MLA_DECODE_KERNEL": kernel} if kernel else {}))
+            jobs.append(((case, mask), 6, 1, dict(tree_mask=mask, env_extra=env, binary=binary)))
+    runs = harness.run_many([(c, n, p, kw) for (c, _m), n, p, kw in jobs], workers=8)
+    for ((case, mask), *_), (out, lse, _meta) in zip(jobs, runs):
+        check_tree(case, mask, out, lse)
+
+
+def test_detector_reports_a_missing_tree_barrier():
+    # the tree merge kernel with its barrier after the drafts' keys are
+    # written taken out (on the CPU only): a wave reads keys another wave
+    # has yet to write
+    from tests.simt_emu import build as _b, harness
+    from tests.tree_cases import tree_masks
+    old = "    dst[1] = v1;\n  }\n  __syncthreads();"
+    assert open(os.path.join(_b.CSRC, "tree_kernel.hip")).read().count(old) == 1
+    binary = _b.build(tag="race_tree_barrier", lds_trace=True,
+                      patches={"tree_kernel.hip": [(old, "    dst[1] = v1;\n  }")]})
+    case = make_case(kv_lens=[300, 8, 70, 4, 1000], q_lens=[4, 8, 3, 4, 0], seed=51,
+                     num_heads=16, page_size=64, sm_scale=1 / math.sqrt(192), max_q_len=8)
+    mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=2)
+    with pytest.raises(RuntimeError, match=r"LDS race \(write after read\) at shared address"):
+        harness.run(case, 6, 1, tree_mask=mask, env_extra=RACE, binary=binary)
