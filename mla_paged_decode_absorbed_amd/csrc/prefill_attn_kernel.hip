@@ -35,6 +35,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "gfx950_asm.h"
 #include "prefill.h"
 
 namespace mla {
@@ -73,7 +74,7 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
 #pragma unroll
     for (int sg = 0; sg < 3; ++sg) {
       const i32x4 kop =
-          *reinterpret_cast<const i32x4*>(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
+          *(const LDS_PTR(i32x4))(ktile + (16 * T + col) * kKStride + 64 * sg + 16 * g);
 #pragma unroll
       for (int u = 0; u < kU; ++u)
         sacc[u][T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[u][sg], sacc[u][T], 0, 0, 0);
@@ -146,11 +147,11 @@ __device__ __forceinline__ void attend_block(const int8_t* ktile, const uint8_t*
   // O^T += V^T P^T per 16-channel tile, straight into the accumulators: the
   // lanes of channel row col hand the instruction that channel's e8m0 scale
   // (its power-of-two exponent + 127), which it applies to the row of V^T
-  const uint32_t* vx = reinterpret_cast<const uint32_t*>(vexp + 8 * col);
+  const LDS_PTR(uint32_t) vx = (const LDS_PTR(uint32_t))(vexp + 8 * col);
   const uint32_t ex[2] = {vx[0], vx[1]};
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    const i32x4* vr = reinterpret_cast<const i32x4*>(vtile + (16 * ct + col) * kVStride + 32 * g);
+    const LDS_PTR(i32x4) vr = (const LDS_PTR(i32x4))(vtile + (16 * ct + col) * kVStride + 32 * g);
     const i32x4 v0 = vr[0], v1 = vr[1];
     const i32x8 vop = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     const int sa = int((ex[ct >> 2] >> (8 * (ct & 3))) & 0xFFu);
@@ -207,15 +208,16 @@ __device__ __forceinline__ void store_block(const BlockRegs<kThreads>& r, int8_t
   for (int j = 0; j < BlockRegs<kThreads>::kK; ++j) {
     const int c = int(threadIdx.x) + kThreads * j;
     const int key = c / 12, part = c - key * 12;
-    *reinterpret_cast<i32x4*>(ktile + key * kKStride + 16 * part) = r.k[j];
+    *(LDS_PTR(i32x4))(ktile + key * kKStride + 16 * part) = r.k[j];
   }
 #pragma unroll
   for (int j = 0; j < BlockRegs<kThreads>::kV; ++j) {
     const int c = int(threadIdx.x) + kThreads * j;
-    *reinterpret_cast<i32x4*>(vtile + (c >> 3) * kVStride + 16 * (c & 7)) = r.v[j];
+    *(LDS_PTR(i32x4))(vtile + (c >> 3) * kVStride + 16 * (c & 7)) = r.v[j];
   }
   // channel c = 16 ct + col goes to byte 8 col + ct: a lane reads its 8 in one
-  if (threadIdx.x < kPfDV) vexp[8 * (threadIdx.x & 15) + (threadIdx.x >> 4)] = uint8_t(r.vx);
+  if (threadIdx.x < kPfDV)
+    *(LDS_PTR(uint8_t))(vexp + 8 * (threadIdx.x & 15) + (threadIdx.x >> 4)) = uint8_t(r.vx);
 }
 
 // kW waves of kU 16-query tiles each: a workgroup covers kQ = 16 kW kU

@@ -201,8 +201,8 @@ void lds_analyze(Wave& w);
 // happened to do.  A copy counts as written when the issuing wave waits for
 // it (vmcnt), and any access to its destination while it is in flight is a
 // race, also by the issuing wave.  The first race stops the run.  Accesses
-// outside the decode kernels' LDS array (the tree merge kernel's shared
-// array) are tracked by address.
+// outside the decode kernels' LDS array (the tree merge and prefill attention
+// kernels' shared arrays) are tracked by address.
 bool race_checking() {
   static const bool v = [] {
     if (!std::getenv("EMU_LDS_RACE")) return false;

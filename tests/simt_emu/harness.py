@@ -224,11 +224,13 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_prefill(case, num_blocks: int, timeout: float = 900.0):
+def run_prefill(case, num_blocks: int, timeout: float = 900.0, env_extra: dict | None = None,
+                binary: str | None = None):
     """A packed prefill case (``workloads.prefill.PrefillCase``) through
     mla_prefill_quantize + mla_prefill_attn.  Returns a dict of the outputs:
     qc, qs, kc [T, H, ...], ks [blocks, H], vc [blocks, H, 128, 128], vs [blocks, H, 128],
-    o (bf16 bits [T, H, 128]), lse [T, H]."""
+    o (bf16 bits [T, H, 128]), lse [T, H].  ``env_extra`` and ``binary`` as
+    for run."""
     S, T, H = case.num_seqs, case.num_tokens, case.num_heads
     hdr = np.array([PREFILL_MAGIC, S, T, H, num_blocks, 0, 0, 0, 0, 0, 0, 0], dtype=np.int32)
     with tempfile.TemporaryDirectory() as d:
@@ -241,7 +243,8 @@ def run_prefill(case, num_blocks: int, timeout: float = 900.0):
                 f.write(np.ascontiguousarray(x).tobytes())
         env = dict(os.environ)
         env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
-        res = subprocess.run([ensure_built(), fin, fout], capture_output=True, text=True,
+        env.update(env_extra or {})
+        res = subprocess.run([binary or ensure_built(), fin, fout], capture_output=True, text=True,
                              timeout=timeout, env=env)
         if res.returncode != 0:
             raise RuntimeError(f"emulated run failed (rc {res.returncode}):\n{res.stderr[-6000:]}")

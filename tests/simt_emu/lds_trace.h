@@ -5,8 +5,8 @@
 // wave rendezvous the accesses of the wave's lanes are lined up (the k-th
 // access of every lane is one instruction) and scored against a model of the
 // LDS banks (emu_runtime.cpp); with EMU_LDS_RACE each access is also checked
-// by the runtime's happens-before race detector.  Only the decode kernels and
-// the tree merge kernel use LDS_PTR.
+// by the runtime's happens-before race detector.  The decode kernels, the tree
+// merge kernel and the prefill attention kernel use LDS_PTR.
 #pragma once
 #include <cstddef>
 

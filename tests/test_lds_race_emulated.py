@@ -270,3 +270,34 @@ def test_detector_reports_a_missing_tree_barrier():
     mask = tree_masks(case.q_lens, case.max_q_len, "branch", seed=2)
     with pytest.raises(RuntimeError, match=r"LDS race \(write after read\) at shared address"):
         harness.run(case, 6, 1, tree_mask=mask, env_extra=RACE, binary=binary)
+
+
+def _prefill(binary):
+    from oracle import prefill_ref
+    from tests.prefill_cases import check_attention, check_quantized
+    from tests.simt_emu import harness
+    from workloads.prefill import make_prefill_case
+    case = make_prefill_case(seqlens=[300, 1, 5, 129], num_heads=2, seed=71)
+    got = harness.run_prefill(case, prefill_ref.num_blocks(case.seqlens), env_extra=RACE,
+                              binary=binary)
+    check_attention(case, got["o"], got["lse"], quantized=check_quantized(case, got))
+
+
+def test_prefill_attention_has_no_lds_race(binary):
+    # the quantized prefill's attention kernel, whose waves share each key
+    # block's INT8 keys, e4m3 values and value exponents through LDS
+    _prefill(binary)
+
+
+def test_detector_reports_a_missing_prefill_barrier():
+    # its barrier between writing a key block and reading it taken out (on
+    # the CPU only)
+    from tests.simt_emu import build as _b
+    old = "    store_block<kThreads>(regs, ktile, vtile, vexp);\n    const float kscale = regs.ks;\n" \
+          "    __syncthreads();"
+    new = "    store_block<kThreads>(regs, ktile, vtile, vexp);\n    const float kscale = regs.ks;"
+    assert open(os.path.join(_b.CSRC, "prefill_attn_kernel.hip")).read().count(old) == 1
+    binary = _b.build(tag="race_prefill_barrier", lds_trace=True,
+                      patches={"prefill_attn_kernel.hip": [(old, new)]})
+    with pytest.raises(RuntimeError, match=r"LDS race \((read after write|write after read)\)"):
+        _prefill(binary)
