@@ -1,5 +1,6 @@
-"""LDS races in the decode kernels, found by a happens-before detector in the
-lane-fiber emulator (CPU only).
+"""LDS races in the decode kernels (and in the tree-draft merge and prefill
+attention kernels), found by a happens-before detector in the lane-fiber
+emulator (CPU only).
 
 With EMU_LDS_RACE set, the LDS-trace build of the emulator
 (tests/simt_emu/emu_runtime.cpp) treats each wave as one thread: a lane
@@ -15,11 +16,13 @@ schedule finding the bad interleaving.
 
 The checks: no decode kernel races on a case with several items per
 workgroup, in any schedule, on seeded random shapes, or with tree-shaped
-drafts (whose merge kernel shares the drafts' keys through LDS); each synchronisation step taken out of a kernel
-(planted in a copy of the source, on the CPU only) is reported, in the
-lockstep schedule, as the kind of race it opens; and the library kernels'
-known restart-flag race (a wave sets the flag while another still reads it
-in the same barrier interval) is reported whenever an item restarts."""
+drafts (whose merge kernel shares the drafts' keys through LDS), and the
+prefill attention kernel does not race either; each synchronisation step
+taken out of a kernel (planted in a copy of the source, on the CPU only) is
+reported, in the lockstep schedule, as the kind of race it opens; and the
+library kernels' known restart-flag race (a wave sets the flag while another
+still reads it in the same barrier interval) is reported whenever an item
+restarts."""
 import math
 import os
 import re
